@@ -1,0 +1,232 @@
+"""CPU oracle for the fused residual-add + RMSNorm forward (bf16 storage).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The GPU library never
+imports, links or calls it, and it imports nothing from the GPU library.
+
+The arithmetic lives in ``add_rmsnorm_oracle.c`` (plain C, single thread,
+binary64 after the fp32 add, bit-level round-to-nearest-even); this module
+builds and loads it with ctypes and adds the measurement helpers of the same
+page (ROCm/aiter issue "rmsnorm2d_fwd_with_add truncates fp32->bf16 on gfx942,
+biasing residual_out and compounding across layers", "Steps to Reproduce"):
+the magnitude-bias metric, the residual-stream RMS and the cosine similarity
+it prints, plus the binary64 chain that never rounds.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "add_rmsnorm_oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+RNE = 0
+TRUNC = 1
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+          "-fno-fast-math", "-fno-tree-vectorize"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``liboracle.so`` next to its source."""
+    if force or not os.path.exists(LIBRARY) or (
+            os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+        compile_library(SOURCE, LIBRARY)
+    return LIBRARY
+
+
+def compile_library(source: str, target: str) -> str:
+    """Compile an oracle source file into a shared library at ``target``."""
+    tmp = target + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, "-lm"], check=True)
+    os.replace(tmp, target)
+    return target
+
+
+class Oracle:
+    """ctypes front end of one build of the C oracle."""
+
+    def __init__(self, path: str):
+        L = ctypes.CDLL(path)
+        L.orc_rne16.restype = ctypes.c_uint16
+        L.orc_rne16.argtypes = [ctypes.c_uint32]
+        L.orc_trunc16.restype = ctypes.c_uint16
+        L.orc_trunc16.argtypes = [ctypes.c_uint32]
+        L.orc_rne16_from_f64.restype = ctypes.c_uint16
+        L.orc_rne16_from_f64.argtypes = [ctypes.c_double]
+        L.orc_rne16_array.restype = None
+        L.orc_rne16_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        L.orc_rne16_range.restype = None
+        L.orc_rne16_range.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p]
+        L.orc_rne16_from_f64_array.restype = None
+        L.orc_rne16_from_f64_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_int64]
+        L.orc_add_rmsnorm.restype = ctypes.c_int
+        L.orc_add_rmsnorm.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                      ctypes.c_int]
+        self.path = path
+        self.lib = L
+
+    # ------------------------------------------------------------ converters
+
+    def rne16(self, u32: int) -> int:
+        """fp32 bit pattern -> bf16 bit pattern, nearest-even (NaN -> quiet NaN)."""
+        return int(self.lib.orc_rne16(int(u32) & 0xFFFFFFFF))
+
+    def trunc16(self, u32: int) -> int:
+        """fp32 bit pattern -> bf16 bit pattern by truncation (negative control)."""
+        return int(self.lib.orc_trunc16(int(u32) & 0xFFFFFFFF))
+
+    def rne16_from_f64(self, y: float) -> int:
+        """binary64 -> bf16 bit pattern, correctly rounded, nearest-even."""
+        return int(self.lib.orc_rne16_from_f64(float(y)))
+
+    def rne16_array(self, u32: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(u32, dtype=np.uint32)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.orc_rne16_array(_ptr(a), _ptr(out), a.size)
+        return out
+
+    def rne16_range(self, start: int, count: int) -> np.ndarray:
+        """bf16 results for the fp32 bit patterns start .. start+count-1."""
+        out = np.empty(count, dtype=np.uint16)
+        self.lib.orc_rne16_range(start, count, _ptr(out))
+        return out
+
+    def rne16_from_f64_array(self, y: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(y, dtype=np.float64)
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.orc_rne16_from_f64_array(_ptr(a), _ptr(out), a.size)
+        return out
+
+    # ------------------------------------------------------------ the fused op
+
+    def add_rmsnorm(self, x: np.ndarray, residual: np.ndarray, weight: np.ndarray,
+                    eps: float = 1e-6, rounding: int = RNE, want_exact: bool = False):
+        """Oracle forward.  x, residual: uint16 [n, hidden] bf16 bits; weight [hidden].
+
+        Returns (out, residual_out) as uint16 arrays, plus the unrounded
+        binary64 out values when ``want_exact`` is set.
+        """
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
+        weight = np.ascontiguousarray(weight, dtype=np.uint16)
+        if x.ndim != 2 or residual.shape != x.shape or weight.shape != (x.shape[1],):
+            raise ValueError("shape mismatch: x %s residual %s weight %s"
+                             % (x.shape, residual.shape, weight.shape))
+        n, h = x.shape
+        out = np.empty_like(x)
+        res_out = np.empty_like(x)
+        y = np.empty(x.shape, dtype=np.float64) if want_exact else None
+        rc = self.lib.orc_add_rmsnorm(_ptr(out), _ptr(res_out),
+                                      _ptr(y) if y is not None else None,
+                                      _ptr(x), _ptr(residual), _ptr(weight), n, h,
+                                      ctypes.c_float(eps), rounding)
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+        if want_exact:
+            return out, res_out, y
+        return out, res_out
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from this package's source (built on first use)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY) or (
+                os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+            build(force=True)
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def rne16(u32: int) -> int:
+    return default().rne16(u32)
+
+
+def trunc16(u32: int) -> int:
+    return default().trunc16(u32)
+
+
+def rne16_from_f64(y: float) -> int:
+    return default().rne16_from_f64(y)
+
+
+def rne16_array(u32: np.ndarray) -> np.ndarray:
+    return default().rne16_array(u32)
+
+
+def rne16_range(start: int, count: int) -> np.ndarray:
+    return default().rne16_range(start, count)
+
+
+def rne16_from_f64_array(y: np.ndarray) -> np.ndarray:
+    return default().rne16_from_f64_array(y)
+
+
+def add_rmsnorm(x, residual, weight, eps: float = 1e-6, rounding: int = RNE,
+                want_exact: bool = False):
+    return default().add_rmsnorm(x, residual, weight, eps, rounding, want_exact)
+
+
+# ---------------------------------------------------------------- measurements
+
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to binary64."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(
+        np.float64)
+
+
+def magnitude_bias(got: np.ndarray, exp: np.ndarray) -> float:
+    """Mean relative magnitude error over the elements where exp is nonzero.
+
+    Follows the page's magnitude_bias: (|got| - |exp|) / max(|exp|, 1e-30),
+    averaged over exp != 0; negative means the values shrank toward zero.
+    Both arguments are real-valued arrays (widen bf16 first).
+    """
+    g = np.asarray(got, dtype=np.float64).ravel()
+    e = np.asarray(exp, dtype=np.float64).ravel()
+    nz = e != 0
+    rel = (np.abs(g[nz]) - np.abs(e[nz])) / np.maximum(np.abs(e[nz]), 1e-30)
+    return float(rel.mean())
+
+
+def ratio_bias(got: np.ndarray, exp: np.ndarray) -> float:
+    """Ratio-of-sums form of the signed magnitude error: sum(|g|-|e|) / sum(|e|).
+
+    Used for long chains, where the per-element relative error is dominated by
+    elements that drift close to zero.
+    """
+    g = np.abs(np.asarray(got, dtype=np.float64).ravel())
+    e = np.abs(np.asarray(exp, dtype=np.float64).ravel())
+    return float((g - e).sum() / e.sum())
+
+
+def rms(a: np.ndarray) -> float:
+    """Root mean square over all elements (the page's residual-stream size)."""
+    a = np.asarray(a, dtype=np.float64)
+    return float(np.sqrt(np.mean(a * a)))
+
+
+def cosine_similarity(a: np.ndarray, b: np.ndarray) -> float:
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    return float(a @ b / (np.sqrt(a @ a) * np.sqrt(b @ b)))
+
+
+def chain_fp64_step(residual64: np.ndarray, x_bf16: np.ndarray) -> np.ndarray:
+    """One step of the never-rounded residual stream: R + x in binary64."""
+    return residual64 + bf16_to_f64(x_bf16)

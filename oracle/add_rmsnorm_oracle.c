@@ -1,0 +1,170 @@
+/*
+ * CPU oracle for the fused residual-add + RMSNorm forward with bf16 storage.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the GPU library links, includes or
+ * calls this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load it.  It shares no code with the HIP path.
+ *
+ * What it computes follows the "Steps to Reproduce" listing of the ROCm/aiter
+ * issue "rmsnorm2d_fwd_with_add truncates fp32->bf16 on gfx942, biasing
+ * residual_out and compounding across layers" (its reference() function):
+ *   acc          = float(x) + float(residual)                 (fp32 add)
+ *   residual_out = bf16(acc)
+ *   out          = bf16( acc * rsqrt(mean(acc^2) + eps) * float(weight) )
+ * with both bf16 stores rounded to nearest, ties to even -- the semantics of
+ * torch's .to(torch.bfloat16), which the same issue uses as its unbiased
+ * reference and which its "mode 0 standard" rebuild reproduces bit for bit.
+ *
+ * Precision: the fp32 add is the definition's own step and is done in fp32.
+ * Everything after it is done in binary64: the sum of squares is exact per
+ * term (a 24-bit significand squared fits in 53 bits) and its sequential sum
+ * carries at most hidden * 2^-53 relative error; out is then rounded once,
+ * correctly, from the binary64 value.  The GPU path works in fp32 and may land
+ * one bf16 ULP away from this value near a rounding boundary.
+ *
+ * The truncation mode (rounding = 1) is the negative control from the same
+ * issue (its bf16_truncate helper and "mode 2" of fp32_to_bf16): it keeps the
+ * high 16 bits of the fp32 value.  It exists only to show that the tests can
+ * tell truncation from round-to-nearest-even.
+ *
+ * Build: plain C11, gcc -O2 -ffp-contract=off -fno-tree-vectorize, no fast-math,
+ * SSE2 binary64 arithmetic with the default MXCSR (no flush-to-zero).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_RNE 0
+#define ORC_TRUNC 1
+
+static uint32_t f32_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return u;
+}
+
+static float bits_f32(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* bf16 -> fp32 widening: a bf16 value is the high half of an fp32 word. */
+static float bf16_to_f32(uint16_t b) { return bits_f32((uint32_t)b << 16); }
+
+/*
+ * fp32 -> bf16, round to nearest, ties to even.  Adding 0x7FFF plus the lowest
+ * kept bit to the word and dropping the low half rounds up exactly when the
+ * dropped half exceeds one half-ULP, or equals it and the kept part is odd.
+ * The carry may ripple into the exponent (correct: the next binade, or Inf for
+ * values at or above the overflow midpoint).  NaN must be caught first: the
+ * same addition would carry a NaN with a small payload into Inf.  NaN maps to
+ * a quiet NaN with its sign and high payload bits kept.
+ */
+uint16_t orc_rne16(uint32_t u) {
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+    return (uint16_t)((u >> 16) | 0x0040u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+/* Negative control: truncation toward zero (keep the high half). */
+uint16_t orc_trunc16(uint32_t u) { return (uint16_t)(u >> 16); }
+
+/*
+ * binary64 -> bf16, correctly rounded (nearest, ties to even), in one step.
+ * bf16 keeps 8 significant bits and fp32's exponent range, so its quantum at
+ * a value with binary exponent e is 2^(max(e,-126) - 7).  Dividing by that
+ * power of two is exact in binary64, nearbyint() rounds to an integer under
+ * the default round-to-nearest-even mode, and multiplying back is exact.
+ * A result above the largest finite bf16 has overflowed and becomes Inf.
+ */
+uint16_t orc_rne16_from_f64(double y) {
+  uint16_t sign = signbit(y) ? 0x8000u : 0u;
+  if (isnan(y)) return (uint16_t)(sign | 0x7FC0u);
+  if (isinf(y)) return (uint16_t)(sign | 0x7F80u);
+  double a = fabs(y);
+  if (a == 0.0) return sign;
+  int e;
+  (void)frexp(a, &e); /* a = f * 2^e with f in [0.5, 1): floor(log2 a) = e-1 */
+  int ex = e - 1;
+  if (ex < -126) ex = -126;
+  double q = ldexp(1.0, ex - 7);
+  double r = nearbyint(a / q) * q;
+  const double bf16_max = ldexp(255.0, 127 - 7); /* 0x7F7F */
+  if (r > bf16_max) return (uint16_t)(sign | 0x7F80u);
+  return (uint16_t)(sign | (f32_bits((float)r) >> 16));
+}
+
+/* Element-wise helpers so that tests can sweep the converter cheaply. */
+void orc_rne16_array(const uint32_t* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_rne16(in[i]);
+}
+
+/* Converts the consecutive fp32 bit patterns start, start+1, ... (mod 2^32). */
+void orc_rne16_range(uint64_t start, int64_t count, uint16_t* out) {
+  for (int64_t i = 0; i < count; ++i) out[i] = orc_rne16((uint32_t)(start + (uint64_t)i));
+}
+
+void orc_rne16_from_f64_array(const double* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_rne16_from_f64(in[i]);
+}
+
+/*
+ * The fused op over n_rows x hidden, row-major, contiguous; weight is [hidden].
+ * All arrays hold raw bf16 bit patterns.  y_exact (may be NULL) receives the
+ * unrounded binary64 value of each out element, for bias measurements.
+ * Returns 0, or -1 on a bad argument.
+ *
+ * Row steps, in the order of the definition:
+ *   1. acc_j = fp32(x_j) + fp32(r_j), an IEEE binary32 addition.
+ *   2. residual_out_j = bf16(acc_j).
+ *   3. S = sum_j acc_j^2, in binary64, j ascending.
+ *   4. The contract accumulates S in fp32, so a sum at or beyond fp32's
+ *      overflow midpoint (2 - 2^-24) * 2^127 is taken as +Inf, as an fp32 sum
+ *      would be.  (Rows within about 2^-20 of that midpoint are not comparable
+ *      with an fp32 implementation and are kept out of parity tests.)
+ *   5. rinv = 1 / sqrt(S / hidden + eps): the population mean (divide by
+ *      hidden), eps added after the mean and inside the square root.
+ *   6. y_j = (acc_j * rinv) * w_j.
+ *   7. out_j = bf16(y_j), rounded once from binary64.
+ * In truncation mode steps 2 and 7 keep the high half of the fp32 value
+ * instead (for step 7, of y_j first rounded to fp32, as an fp32 kernel would).
+ */
+int orc_add_rmsnorm(uint16_t* out, uint16_t* residual_out, double* y_exact,
+                    const uint16_t* x, const uint16_t* residual,
+                    const uint16_t* weight, int64_t n_rows, int64_t hidden,
+                    float eps, int rounding) {
+  if (n_rows < 0 || hidden <= 0) return -1;
+  if (rounding != ORC_RNE && rounding != ORC_TRUNC) return -1;
+  if (n_rows == 0) return 0;
+  if (!out || !residual_out || !x || !residual || !weight) return -1;
+
+  const double f32_overflow = ldexp(2.0 - ldexp(1.0, -24), 127);
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const uint16_t* xr = x + i * hidden;
+    const uint16_t* rr = residual + i * hidden;
+    uint16_t* ro = residual_out + i * hidden;
+    uint16_t* orow = out + i * hidden;
+
+    double s = 0.0;
+    for (int64_t j = 0; j < hidden; ++j) {
+      float acc = bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]);
+      uint32_t ab = f32_bits(acc);
+      ro[j] = rounding == ORC_RNE ? orc_rne16(ab) : orc_trunc16(ab);
+      double a = (double)acc;
+      s += a * a;
+    }
+    if (s >= f32_overflow) s = INFINITY;
+    double rinv = 1.0 / sqrt(s / (double)hidden + (double)eps);
+
+    for (int64_t j = 0; j < hidden; ++j) {
+      /* acc again, as in step 1: recomputing is cheaper than a row buffer. */
+      double a = (double)(bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]));
+      double y = (a * rinv) * (double)bf16_to_f32(weight[j]);
+      if (y_exact) y_exact[i * hidden + j] = y;
+      orow[j] = rounding == ORC_RNE ? orc_rne16_from_f64(y)
+                                    : orc_trunc16(f32_bits((float)y));
+    }
+  }
+  return 0;
+}
