@@ -1,0 +1,203 @@
+"""Benchmark of the fused residual-add + RMSNorm forward on one MI355X.
+
+A step is one add_rmsnorm_fwd call over the 4096 x 8192 bf16 workload
+(x, residual ~ N(0,1), weight ~ 1 + 0.1 N(0,1), eps = 1e-6), with the inputs
+already resident in HBM.  The timed region is K back-to-back steps on one
+stream, bracketed by device synchronisation and measured with HIP events on
+that stream.  Successive steps rotate over several buffer sets whose total
+footprint exceeds MI355X's 256 MB last-level cache, so each step streams from
+HBM rather than from cache.
+
+Output: one JSON line with the throughput in GB/s of algorithmic traffic
+(read x and residual, write out and residual_out: 8 bytes per element, plus
+the weight once), the HBM roofline fraction against 8 TB/s, and the CPU
+oracle timed on the host as a baseline.
+
+  python bench.py [--steps K] [--warmup W] [--workload 4096x8192]
+                  [--no-cpu-baseline] [--calibrate-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+CACHE_DEFEAT_BYTES = 1 << 30  # rotate buffer sets until the footprint is >= 1 GiB
+
+
+def algorithmic_bytes(n_rows: int, hidden: int) -> int:
+    """Bytes the method must move per call: x, residual read; out, residual_out
+    written (2 bytes each per element); the weight read once."""
+    return 8 * n_rows * hidden + 2 * hidden
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--workload", default="4096x8192")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="time budget of the CPU oracle baseline")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain device copy of known size (counter calibration)")
+    return p.parse_args(argv)
+
+
+def traffic_from_profiles(kernel_tag: str, workload: str, digest: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_%s.txt" % (kernel_tag, workload))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        m = re.match(r"^(\w+):\s*(\S+)", line)
+        if m:
+            fields[m.group(1)] = m.group(2)
+    if fields.get("sources_sha256") != digest:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def run_copy_calibration(torch, nbytes=1 << 30, reps=20):
+    """A plain device-to-device copy of nbytes, for reading what FETCH_SIZE and
+    WRITE_SIZE report for a known byte count."""
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes, "reps": reps}))
+
+
+def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s):
+    """The oracle (single-threaded C) over the whole workload, repeated until the
+    time budget is spent."""
+    import oracle
+
+    oracle.default()
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.add_rmsnorm(x, r, w, eps)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    gbps = algorithmic_bytes(n_rows, hidden) * passes / el / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full passes over the %dx%d workload in %.1f s (single thread)"
+                      % (passes, n_rows, hidden, el)}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows would shard across GPUs with no communication); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bf16_rounding_numerics_amd as arn
+    from bf16_rounding_numerics_amd import build as hip_build
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    arn.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    if args.calibrate_copy:
+        run_copy_calibration(torch)
+        return 0
+
+    n_rows, hidden = (int(v) for v in args.workload.split("x"))
+    cfg = synth.CONFIGS.get(args.workload, dict(seed=3, n_rows=n_rows, hidden=hidden))
+    eps = 1e-6
+    x, r, w = synth.workload(cfg["seed"], n_rows, hidden)
+    tensor_bytes = n_rows * hidden * 2
+    sets = max(1, -(-CACHE_DEFEAT_BYTES // (4 * tensor_bytes)))
+    xd0 = torch.from_numpy(x.view(np.int16)).to(dev)
+    rd0 = torch.from_numpy(r.view(np.int16)).to(dev)
+    wd = torch.from_numpy(w.view(np.int16)).to(dev)
+    bufs = []
+    for i in range(sets):
+        xd = xd0 if i == 0 else xd0.clone()
+        rd = rd0 if i == 0 else rd0.clone()
+        bufs.append((torch.empty_like(xd), torch.empty_like(xd), xd, rd))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        o, ro, xd, rd = bufs[i % sets]
+        arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, eps)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        o, ro, xd, rd = bufs[i % sets]
+        arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, eps)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    nbytes = algorithmic_bytes(n_rows, hidden)
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+
+    path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"
+    digest = hip_build.source_digest()
+    traffic = traffic_from_profiles(path, args.workload, digest)
+    roofline = {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                "traffic": traffic}
+
+    line = {
+        "metric": "fused add+RMSNorm HBM GB/s and % of peak, n=4096 x hidden=8192 bf16",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "add_rmsnorm_fwd rows=%d hidden=%d bf16, eps=1e-6, "
+                               "x,residual~N(0,1), weight~1+0.1N(0,1)" % (n_rows, hidden),
+                   "n_rows": n_rows, "hidden": hidden, "kernel": path,
+                   "buffer_sets": sets, "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+                   "wall_s_timed_region": round(wall_s, 4)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, r, w, eps, n_rows, hidden, args.cpu_seconds)
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,194 @@
+"""Python binding of libaddrmsnorm.so: fused residual-add + RMSNorm forward
+for MI355X (gfx950) with round-to-nearest-even bf16 stores.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C entry points declared in include/add_rmsnorm.h; the
+functions here carry the same names, take torch tensors (used only as device
+memory) and pass their pointers, shapes and the current HIP stream through.
+There is no fallback: without the built library, or without a GPU tensor,
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
+
+ABI_VERSION = 1
+MAX_HIDDEN = 32768
+
+OK = 0
+EINVAL = -1
+EALIGN = -2
+EALIAS = -3
+ERANGE = -4
+EHIP = -5
+
+PATH_AUTO = 0
+PATH_WAVE_ROW = 1
+PATH_WG_ROW = 2
+PATH_LDS_TWO_PASS = 3
+
+
+class AddRmsnormError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("add_rmsnorm status %d: %s" % (status, message))
+        self.status = status
+
+
+class LaunchCfg(ctypes.Structure):
+    """struct add_rmsnorm_launch_cfg."""
+    _fields_ = [("path", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("grid_blocks", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+_lib = None
+
+EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_test_cvt_range",
+           "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error", "add_rmsnorm_abi_version",
+           "add_rmsnorm_build_info")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise ImportError(
+            "%s is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')"
+            % LIBRARY)
+    L = ctypes.CDLL(LIBRARY)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    L.add_rmsnorm_fwd.restype = i32
+    L.add_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, vp]
+    L.add_rmsnorm_fwd_cfg.restype = i32
+    L.add_rmsnorm_fwd_cfg.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32,
+                                      ctypes.POINTER(LaunchCfg), vp]
+    L.add_rmsnorm_test_cvt_range.restype = i32
+    L.add_rmsnorm_test_cvt_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
+    L.add_rmsnorm_strerror.restype = ctypes.c_char_p
+    L.add_rmsnorm_strerror.argtypes = [i32]
+    L.add_rmsnorm_last_hip_error.restype = ctypes.c_char_p
+    L.add_rmsnorm_last_hip_error.argtypes = []
+    L.add_rmsnorm_abi_version.restype = i32
+    L.add_rmsnorm_abi_version.argtypes = []
+    L.add_rmsnorm_build_info.restype = ctypes.c_char_p
+    L.add_rmsnorm_build_info.argtypes = []
+    got = L.add_rmsnorm_abi_version()
+    if got != ABI_VERSION:
+        raise ImportError("libaddrmsnorm ABI %d, binding expects %d: rebuild" % (got, ABI_VERSION))
+    _lib = L
+    return L
+
+
+def add_rmsnorm_strerror(status: int) -> str:
+    return lib().add_rmsnorm_strerror(status).decode()
+
+
+def add_rmsnorm_last_hip_error() -> str:
+    return lib().add_rmsnorm_last_hip_error().decode()
+
+
+def add_rmsnorm_abi_version() -> int:
+    return int(lib().add_rmsnorm_abi_version())
+
+
+def add_rmsnorm_build_info() -> str:
+    return lib().add_rmsnorm_build_info().decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        msg = add_rmsnorm_strerror(status)
+        if status == EHIP:
+            msg += " (" + add_rmsnorm_last_hip_error() + ")"
+        raise AddRmsnormError(status, msg)
+
+
+def _rows_hidden(x, weight):
+    import torch
+
+    tensors = (x, weight)
+    for t in tensors:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("expected torch tensors")
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError("tensors must hold bf16 (bfloat16, or raw 16-bit patterns)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if weight.dim() != 1:
+        raise ValueError("weight must be 1-D [hidden]")
+    hidden = weight.shape[0]
+    if x.dim() < 1 or x.shape[-1] != hidden:
+        raise ValueError("x must be [..., hidden] with hidden = weight.shape[0]")
+    return x.numel() // hidden if hidden else 0, hidden
+
+
+def _stream_handle(device, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _marshal(out, residual_out, x, residual, weight):
+    for t in (out, residual_out, residual):
+        if t.shape != x.shape:
+            raise ValueError("out, residual_out and residual must have x's shape %s"
+                             % (tuple(x.shape),))
+        if t.device != x.device or weight.device != x.device:
+            raise ValueError("all tensors must be on one device")
+    n_rows, hidden = _rows_hidden(x, weight)
+    for t in (out, residual_out, residual):
+        _rows_hidden(t, weight)
+    return n_rows, hidden
+
+
+def add_rmsnorm_fwd(out, residual_out, x, residual, weight, eps: float = 1e-6,
+                    stream=None) -> None:
+    """out, residual_out <- fused add + RMSNorm of x, residual with weight.
+
+    All tensors bf16 on one GPU, contiguous, x/residual/out/residual_out of
+    shape [..., hidden] and weight [hidden].  Enqueued on ``stream`` (default:
+    torch's current stream for that device); does not synchronise.
+    """
+    import torch
+
+    n_rows, hidden = _marshal(out, residual_out, x, residual, weight)
+    with torch.cuda.device(x.device):
+        _check(lib().add_rmsnorm_fwd(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+                                     residual.data_ptr(), weight.data_ptr(), n_rows, hidden,
+                                     eps, _stream_handle(x.device, stream)))
+
+
+def add_rmsnorm_fwd_cfg(out, residual_out, x, residual, weight, eps: float = 1e-6,
+                        path: int = PATH_AUTO, block_threads: int = 0, grid_blocks: int = 0,
+                        stream=None) -> None:
+    """add_rmsnorm_fwd with an explicit launch configuration (same results)."""
+    import torch
+
+    n_rows, hidden = _marshal(out, residual_out, x, residual, weight)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    with torch.cuda.device(x.device):
+        _check(lib().add_rmsnorm_fwd_cfg(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+                                         residual.data_ptr(), weight.data_ptr(), n_rows, hidden,
+                                         eps, ctypes.byref(cfg),
+                                         _stream_handle(x.device, stream)))
+
+
+def add_rmsnorm_test_cvt_range(out, start: int, stream=None) -> None:
+    """out[i] <- bf16 (nearest-even, by the kernels' store routine) of the fp32
+    bit pattern (start + i) mod 2^32.  out: contiguous 16-bit GPU tensor."""
+    import torch
+
+    if not out.is_cuda or out.element_size() != 2 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous 16-bit GPU tensor")
+    with torch.cuda.device(out.device):
+        _check(lib().add_rmsnorm_test_cvt_range(out.data_ptr(), start & 0xFFFFFFFF, out.numel(),
+                                                _stream_handle(out.device, stream)))

@@ -1,0 +1,182 @@
+// C entry points of the fused residual-add + RMSNorm forward: argument
+// validation (on the host, before anything is enqueued), kernel choice by
+// hidden size, launch on the caller's stream.  The contract is documented in
+// include/add_rmsnorm.h.
+#include "add_rmsnorm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+#ifndef ADD_RMSNORM_BUILD_INFO
+#define ADD_RMSNORM_BUILD_INFO "unknown build"
+#endif
+
+namespace {
+
+thread_local char g_hip_error[256] = "no HIP error recorded";
+
+int hip_failure(hipError_t e) {
+  std::snprintf(g_hip_error, sizeof g_hip_error, "%s: %s", hipGetErrorName(e),
+                hipGetErrorString(e));
+  return ADD_RMSNORM_EHIP;
+}
+
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uint64_t pa = reinterpret_cast<uintptr_t>(a);
+  const uint64_t pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_block(int b) { return b == 64 || b == 128 || b == 256 || b == 512 || b == 1024; }
+
+// Smallest of 1, 2, 4, 8 that is >= need (0 if none).
+int pow2_at_least(int64_t need) {
+  for (int j = 1; j <= 8; j *= 2)
+    if (j >= need) return j;
+  return 0;
+}
+
+// Default workgroup sizes per path.
+constexpr int kWaveRowThreads = 256;
+constexpr int kWgRowThreads = 256;
+constexpr int kTwoPassThreads = 512;
+
+// Upper hidden sizes of the automatic choice.
+constexpr int64_t kWaveRowMaxHidden = 2048;
+constexpr int64_t kWgRowMaxHidden = 8192;
+
+int device_max_lds(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_failure(e);
+  e = hipDeviceGetAttribute(out, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return hip_failure(e);
+  return ADD_RMSNORM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
+                        const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
+                        int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                        struct ihipStream_t* stream) {
+  // Scalars first.
+  if (n_rows < 0 || hidden <= 0 || !std::isfinite(eps) || eps < 0.0f) return ADD_RMSNORM_EINVAL;
+  if (hidden % 8 != 0) return ADD_RMSNORM_EALIGN;
+  if (hidden > ADD_RMSNORM_MAX_HIDDEN) return ADD_RMSNORM_ERANGE;
+
+  add_rmsnorm_launch_cfg c = {ADD_RMSNORM_PATH_AUTO, 0, 0, 0};
+  if (cfg) c = *cfg;
+  if (c.flags != 0 || c.grid_blocks < -1) return ADD_RMSNORM_EINVAL;
+  if (c.path < ADD_RMSNORM_PATH_AUTO || c.path > ADD_RMSNORM_PATH_LDS_TWO_PASS)
+    return ADD_RMSNORM_EINVAL;
+  if (c.block_threads != 0 && !valid_block(c.block_threads)) return ADD_RMSNORM_EINVAL;
+
+  if (n_rows == 0) return ADD_RMSNORM_OK;
+
+  // Pointers.
+  if (!out || !residual_out || !x || !residual || !weight) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(out) || !aligned16(residual_out) || !aligned16(x) || !aligned16(residual) ||
+      !aligned16(weight))
+    return ADD_RMSNORM_EALIGN;
+  const uint64_t row_bytes = (uint64_t)hidden * 2;
+  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
+  const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
+  if (overlap(out, t_bytes, residual_out, t_bytes)) return ADD_RMSNORM_EALIAS;
+  const void* outs[2] = {out, residual_out};
+  for (const void* o : outs) {
+    if (overlap(o, t_bytes, x, t_bytes) || overlap(o, t_bytes, residual, t_bytes) ||
+        overlap(o, t_bytes, weight, row_bytes))
+      return ADD_RMSNORM_EALIAS;
+  }
+
+  // Path and shape.
+  int path = c.path;
+  if (path == ADD_RMSNORM_PATH_AUTO) {
+    path = hidden <= kWaveRowMaxHidden ? ADD_RMSNORM_PATH_WAVE_ROW
+           : hidden <= kWgRowMaxHidden ? ADD_RMSNORM_PATH_WG_ROW
+                                       : ADD_RMSNORM_PATH_LDS_TWO_PASS;
+  }
+  const int64_t segs = hidden / 8;
+  const addrms::FwdArgs a = {out, residual_out, x, residual, weight, n_rows, (int32_t)hidden,
+                             eps};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+
+  if (path == ADD_RMSNORM_PATH_WAVE_ROW) {
+    const int b = c.block_threads ? c.block_threads : kWaveRowThreads;
+    const int j = pow2_at_least((segs + 63) / 64);
+    if (j == 0 || !addrms::wave_row_supported(b, j)) return ADD_RMSNORM_ERANGE;
+    int64_t grid = c.grid_blocks;
+    if (grid == -1) grid = addrms::resident_blocks_wave_row(b, j);
+    e = addrms::launch_wave_row(a, b, j, grid, s);
+  } else if (path == ADD_RMSNORM_PATH_WG_ROW) {
+    const int b = c.block_threads ? c.block_threads : kWgRowThreads;
+    const int j = pow2_at_least((segs + b - 1) / b);
+    if (j == 0 || !addrms::wg_row_supported(b, j)) return ADD_RMSNORM_ERANGE;
+    int64_t grid = c.grid_blocks;
+    if (grid == -1) grid = addrms::resident_blocks_wg_row(b, j);
+    e = addrms::launch_wg_row(a, b, j, grid, s);
+  } else {
+    const int b = c.block_threads ? c.block_threads : kTwoPassThreads;
+    int max_lds = 0;
+    const int rc = device_max_lds(&max_lds);
+    if (rc != ADD_RMSNORM_OK) return rc;
+    if (addrms::lds_two_pass_lds_bytes((int)hidden) > (size_t)max_lds) return ADD_RMSNORM_ERANGE;
+    int64_t grid = c.grid_blocks;
+    if (grid == -1) grid = addrms::resident_blocks_lds_two_pass(b, (int)hidden);
+    e = addrms::launch_lds_two_pass(a, b, grid, s);
+  }
+  if (e != hipSuccess) return hip_failure(e);
+  return ADD_RMSNORM_OK;
+}
+
+int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
+                    const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
+                    int64_t hidden, float eps, struct ihipStream_t* stream) {
+  return add_rmsnorm_fwd_cfg(out, residual_out, x, residual, weight, n_rows, hidden, eps,
+                             nullptr, stream);
+}
+
+int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,
+                               struct ihipStream_t* stream) {
+  if (count < 0) return ADD_RMSNORM_EINVAL;
+  if (count % 8 != 0) return ADD_RMSNORM_EALIGN;
+  if (count == 0) return ADD_RMSNORM_OK;
+  if (!out) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(out)) return ADD_RMSNORM_EALIGN;
+  hipError_t e = addrms::launch_cvt_range(out, start, count, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_failure(e);
+  return ADD_RMSNORM_OK;
+}
+
+const char* add_rmsnorm_strerror(int status) {
+  switch (status) {
+    case ADD_RMSNORM_OK: return "success";
+    case ADD_RMSNORM_EINVAL:
+      return "invalid argument (null pointer, negative rows, hidden <= 0, bad eps or launch "
+             "configuration)";
+    case ADD_RMSNORM_EALIGN: return "a pointer is not 16-byte aligned, or hidden % 8 != 0";
+    case ADD_RMSNORM_EALIAS: return "an output overlaps an input or the other output";
+    case ADD_RMSNORM_ERANGE: return "hidden (or the problem size) is above what the path supports";
+    case ADD_RMSNORM_EHIP: return "the HIP launch failed (see add_rmsnorm_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+const char* add_rmsnorm_last_hip_error(void) { return g_hip_error; }
+
+int add_rmsnorm_abi_version(void) { return ADD_RMSNORM_ABI_VERSION; }
+
+const char* add_rmsnorm_build_info(void) { return ADD_RMSNORM_BUILD_INFO; }
+
+}  // extern "C"

@@ -1,0 +1,582 @@
+// Kernels of the fused residual-add + RMSNorm forward for gfx950 (MI355X).
+//
+// The operation is the reference() of the ROCm/aiter issue
+// "rmsnorm2d_fwd_with_add truncates fp32->bf16 on gfx942, biasing
+// residual_out and compounding across layers" ("Steps to Reproduce"), with
+// both bf16 stores rounded to nearest, ties to even, as its "Cost of fixing"
+// section asks for residual_out and as this library does for out too.
+//
+// Numerics shared by all three kernels (so that every path and every launch
+// shape produces the same bits):
+//   * bf16 -> fp32 widening is a 16-bit shift (exact).
+//   * acc = x + r is one IEEE fp32 add per element.
+//   * Both stores go through v_cvt_pk_bf16_f32, gfx950's packed fp32 -> bf16
+//     conversion, which rounds to nearest-even under the default MODE and
+//     keeps NaN a NaN (the aiter issue's Notes: on gfx942 the library's
+//     fallback truncated; gfx950 has the instruction).
+//   * The sum of squares follows one fixed tree that depends on hidden only.
+//     A segment is 8 consecutive elements (one 16-byte load); its sum is
+//     t = a0*a0, then t = fma(ak, ak, t) for k = 1..7.  Segment sums are then
+//     added by a balanced pairwise tree in index order, padded with +0 to a
+//     power of two.  Every subtree is an aligned block of segments, so a
+//     wavefront that holds 64 consecutive segments (one per lane) computes
+//     that block's subtree with a butterfly, and the block sums finish the
+//     tree in registers or through LDS, whatever the workgroup size.  Padding
+//     with more +0 leaves the result unchanged (x + 0 = x for the non-negative
+//     partial sums), so the tree is the same for every padded size.
+//   * rinv = 1 / sqrt(S / hidden + eps) with correctly rounded fp32 division
+//     and square root (HIP's defaults; no fast-math), once per row.
+//   * y = (acc * rinv) * w: two fp32 multiplies in that order; no contraction
+//     (built with -ffp-contract=off).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace addrms {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+#define DEV __device__ __forceinline__
+
+struct Params {
+  u32x4* out;
+  u32x4* residual_out;
+  const u32x4* x;
+  const u32x4* residual;
+  const u32x4* weight;
+  int64_t n_rows;
+  int32_t segs;  // hidden / 8
+  float hidden_f;
+  float eps;
+};
+
+// ---------------------------------------------------------------- memory
+
+// Streaming loads and stores: every byte of x, residual, out and residual_out
+// is touched once, so they bypass cache retention (nontemporal).  The weight
+// is re-read by every row and uses ordinary cached loads.
+DEV u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+DEV void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+// ---------------------------------------------------------------- numerics
+
+DEV void unpack8(u32x4 q, float (&a)[8]) {
+  a[0] = __builtin_bit_cast(float, q.x << 16);
+  a[1] = __builtin_bit_cast(float, q.x & 0xFFFF0000u);
+  a[2] = __builtin_bit_cast(float, q.y << 16);
+  a[3] = __builtin_bit_cast(float, q.y & 0xFFFF0000u);
+  a[4] = __builtin_bit_cast(float, q.z << 16);
+  a[5] = __builtin_bit_cast(float, q.z & 0xFFFF0000u);
+  a[6] = __builtin_bit_cast(float, q.w << 16);
+  a[7] = __builtin_bit_cast(float, q.w & 0xFFFF0000u);
+}
+
+// Two fp32 values -> two bf16 in one word (first value in the low half), by
+// the hardware's packed round-to-nearest-even conversion.
+DEV uint32_t pack2_rne(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+DEV u32x4 pack8_rne(const float (&a)[8]) {
+  u32x4 q;
+  q.x = pack2_rne(a[0], a[1]);
+  q.y = pack2_rne(a[2], a[3]);
+  q.z = pack2_rne(a[4], a[5]);
+  q.w = pack2_rne(a[6], a[7]);
+  return q;
+}
+
+// Sum of squares of one segment, in element order.
+DEV float seg_sumsq(const float (&a)[8]) {
+  float t = a[0] * a[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) t = __builtin_fmaf(a[k], a[k], t);
+  return t;
+}
+
+// Cross-lane moves.  Each level adds two aligned sibling sub-blocks; once a
+// sub-block holds one value in all its lanes, a mirror within the enclosing
+// block reaches the sibling just as an xor would.
+#define ADDRMS_DPP(v, ctrl) \
+  __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
+
+// Sum of the 64 lanes' values as a balanced pairwise tree over lane index:
+// (0,1) (2,3) ..., then aligned 4s, 8s, 16s, 32s, 64.  Returns the same bits
+// in every lane.  Must be called with all 64 lanes active.
+DEV float wave_block_sum(float v) {
+  v = v + ADDRMS_DPP(v, 0xB1);   // quad_perm [1,0,3,2]: lane ^ 1
+  v = v + ADDRMS_DPP(v, 0x4E);   // quad_perm [2,3,0,1]: lane ^ 2
+  v = v + ADDRMS_DPP(v, 0x141);  // row_half_mirror: the other quad of the 8
+  v = v + ADDRMS_DPP(v, 0x140);  // row_mirror: the other 8 of the 16
+  // ds_swizzle, bit-mask mode (and 0x1F, or 0, xor 0x10): lane ^ 16 within 32.
+  v = v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  return lo + hi;
+}
+
+// Balanced pairwise tree over N (a power of two) values in index order.
+template <int N>
+DEV float pairwise_tree(float (&v)[N]) {
+#pragma unroll
+  for (int n = N; n > 1; n >>= 1) {
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  }
+  return v[0];
+}
+
+template <int N>
+DEV float pairwise_tree_lds(const float* b) {
+  float v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = b[i];
+  return pairwise_tree<N>(v);
+}
+
+DEV float row_rinv(float sumsq, const Params& p) {
+  return 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
+}
+
+// out = bf16((acc * rinv) * w) for one segment.
+DEV u32x4 normalise8(const float (&acc)[8], float rinv, u32x4 wq) {
+  float w[8], y[8];
+  unpack8(wq, w);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = (acc[k] * rinv) * w[k];
+  return pack8_rne(y);
+}
+
+// acc = x + r for one segment; returns its sum of squares.
+DEV float add_segment(u32x4 xq, u32x4 rq, float (&acc)[8]) {
+  float xa[8], ra[8];
+  unpack8(xq, xa);
+  unpack8(rq, ra);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = xa[k] + ra[k];
+  return seg_sumsq(acc);
+}
+
+// ---------------------------------------------------------------- wave per row
+
+// WAVES rows per workgroup, one per wavefront; lane l holds segments
+// l, l + 64, ..., l + 64 (J - 1).  Block j of 64 segments is summed by one
+// butterfly; the J block sums finish the tree in registers.
+template <int WAVES, int J>
+__global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int C = p.segs;
+
+  u32x4 wq[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int s = lane + 64 * j;
+    wq[j] = s < C ? p.weight[s] : u32x4{0, 0, 0, 0};
+  }
+
+  const int64_t stride = (int64_t)gridDim.x * WAVES;
+  for (int64_t row = (int64_t)blockIdx.x * WAVES + wave; row < p.n_rows; row += stride) {
+    const size_t base = (size_t)row * (size_t)C;
+    u32x4 xq[J], rq[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int s = lane + 64 * j;
+      if (s < C) {
+        xq[j] = load_stream(p.x + base + s);
+        rq[j] = load_stream(p.residual + base + s);
+      } else {
+        xq[j] = u32x4{0, 0, 0, 0};
+        rq[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+    float acc[J][8];
+    float blk[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int s = lane + 64 * j;
+      blk[j] = add_segment(xq[j], rq[j], acc[j]);
+      if (s < C) store_stream(p.residual_out + base + s, pack8_rne(acc[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) blk[j] = wave_block_sum(blk[j]);
+    const float rinv = row_rinv(pairwise_tree<J>(blk), p);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int s = lane + 64 * j;
+      if (s < C) store_stream(p.out + base + s, normalise8(acc[j], rinv, wq[j]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- workgroup per row
+
+// B threads per row; thread t holds segments t, t + B, ..., t + B (J - 1).
+// For each j, wave w's butterfly yields the sum of block w + j * (B / 64);
+// the B / 64 * J block sums meet in LDS and every thread finishes the tree.
+template <int B, int J>
+__global__ __launch_bounds__(B) void k_wg_row(Params p) {
+  constexpr int W = B / 64;
+  constexpr int NB = W * J;
+  __shared__ float blk[2][NB];  // alternates by row so one barrier per row suffices
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int C = p.segs;
+
+  u32x4 wq[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int s = t + B * j;
+    wq[j] = s < C ? p.weight[s] : u32x4{0, 0, 0, 0};
+  }
+
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x, parity ^= 1) {
+    const size_t base = (size_t)row * (size_t)C;
+    u32x4 xq[J], rq[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int s = t + B * j;
+      if (s < C) {
+        xq[j] = load_stream(p.x + base + s);
+        rq[j] = load_stream(p.residual + base + s);
+      } else {
+        xq[j] = u32x4{0, 0, 0, 0};
+        rq[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+    float acc[J][8];
+    float bs[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int s = t + B * j;
+      bs[j] = add_segment(xq[j], rq[j], acc[j]);
+      if (s < C) store_stream(p.residual_out + base + s, pack8_rne(acc[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) bs[j] = wave_block_sum(bs[j]);
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) blk[parity][wave + W * j] = bs[j];
+    }
+    __syncthreads();
+    const float rinv = row_rinv(pairwise_tree_lds<NB>(blk[parity]), p);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int s = t + B * j;
+      if (s < C) store_stream(p.out + base + s, normalise8(acc[j], rinv, wq[j]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- LDS two-pass
+
+// B threads per row.  Pass 1 walks the row in chunks of B segments: acc,
+// residual_out, the segment's fp32 values staged in LDS (two planes of
+// 16 bytes per segment, so a wavefront's accesses are contiguous), and one
+// block sum per wave per chunk.  After one barrier every thread finishes the
+// tree over NB padded block sums; pass 2 reads the staged values back (each
+// thread only its own) and writes out.
+template <int B, int NB>
+__global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
+  constexpr int W = B / 64;
+  __shared__ float blk[NB];
+  extern __shared__ float4 stage[];  // [2][C]: elements 0-3, then 4-7, of each segment
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int C = p.segs;
+  const int chunks = (C + B - 1) / B;
+  float4* lo = stage;
+  float4* hi = stage + C;
+
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
+    const size_t base = (size_t)row * (size_t)C;
+    // Blocks past the row's last chunk are +0.
+    for (int i = chunks * W + t; i < NB; i += B) blk[i] = 0.0f;
+    for (int c = 0; c < chunks; ++c) {
+      const int s = c * B + t;
+      u32x4 xq = {0, 0, 0, 0}, rq = {0, 0, 0, 0};
+      if (s < C) {
+        xq = load_stream(p.x + base + s);
+        rq = load_stream(p.residual + base + s);
+      }
+      float acc[8];
+      float bs = add_segment(xq, rq, acc);
+      if (s < C) {
+        store_stream(p.residual_out + base + s, pack8_rne(acc));
+        lo[s] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        hi[s] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      }
+      bs = wave_block_sum(bs);
+      if (lane == 0) blk[c * W + wave] = bs;
+    }
+    __syncthreads();
+    const float rinv = row_rinv(pairwise_tree_lds<NB>(blk), p);
+    for (int c = 0; c < chunks; ++c) {
+      const int s = c * B + t;
+      if (s < C) {
+        const float4 l = lo[s], h = hi[s];
+        const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
+        store_stream(p.out + base + s, normalise8(acc, rinv, p.weight[s]));
+      }
+    }
+    __syncthreads();  // blk is rewritten by the next row
+  }
+}
+
+// ---------------------------------------------------------------- epilogue test
+
+__global__ __launch_bounds__(256) void k_cvt_range(u32x4* out, uint32_t start, int64_t groups) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
+    const uint32_t u0 = start + (uint32_t)(g * 8);
+    float a[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = __builtin_bit_cast(float, u0 + (uint32_t)k);
+    out[g] = pack8_rne(a);
+  }
+}
+
+// ---------------------------------------------------------------- launch helpers
+
+Params make_params(const FwdArgs& a) {
+  Params p;
+  p.out = reinterpret_cast<u32x4*>(a.out);
+  p.residual_out = reinterpret_cast<u32x4*>(a.residual_out);
+  p.x = reinterpret_cast<const u32x4*>(a.x);
+  p.residual = reinterpret_cast<const u32x4*>(a.residual);
+  p.weight = reinterpret_cast<const u32x4*>(a.weight);
+  p.n_rows = a.n_rows;
+  p.segs = a.hidden / 8;
+  p.hidden_f = (float)a.hidden;
+  p.eps = a.eps;
+  return p;
+}
+
+// Grid size: an explicit block count, else one workgroup per row group
+// (capped; the kernels loop over any rows beyond the grid).
+unsigned grid_for(int64_t grid_blocks, int64_t row_groups) {
+  const int64_t cap = (int64_t)1 << 30;
+  int64_t g = grid_blocks > 0 ? grid_blocks : row_groups;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+template <typename K>
+int64_t resident(K kernel, int block_threads, size_t lds) {
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, lds) !=
+      hipSuccess)
+    return 0;
+  return (int64_t)per_cu * cus;
+}
+
+template <int WAVES, int J>
+hipError_t go_wave(const Params& p, int64_t grid_blocks, hipStream_t s) {
+  const int64_t groups = (p.n_rows + WAVES - 1) / WAVES;
+  hipLaunchKernelGGL((k_wave_row<WAVES, J>), dim3(grid_for(grid_blocks, groups)),
+                     dim3(WAVES * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+// Combinations that would not fit the register file (segments held per thread
+// times threads per workgroup) are not built; wave_row_supported() and
+// wg_row_supported() say which exist.
+template <int WAVES>
+hipError_t go_wave_j(const Params& p, int j, int64_t grid_blocks, hipStream_t s) {
+  switch (j) {
+    case 1: return go_wave<WAVES, 1>(p, grid_blocks, s);
+    case 2: return go_wave<WAVES, 2>(p, grid_blocks, s);
+    case 4: return go_wave<WAVES, 4>(p, grid_blocks, s);
+    case 8:
+      if constexpr (WAVES < 16) return go_wave<WAVES, 8>(p, grid_blocks, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int B, int J>
+hipError_t go_wg(const Params& p, int64_t grid_blocks, hipStream_t s) {
+  hipLaunchKernelGGL((k_wg_row<B, J>), dim3(grid_for(grid_blocks, p.n_rows)), dim3(B), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t go_wg_j(const Params& p, int j, int64_t grid_blocks, hipStream_t s) {
+  switch (j) {
+    case 1: return go_wg<B, 1>(p, grid_blocks, s);
+    case 2: return go_wg<B, 2>(p, grid_blocks, s);
+    case 4:
+      if constexpr (B * 4 <= 2048) return go_wg<B, 4>(p, grid_blocks, s);
+      break;
+    case 8:
+      if constexpr (B * 8 <= 2048) return go_wg<B, 8>(p, grid_blocks, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+// Padded block count of the two-pass tree: 32 blocks of 64 segments cover
+// hidden <= 16384, 64 cover the library's maximum.
+int two_pass_nb(int hidden) { return hidden <= 16384 ? 32 : 64; }
+
+template <int B, int NB>
+hipError_t go_two_pass(const Params& p, int64_t grid_blocks, hipStream_t s) {
+  const size_t lds = (size_t)p.segs * 32;
+  hipLaunchKernelGGL((k_lds_two_pass<B, NB>), dim3(grid_for(grid_blocks, p.n_rows)), dim3(B),
+                     lds, s, p);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t go_two_pass_nb(const Params& p, int hidden, int64_t grid_blocks, hipStream_t s) {
+  if (two_pass_nb(hidden) == 32) return go_two_pass<B, 32>(p, grid_blocks, s);
+  return go_two_pass<B, 64>(p, grid_blocks, s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- internal API
+
+hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
+                           int64_t grid_blocks, hipStream_t s) {
+  const Params p = make_params(a);
+  switch (block_threads) {
+    case 64: return go_wave_j<1>(p, segs_per_lane, grid_blocks, s);
+    case 128: return go_wave_j<2>(p, segs_per_lane, grid_blocks, s);
+    case 256: return go_wave_j<4>(p, segs_per_lane, grid_blocks, s);
+    case 512: return go_wave_j<8>(p, segs_per_lane, grid_blocks, s);
+    case 1024: return go_wave_j<16>(p, segs_per_lane, grid_blocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_wg_row(const FwdArgs& a, int block_threads, int segs_per_thread,
+                         int64_t grid_blocks, hipStream_t s) {
+  const Params p = make_params(a);
+  switch (block_threads) {
+    case 64: return go_wg_j<64>(p, segs_per_thread, grid_blocks, s);
+    case 128: return go_wg_j<128>(p, segs_per_thread, grid_blocks, s);
+    case 256: return go_wg_j<256>(p, segs_per_thread, grid_blocks, s);
+    case 512: return go_wg_j<512>(p, segs_per_thread, grid_blocks, s);
+    case 1024: return go_wg_j<1024>(p, segs_per_thread, grid_blocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_lds_two_pass(const FwdArgs& a, int block_threads, int64_t grid_blocks,
+                               hipStream_t s) {
+  const Params p = make_params(a);
+  switch (block_threads) {
+    case 64: return go_two_pass_nb<64>(p, a.hidden, grid_blocks, s);
+    case 128: return go_two_pass_nb<128>(p, a.hidden, grid_blocks, s);
+    case 256: return go_two_pass_nb<256>(p, a.hidden, grid_blocks, s);
+    case 512: return go_two_pass_nb<512>(p, a.hidden, grid_blocks, s);
+    case 1024: return go_two_pass_nb<1024>(p, a.hidden, grid_blocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool wave_row_supported(int block_threads, int segs_per_lane) {
+  return !(block_threads == 1024 && segs_per_lane == 8);
+}
+
+bool wg_row_supported(int block_threads, int segs_per_thread) {
+  return block_threads * segs_per_thread <= 2048;
+}
+
+size_t lds_two_pass_lds_bytes(int hidden) {
+  return (size_t)(hidden / 8) * 32 + (size_t)two_pass_nb(hidden) * sizeof(float);
+}
+
+namespace {
+template <int WAVES>
+int64_t res_wave(int j) {
+  switch (j) {
+    case 1: return resident(k_wave_row<WAVES, 1>, WAVES * 64, 0);
+    case 2: return resident(k_wave_row<WAVES, 2>, WAVES * 64, 0);
+    case 4: return resident(k_wave_row<WAVES, 4>, WAVES * 64, 0);
+    case 8:
+      if constexpr (WAVES < 16) return resident(k_wave_row<WAVES, 8>, WAVES * 64, 0);
+      break;
+  }
+  return 0;
+}
+template <int B>
+int64_t res_wg(int j) {
+  switch (j) {
+    case 1: return resident(k_wg_row<B, 1>, B, 0);
+    case 2: return resident(k_wg_row<B, 2>, B, 0);
+    case 4:
+      if constexpr (B * 4 <= 2048) return resident(k_wg_row<B, 4>, B, 0);
+      break;
+    case 8:
+      if constexpr (B * 8 <= 2048) return resident(k_wg_row<B, 8>, B, 0);
+      break;
+  }
+  return 0;
+}
+template <int B>
+int64_t res_two_pass(int hidden) {
+  const size_t lds = (size_t)(hidden / 8) * 32;
+  if (two_pass_nb(hidden) == 32) return resident(k_lds_two_pass<B, 32>, B, lds);
+  return resident(k_lds_two_pass<B, 64>, B, lds);
+}
+}  // namespace
+
+int64_t resident_blocks_wave_row(int block_threads, int segs_per_lane) {
+  switch (block_threads) {
+    case 64: return res_wave<1>(segs_per_lane);
+    case 128: return res_wave<2>(segs_per_lane);
+    case 256: return res_wave<4>(segs_per_lane);
+    case 512: return res_wave<8>(segs_per_lane);
+    case 1024: return res_wave<16>(segs_per_lane);
+  }
+  return 0;
+}
+
+int64_t resident_blocks_wg_row(int block_threads, int segs_per_thread) {
+  switch (block_threads) {
+    case 64: return res_wg<64>(segs_per_thread);
+    case 128: return res_wg<128>(segs_per_thread);
+    case 256: return res_wg<256>(segs_per_thread);
+    case 512: return res_wg<512>(segs_per_thread);
+    case 1024: return res_wg<1024>(segs_per_thread);
+  }
+  return 0;
+}
+
+int64_t resident_blocks_lds_two_pass(int block_threads, int hidden) {
+  switch (block_threads) {
+    case 64: return res_two_pass<64>(hidden);
+    case 128: return res_two_pass<128>(hidden);
+    case 256: return res_two_pass<256>(hidden);
+    case 512: return res_two_pass<512>(hidden);
+    case 1024: return res_two_pass<1024>(hidden);
+  }
+  return 0;
+}
+
+hipError_t launch_cvt_range(uint16_t* out, uint32_t start, int64_t count, hipStream_t s) {
+  const int64_t groups = count / 8;
+  int64_t blocks = (groups + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_cvt_range, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<u32x4*>(out), start, groups);
+  return hipGetLastError();
+}
+
+}  // namespace addrms

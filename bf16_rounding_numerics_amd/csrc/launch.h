@@ -1,0 +1,56 @@
+// Internal interface between the C entry points (api.cpp) and the kernels
+// (kernels.hip).  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace addrms {
+
+struct FwdArgs {
+  uint16_t* out;
+  uint16_t* residual_out;
+  const uint16_t* x;
+  const uint16_t* residual;
+  const uint16_t* weight;
+  int64_t n_rows;
+  int32_t hidden;  // multiple of 8
+  float eps;
+};
+
+// Largest number of 8-element segments any row can have.
+constexpr int kMaxSegments = 32768 / 8;
+
+// One wavefront per row, block_threads / 64 rows per workgroup.  The row's
+// segments are spread over the 64 lanes, segs_per_lane (1, 2, 4 or 8) each.
+// grid_blocks > 0 launches that many workgroups, which loop over the rows.
+hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
+                           int64_t grid_blocks, hipStream_t stream);
+
+// One workgroup of block_threads per row, the row in registers:
+// segs_per_thread (1, 2, 4 or 8) segments per thread.
+hipError_t launch_wg_row(const FwdArgs& a, int block_threads, int segs_per_thread,
+                         int64_t grid_blocks, hipStream_t stream);
+
+// One workgroup per row; pass 1 streams the row in chunks of block_threads
+// segments, storing residual_out and staging fp32 sums in LDS; pass 2
+// normalises from LDS.  lds_two_pass_lds_bytes() gives its LDS size.
+hipError_t launch_lds_two_pass(const FwdArgs& a, int block_threads, int64_t grid_blocks,
+                               hipStream_t stream);
+size_t lds_two_pass_lds_bytes(int hidden);
+
+// Which (workgroup size, segments per thread) pairs are built: those whose
+// per-thread row share fits the register file without spilling.
+bool wave_row_supported(int block_threads, int segs_per_lane);
+bool wg_row_supported(int block_threads, int segs_per_thread);
+
+// Workgroups of the given kernel that fit on the current device at once
+// (occupancy x compute units); 0 if the query fails.
+int64_t resident_blocks_wave_row(int block_threads, int segs_per_lane);
+int64_t resident_blocks_wg_row(int block_threads, int segs_per_thread);
+int64_t resident_blocks_lds_two_pass(int block_threads, int hidden);
+
+// Test hook: the store epilogue applied to consecutive fp32 bit patterns.
+hipError_t launch_cvt_range(uint16_t* out, uint32_t start, int64_t count, hipStream_t stream);
+
+}  // namespace addrms

@@ -1,0 +1,147 @@
+/*
+ * add_rmsnorm.h -- fused residual-add + RMSNorm forward for MI355X (gfx950),
+ * bf16 storage, round-to-nearest-even on both stores.
+ *
+ * The operation is the one the ROCm/aiter issue "rmsnorm2d_fwd_with_add
+ * truncates fp32->bf16 on gfx942, biasing residual_out and compounding across
+ * layers" defines in the reference() function of its "Steps to Reproduce"
+ * script, with the rounding that its "Cost of fixing" and "Additional
+ * Information" sections ask for (round to nearest, ties to even, never
+ * truncation).  Per row i of n_rows and column j of hidden:
+ *
+ *   acc_j          = fp32(x[i,j]) + fp32(residual[i,j])          (IEEE fp32 add)
+ *   residual_out_j = bf16_rne(acc_j)
+ *   S              = sum_j acc_j^2                                 (fp32, fixed tree)
+ *   rinv           = 1 / sqrt(S / hidden + eps)                    (fp32, correctly rounded)
+ *   out[i,j]       = bf16_rne((acc_j * rinv) * fp32(weight[j]))
+ *
+ * Results are bit-identical across runs, launch configurations and kernel
+ * paths: the sum of squares always follows one reduction tree that depends on
+ * hidden only (8-element segments summed in order by fused multiply-add, then
+ * a balanced pairwise tree over the segments in index order, padded with +0
+ * to a power of two).  residual_out equals the correctly rounded bf16 of the
+ * exact x + residual; out is within one bf16 ULP of the correctly rounded
+ * real value.
+ *
+ * Conventions shared by every entry point below:
+ *   - Tensors are raw bf16 bit patterns (uint16_t), row-major and contiguous:
+ *     x, residual, out, residual_out are [n_rows, hidden], weight is [hidden].
+ *   - All tensor pointers are DEVICE pointers (HIP device memory, or memory
+ *     the device can address), 16-byte aligned.  The caller owns them; the
+ *     library never allocates, frees or synchronises, keeps no state between
+ *     calls, and is safe to call from several host threads.
+ *   - Work is enqueued on `stream` (NULL = the null stream) and the call
+ *     returns without waiting.  The caller synchronises before reading.
+ *   - Argument errors are detected on the host, before anything is enqueued,
+ *     and returned as a negative status; nothing is written then.  NaN and
+ *     Inf in the data are not errors: they propagate per IEEE arithmetic.
+ */
+#ifndef ADD_RMSNORM_H
+#define ADD_RMSNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t is a pointer to this opaque struct. */
+struct ihipStream_t;
+
+#define ADD_RMSNORM_ABI_VERSION 1
+
+/* Largest supported hidden size. */
+#define ADD_RMSNORM_MAX_HIDDEN 32768
+
+/* Status codes. */
+#define ADD_RMSNORM_OK 0
+#define ADD_RMSNORM_EINVAL (-1) /* null pointer, n_rows < 0, hidden <= 0, eps < 0 or not finite, bad cfg */
+#define ADD_RMSNORM_EALIGN (-2) /* a pointer not 16-byte aligned, or hidden % 8 != 0 */
+#define ADD_RMSNORM_EALIAS (-3) /* an output overlaps an input or the other output */
+#define ADD_RMSNORM_ERANGE (-4) /* hidden above the maximum (of the library, the chosen path or the device) */
+#define ADD_RMSNORM_EHIP (-5)   /* the HIP launch failed; add_rmsnorm_last_hip_error() has the detail */
+
+/*
+ * The fused forward.
+ *   out           [n_rows, hidden] bf16, written: the normalised, weighted rows.
+ *   residual_out  [n_rows, hidden] bf16, written: x + residual.
+ *   x, residual   [n_rows, hidden] bf16, read.
+ *   weight        [hidden] bf16, read.
+ *   n_rows >= 0 (0 enqueues nothing and returns OK; pointers are not checked),
+ *   8 <= hidden <= ADD_RMSNORM_MAX_HIDDEN with hidden % 8 == 0,
+ *   eps finite and >= 0, added to the mean of squares inside the square root.
+ * Outputs must not overlap inputs or each other (no in-place operation).
+ * The kernel is chosen by hidden: one wavefront per row up to 2048, one
+ * workgroup per row with the row held in registers up to 8192, and above
+ * that one workgroup per row that stages the row's fp32 sums in LDS and
+ * normalises in a second pass over LDS.
+ * Returns ADD_RMSNORM_OK or a negative status.
+ */
+int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
+                    const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
+                    int64_t hidden, float eps, struct ihipStream_t* stream);
+
+/* Kernel paths for add_rmsnorm_fwd_cfg. */
+#define ADD_RMSNORM_PATH_AUTO 0
+#define ADD_RMSNORM_PATH_WAVE_ROW 1     /* hidden <= 4096 (2048 with 1024 threads) when forced */
+#define ADD_RMSNORM_PATH_WG_ROW 2       /* hidden <= min(64 * block_threads, 16384) when forced */
+#define ADD_RMSNORM_PATH_LDS_TWO_PASS 3 /* any supported hidden */
+
+/*
+ * Launch configuration, for tests and benchmarks that must show that results
+ * do not depend on it.  Every field 0 means "the library's choice".
+ *   path           one of ADD_RMSNORM_PATH_*.
+ *   block_threads  workgroup size: 64, 128, 256, 512 or 1024 (the wave path
+ *                  runs block_threads / 64 rows per workgroup).
+ *   grid_blocks    0: one workgroup per row (per row group on the wave path);
+ *                  > 0: exactly that many workgroups, each looping over rows
+ *                  (a persistent grid); -1: as many as fit on the device at
+ *                  once.
+ *   flags          must be 0.
+ */
+struct add_rmsnorm_launch_cfg {
+  int32_t path;
+  int32_t block_threads;
+  int32_t grid_blocks;
+  int32_t flags;
+};
+
+/*
+ * add_rmsnorm_fwd with an explicit launch configuration (cfg may be NULL,
+ * meaning all defaults).  Same arguments, results and errors as
+ * add_rmsnorm_fwd; a configuration the chosen path cannot run returns
+ * ADD_RMSNORM_EINVAL (bad field) or ADD_RMSNORM_ERANGE (hidden too large for
+ * that path).  The numerical result is the same for every configuration.
+ */
+int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
+                        const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
+                        int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                        struct ihipStream_t* stream);
+
+/*
+ * Test hook for the store epilogue: out[i] = bf16_rne of the fp32 whose bit
+ * pattern is (start + i) mod 2^32, for 0 <= i < count, converted by the same
+ * device routine that rounds both stores of the fused kernels.  out is a
+ * device pointer to count uint16_t, 16-byte aligned; count >= 0 and a
+ * multiple of 8.  Enqueued on stream like the forward.
+ */
+int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,
+                               struct ihipStream_t* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* add_rmsnorm_strerror(int status);
+
+/* Text of the HIP error behind the last ADD_RMSNORM_EHIP on this thread. */
+const char* add_rmsnorm_last_hip_error(void);
+
+/* ADD_RMSNORM_ABI_VERSION of the built library; bindings refuse a mismatch. */
+int add_rmsnorm_abi_version(void);
+
+/* Target architecture, compiler flags and source digest of the build. */
+const char* add_rmsnorm_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADD_RMSNORM_H */

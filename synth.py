@@ -23,6 +23,7 @@ x of chain step k = 1000 + k (the pages reseed each chain step with 1000+step).
 from __future__ import annotations
 
 import hashlib
+import os
 
 import numpy as np
 
@@ -61,26 +62,50 @@ def splitmix64(s0: int, start: int, count: int) -> np.ndarray:
         return _mix(np.uint64(s0 & _MASK) + i * GAMMA)
 
 
+def _normal_pairs(key: int, p0: int, p1: int) -> np.ndarray:
+    """Box-Muller deviates 2*p0 .. 2*p1-1 of the stream with state key."""
+    z = splitmix64(key, 2 * p0, 2 * (p1 - p0))
+    scale = 2.0 ** -53
+    u1 = ((z[0::2] >> np.uint64(11)) + np.uint64(1)).astype(np.float64) * scale
+    u2 = (z[1::2] >> np.uint64(11)).astype(np.float64) * scale
+    rad = np.sqrt(-2.0 * np.log(u1))
+    th = (2.0 * np.pi) * u2
+    pair = np.empty((p1 - p0, 2), dtype=np.float64)
+    pair[:, 0] = rad * np.cos(th)
+    pair[:, 1] = rad * np.sin(th)
+    return pair.reshape(-1)
+
+
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+
+        _POOL = ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1)))
+    return _POOL
+
+
 def normal(seed: int, stream: int, n: int, mean: float = 0.0, std: float = 1.0,
-           chunk: int = 1 << 22) -> np.ndarray:
-    """n binary64 normal deviates mean + std * N(0, 1) (Box-Muller)."""
+           chunk: int = 1 << 20) -> np.ndarray:
+    """n binary64 normal deviates mean + std * N(0, 1) (Box-Muller).
+
+    Chunks are computed on a thread pool (numpy releases the GIL); the values
+    depend only on (seed, stream, index), not on the chunking.
+    """
     key = stream_key(seed, stream)
     out = np.empty(n, dtype=np.float64)
     pairs = (n + 1) // 2
-    two_pi = 2.0 * np.pi
-    scale = 2.0 ** -53
-    for p0 in range(0, pairs, chunk):
+
+    def work(p0):
         p1 = min(pairs, p0 + chunk)
-        z = splitmix64(key, 2 * p0, 2 * (p1 - p0))
-        u1 = ((z[0::2] >> np.uint64(11)) + np.uint64(1)).astype(np.float64) * scale
-        u2 = (z[1::2] >> np.uint64(11)).astype(np.float64) * scale
-        rad = np.sqrt(-2.0 * np.log(u1))
-        th = two_pi * u2
-        pair = np.empty((p1 - p0, 2), dtype=np.float64)
-        pair[:, 0] = rad * np.cos(th)
-        pair[:, 1] = rad * np.sin(th)
+        vals = _normal_pairs(key, p0, p1)
         lo, hi = 2 * p0, min(n, 2 * p1)
-        out[lo:hi] = pair.reshape(-1)[: hi - lo]
+        out[lo:hi] = vals[: hi - lo]
+
+    list(_pool().map(work, range(0, pairs, chunk)))
     return mean + std * out
 
 

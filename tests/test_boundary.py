@@ -1,0 +1,200 @@
+"""The C-ABI boundary, on the CPU: the library loads, exports every entry point
+include/*.h declares, and rejects bad arguments on the host before any HIP
+call.  (No computation runs here; that needs the GPU.)"""
+import ctypes
+import glob
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import bf16_rounding_numerics_amd as arn
+from bf16_rounding_numerics_amd import build as hip_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M):
+            if not m.group(0).lstrip().startswith("#"):
+                names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(arn.EXPORTS) == set(names), names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", arn.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(arn.lib(), name)
+
+
+def test_abi_version_matches_header():
+    hdr = open(os.path.join(ROOT, "include", "add_rmsnorm.h")).read()
+    v = int(re.search(r"#define ADD_RMSNORM_ABI_VERSION (\d+)", hdr).group(1))
+    assert arn.add_rmsnorm_abi_version() == v == arn.ABI_VERSION
+    m = int(re.search(r"#define ADD_RMSNORM_MAX_HIDDEN (\d+)", hdr).group(1))
+    assert m == arn.MAX_HIDDEN
+
+
+def test_build_info_names_target_flags_and_current_sources():
+    info = arn.add_rmsnorm_build_info()
+    assert "arch=gfx950" in info
+    for flag in ("-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+                 "-fhip-fp32-correctly-rounded-divide-sqrt", "-packed-fp32-ops"):
+        assert flag in info
+    # A library built from other sources than the tree's is stale.
+    assert "sources_sha256=" + hip_build.source_digest() in info
+
+
+def test_strerror_texts():
+    texts = {s: arn.add_rmsnorm_strerror(s) for s in (0, -1, -2, -3, -4, -5)}
+    assert len(set(texts.values())) == 6
+    assert arn.add_rmsnorm_strerror(-99) == "unknown status"
+
+
+# ---------------------------------------------------------------- validation
+
+A = 1 << 20  # fake, 16-byte aligned "device" addresses far apart
+MB = 1 << 24
+
+
+def _gpu_visible():
+    import torch
+
+    return torch.cuda.device_count() > 0
+
+
+# Every call below must be rejected before a launch; where a GPU is visible
+# they are skipped anyway, so that fake addresses can never reach a kernel.
+fake_addresses = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: CPU only")
+
+
+def call(out=A, res=A + MB, x=A + 2 * MB, r=A + 3 * MB, w=A + 4 * MB, n=4, h=64, eps=1e-6,
+         cfg=None):
+    L = arn.lib()
+    if cfg is None:
+        return L.add_rmsnorm_fwd(out, res, x, r, w, n, h, eps, None)
+    c = arn.LaunchCfg(*cfg)
+    return L.add_rmsnorm_fwd_cfg(out, res, x, r, w, n, h, eps, ctypes.byref(c), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), arn.EINVAL),
+    (dict(h=0), arn.EINVAL),
+    (dict(h=-8), arn.EINVAL),
+    (dict(eps=-1.0), arn.EINVAL),
+    (dict(eps=math.nan), arn.EINVAL),
+    (dict(eps=math.inf), arn.EINVAL),
+    (dict(h=12), arn.EALIGN),
+    (dict(h=4), arn.EALIGN),
+    (dict(h=32776), arn.ERANGE),
+    (dict(out=0), arn.EINVAL),
+    (dict(res=0), arn.EINVAL),
+    (dict(x=0), arn.EINVAL),
+    (dict(r=0), arn.EINVAL),
+    (dict(w=0), arn.EINVAL),
+    (dict(x=A + 2 * MB + 8), arn.EALIGN),
+    (dict(w=A + 4 * MB + 2), arn.EALIGN),
+    (dict(out=A + 2 * MB), arn.EALIAS),                 # out == x
+    (dict(res=A + 3 * MB), arn.EALIAS),                 # residual_out == residual
+    (dict(res=A + 4 * 64 * 2 - 16), arn.EALIAS),        # residual_out overlaps out's tail
+    (dict(res=A + 4 * MB + 64), arn.EALIAS),            # residual_out overlaps weight
+    (dict(n=1 << 62, h=8), arn.ERANGE),                 # byte count overflows
+])
+@fake_addresses
+def test_argument_errors(kw, status):
+    assert call(**kw) == status
+
+
+@fake_addresses
+def test_zero_rows_is_a_no_op_without_pointer_checks():
+    assert call(out=0, res=0, x=0, r=0, w=0, n=0) == arn.OK
+    assert call(n=0) == arn.OK
+
+
+@fake_addresses
+def test_adjacent_buffers_are_not_overlap():
+    # residual_out right after out: touching, not overlapping.  A forced path
+    # that cannot take hidden = 8192 is rejected after the overlap checks, so
+    # ERANGE (not EALIAS) shows the adjacent buffers passed, and nothing is
+    # launched with these fake addresses.
+    assert call(res=A + 4 * 8192 * 2, h=8192, x=A + 8 * MB, r=A + 9 * MB, w=A + 10 * MB,
+                cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.ERANGE
+    assert call(res=A + 4 * 8192 * 2 - 16, h=8192, x=A + 8 * MB, r=A + 9 * MB, w=A + 10 * MB,
+                cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.EALIAS
+
+
+@pytest.mark.parametrize("cfg,status", [
+    ((0, 0, 0, 1), arn.EINVAL),                 # flags must be 0
+    ((9, 0, 0, 0), arn.EINVAL),                 # unknown path
+    ((-1, 0, 0, 0), arn.EINVAL),
+    ((0, 100, 0, 0), arn.EINVAL),               # not a supported workgroup size
+    ((0, 2048, 0, 0), arn.EINVAL),
+    ((0, 0, -2, 0), arn.EINVAL),                # grid_blocks below -1
+])
+@fake_addresses
+def test_bad_launch_configuration(cfg, status):
+    assert call(cfg=cfg) == status
+
+
+@pytest.mark.parametrize("path,block,h", [
+    (arn.PATH_WAVE_ROW, 0, 8192),       # more than 8 segments per lane
+    (arn.PATH_WAVE_ROW, 1024, 4096),    # 8 per lane at 1024 threads is not built
+    (arn.PATH_WG_ROW, 64, 8192),
+    (arn.PATH_WG_ROW, 1024, 32768),     # 4 per thread at 1024 threads is not built
+    (arn.PATH_WG_ROW, 0, 32768),
+])
+@fake_addresses
+def test_forced_path_outside_its_range(path, block, h):
+    assert call(h=h, cfg=(path, block, 0, 0)) == arn.ERANGE
+
+
+@fake_addresses
+def test_cvt_range_errors():
+    L = arn.lib()
+    assert L.add_rmsnorm_test_cvt_range(A, 0, -8, None) == arn.EINVAL
+    assert L.add_rmsnorm_test_cvt_range(A, 0, 12, None) == arn.EALIGN
+    assert L.add_rmsnorm_test_cvt_range(A + 4, 0, 16, None) == arn.EALIGN
+    assert L.add_rmsnorm_test_cvt_range(0, 0, 16, None) == arn.EINVAL
+    assert L.add_rmsnorm_test_cvt_range(0, 0, 0, None) == arn.OK
+
+
+# ---------------------------------------------------------------- binding
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        arn.add_rmsnorm_fwd(torch.empty_like(x), torch.empty_like(x), x, x.clone(), w)
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(arn, "_lib", None)
+    monkeypatch.setattr(arn, "LIBRARY", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        arn.lib()
+
+
+def test_status_codes_match_header():
+    hdr = open(os.path.join(ROOT, "include", "add_rmsnorm.h")).read()
+    for name in ("OK", "EINVAL", "EALIGN", "EALIAS", "ERANGE", "EHIP"):
+        m = re.search(r"#define ADD_RMSNORM_%s \(?(-?\d+)\)?" % name, hdr)
+        assert int(m.group(1)) == getattr(arn, name), name
+    for name in ("AUTO", "WAVE_ROW", "WG_ROW", "LDS_TWO_PASS"):
+        m = re.search(r"#define ADD_RMSNORM_PATH_%s (\d+)" % name, hdr)
+        assert int(m.group(1)) == getattr(arn, "PATH_" + name), name

@@ -1,0 +1,97 @@
+"""Bitwise invariance of the HIP path (GPU): results must not depend on the
+kernel path, workgroup size, grid shape, repetition or batch composition.
+
+The determinism failure on the ROCm TransformerEngine issue "CP LSE merge
+switches compiled variants on ROCm, breaking forward reproducibility" came
+from one computation compiled into launch-configuration-dependent variants;
+its Root cause section sweeps launch configurations and counts result groups.
+Here every configuration must land in a single group.
+"""
+import numpy as np
+import pytest
+
+import bf16_rounding_numerics_amd as arn
+import synth
+from gpu_helpers import announce, check_parity, gpu_fwd, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+BLOCKS = (64, 128, 256, 512, 1024)
+
+
+def configurations(h):
+    """Every (path, block, grid) that the library accepts for hidden h."""
+    segs = h // 8
+    cfgs = []
+    for b in BLOCKS:
+        if segs <= 512 and not (b == 1024 and segs > 256):
+            cfgs.append((arn.PATH_WAVE_ROW, b))
+        j = -(-segs // b)
+        jj = next((p for p in (1, 2, 4, 8) if p >= j), None)
+        if jj is not None and b * jj <= 2048:
+            cfgs.append((arn.PATH_WG_ROW, b))
+        cfgs.append((arn.PATH_LDS_TWO_PASS, b))
+    out = []
+    for path, b in cfgs:
+        for grid in (0, 7, -1):
+            out.append((path, b, grid))
+    return out
+
+
+@pytest.mark.parametrize("h", [64, 1000, 1024, 2048, 3000, 4096, 8192, 12288, 16384])
+def test_every_launch_configuration_gives_the_same_bits(h):
+    n = 37
+    x, r, w = synth.workload(2000 + h, n, h)
+    announce("invariance hidden %d: auto" % h)
+    ref_out, ref_res = gpu_fwd(x, r, w, 1e-6)
+    check_parity(x, r, w, 1e-6, ref_out, ref_res, label="auto h=%d" % h)
+    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    groups = {}
+    for path, b, grid in configurations(h):
+        announce("  path %d block %d grid %d" % (path, b, grid))
+        out, res = gpu_fwd(x, r, w, 1e-6, path=path, block=b, grid=grid, xd=xd, rd=rd, wd=wd)
+        key = (out.tobytes(), res.tobytes())
+        groups.setdefault(key, []).append((path, b, grid))
+    assert len(groups) == 1, "%d result groups: %s" % (
+        len(groups), [v[:3] for v in groups.values()])
+    (only,) = groups
+    assert only == (ref_out.tobytes(), ref_res.tobytes())
+
+
+def test_repeated_launches_are_bitwise_identical():
+    import torch
+
+    x, r, w = synth.workload(71, 512, 8192)
+    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    announce("repeat x50 at 512x8192")
+    first = gpu_fwd(x, r, w, 1e-6, xd=xd, rd=rd, wd=wd)
+    outs = []
+    for i in range(50):
+        out = torch.empty_like(xd)
+        res = torch.empty_like(xd)
+        arn.add_rmsnorm_fwd(out, res, xd, rd, wd, 1e-6)
+        outs.append((out, res))
+    torch.cuda.synchronize()
+    for out, res in outs:
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), first[0])
+        assert np.array_equal(res.cpu().numpy().view(np.uint16), first[1])
+
+
+@pytest.mark.parametrize("h", [1024, 8192, 16384])
+def test_batch_invariance(h):
+    """A row gives the same bits alone, in a batch, or at another batch index."""
+    x, r, w = synth.workload(81, 64, h)
+    announce("batch invariance hidden %d" % h)
+    full_out, full_res = gpu_fwd(x, r, w, 1e-6)
+    for i in (0, 17, 63):
+        o, s = gpu_fwd(x[i:i + 1], r[i:i + 1], w, 1e-6)
+        assert np.array_equal(o[0], full_out[i]) and np.array_equal(s[0], full_res[i])
+    perm = np.random.default_rng(0).permutation(64)
+    po, ps = gpu_fwd(x[perm], r[perm], w, 1e-6)
+    assert np.array_equal(po, full_out[perm]) and np.array_equal(ps, full_res[perm])
