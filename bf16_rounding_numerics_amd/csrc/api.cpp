@@ -45,7 +45,7 @@ int pow2_at_least(int64_t need) {
 
 // Default workgroup sizes per path.
 constexpr int kWaveRowThreads = 256;
-constexpr int kWgRowThreads = 256;
+constexpr int kWgRowThreads = 512;
 constexpr int kTwoPassThreads = 512;
 
 // Upper hidden sizes of the automatic choice.

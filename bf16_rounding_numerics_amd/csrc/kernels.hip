@@ -62,6 +62,20 @@ struct Params {
 DEV u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 DEV void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
+// Buffer resource over one row of a tensor: offsets stay 32-bit whatever the
+// tensor size, and the hardware range check (reads past num_records return
+// 0) lets a prefetch run without a branch.  A row outside the tensor gets
+// num_records = 0.  The last word selects 32-bit raw data (gfx9 layout).
+DEV __amdgpu_buffer_rsrc_t row_rsrc(const u32x4* t, int64_t row, int segs, bool valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(t) + (valid ? row * segs : 0), 0,
+                                           valid ? segs * 16 : 0, 0x00020000);
+}
+
+// Nontemporal (aux bit 1) 16-byte load of segment s through a row resource.
+DEV u32x4 load_seg(__amdgpu_buffer_rsrc_t r, int s) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, s * 16, 0, 2);
+}
+
 // ---------------------------------------------------------------- numerics
 
 DEV void unpack8(u32x4 q, float (&a)[8]) {
@@ -283,7 +297,11 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
 // block sum per wave per chunk.  After one barrier every thread finishes the
 // tree over NB padded block sums; pass 2 reads the staged values back (each
 // thread only its own) and writes out.
-template <int B, int NB>
+// Pass 1 issues the loads of U chunks at once before processing them, so
+// each wavefront keeps U chunks of x and residual in flight.  Loads go
+// through a per-row buffer resource: segments past the row read as zero,
+// without a branch.
+template <int B, int NB, int U>
 __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
   constexpr int W = B / 64;
   __shared__ float blk[NB];
@@ -298,24 +316,32 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
 
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
     const size_t base = (size_t)row * (size_t)C;
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, C, true);
+    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, C, true);
     // Blocks past the row's last chunk are +0.
     for (int i = chunks * W + t; i < NB; i += B) blk[i] = 0.0f;
-    for (int c = 0; c < chunks; ++c) {
-      const int s = c * B + t;
-      u32x4 xq = {0, 0, 0, 0}, rq = {0, 0, 0, 0};
-      if (s < C) {
-        xq = load_stream(p.x + base + s);
-        rq = load_stream(p.residual + base + s);
+    for (int c0 = 0; c0 < chunks; c0 += U) {
+      u32x4 xq[U], rq[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        xq[u] = load_seg(rx, (c0 + u) * B + t);
+        rq[u] = load_seg(rr, (c0 + u) * B + t);
       }
-      float acc[8];
-      float bs = add_segment(xq, rq, acc);
-      if (s < C) {
-        store_stream(p.residual_out + base + s, pack8_rne(acc));
-        lo[s] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        hi[s] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u;
+        if (c >= chunks) break;  // uniform across the workgroup
+        const int s = c * B + t;
+        float acc[8];
+        float bs = add_segment(xq[u], rq[u], acc);
+        if (s < C) {
+          store_stream(p.residual_out + base + s, pack8_rne(acc));
+          lo[s] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          hi[s] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
+        bs = wave_block_sum(bs);
+        if (lane == 0) blk[c * W + wave] = bs;
       }
-      bs = wave_block_sum(bs);
-      if (lane == 0) blk[c * W + wave] = bs;
     }
     __syncthreads();
     const float rinv = row_rinv(pairwise_tree_lds<NB>(blk), p);
@@ -432,11 +458,18 @@ hipError_t go_wg_j(const Params& p, int j, int64_t grid_blocks, hipStream_t s) {
 // hidden <= 16384, 64 cover the library's maximum.
 int two_pass_nb(int hidden) { return hidden <= 16384 ? 32 : 64; }
 
+// Chunks in flight per wavefront in the two-pass kernel: 2048 segments per
+// batch at most (a whole 16384-wide row), and no more than 4.
+template <int B>
+constexpr int two_pass_batch() {
+  return 2048 / B < 4 ? 2048 / B : 4;
+}
+
 template <int B, int NB>
 hipError_t go_two_pass(const Params& p, int64_t grid_blocks, hipStream_t s) {
   const size_t lds = (size_t)p.segs * 32;
-  hipLaunchKernelGGL((k_lds_two_pass<B, NB>), dim3(grid_for(grid_blocks, p.n_rows)), dim3(B),
-                     lds, s, p);
+  hipLaunchKernelGGL((k_lds_two_pass<B, NB, two_pass_batch<B>()>),
+                     dim3(grid_for(grid_blocks, p.n_rows)), dim3(B), lds, s, p);
   return hipGetLastError();
 }
 
@@ -531,8 +564,9 @@ int64_t res_wg(int j) {
 template <int B>
 int64_t res_two_pass(int hidden) {
   const size_t lds = (size_t)(hidden / 8) * 32;
-  if (two_pass_nb(hidden) == 32) return resident(k_lds_two_pass<B, 32>, B, lds);
-  return resident(k_lds_two_pass<B, 64>, B, lds);
+  if (two_pass_nb(hidden) == 32)
+    return resident(k_lds_two_pass<B, 32, two_pass_batch<B>()>, B, lds);
+  return resident(k_lds_two_pass<B, 64, two_pass_batch<B>()>, B, lds);
 }
 }  // namespace
 
