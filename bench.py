@@ -83,6 +83,28 @@ def run_copy_calibration(torch, nbytes=1 << 30, reps=20):
     print(json.dumps({"calibration_copy_bytes": nbytes, "reps": reps}))
 
 
+def copy_ceiling(torch, arn, bufs, steps, n_rows, hidden):
+    """The same bytes moved by the library's reference copy (x -> one output
+    buffer, residual -> the other; 16-byte nontemporal loads and stores, no
+    arithmetic), rotated like the kernel's buffers: the streaming rate this
+    device gives the fused kernel's read/write mix."""
+    sets = len(bufs)
+    for i in range(min(steps, 20)):
+        o, ro, xd, rd = bufs[i % sets]
+        arn.add_rmsnorm_test_copy2(ro, o, xd, rd)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        o, ro, xd, rd = bufs[i % sets]
+        arn.add_rmsnorm_test_copy2(ro, o, xd, rd)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    return 8 * n_rows * hidden / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s):
     """The oracle (single-threaded C) over the whole workload, repeated until the
     time budget is spent."""
@@ -166,6 +188,8 @@ def main(argv=None):
     nbytes = algorithmic_bytes(n_rows, hidden)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
+    copy_gbps = copy_ceiling(torch, arn, bufs, min(args.steps, 500), n_rows, hidden)
+
     path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"
     digest = hip_build.source_digest()
     traffic = traffic_from_profiles(path, args.workload, digest)
@@ -192,6 +216,10 @@ def main(argv=None):
                    "buffer_sets": sets, "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                    "wall_s_timed_region": round(wall_s, 4)},
         "roofline": roofline,
+        "copy_ceiling": {"gbps": round(copy_gbps, 2), "kernel_frac_of_copy": round(gbps / copy_gbps, 4),
+                         "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+                         "what": "add_rmsnorm_test_copy2 over the same bytes: two 16-byte "
+                                 "nontemporal streaming copies, no arithmetic, same buffer rotation"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, r, w, eps, n_rows, hidden, args.cpu_seconds)

@@ -47,8 +47,8 @@ class LaunchCfg(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_test_cvt_range",
-           "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error", "add_rmsnorm_abi_version",
-           "add_rmsnorm_build_info")
+           "add_rmsnorm_test_copy2", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
+           "add_rmsnorm_abi_version", "add_rmsnorm_build_info")
 
 
 def lib() -> ctypes.CDLL:
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(LaunchCfg), vp]
     L.add_rmsnorm_test_cvt_range.restype = i32
     L.add_rmsnorm_test_cvt_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
+    L.add_rmsnorm_test_copy2.restype = i32
+    L.add_rmsnorm_test_copy2.argtypes = [vp, vp, vp, vp, i64, vp]
     L.add_rmsnorm_strerror.restype = ctypes.c_char_p
     L.add_rmsnorm_strerror.argtypes = [i32]
     L.add_rmsnorm_last_hip_error.restype = ctypes.c_char_p
@@ -108,46 +110,68 @@ def _check(status: int) -> None:
         raise AddRmsnormError(status, msg)
 
 
-def _rows_hidden(x, weight):
-    import torch
-
-    tensors = (x, weight)
-    for t in tensors:
-        if not isinstance(t, torch.Tensor):
-            raise TypeError("expected torch tensors")
-        if not t.is_cuda:
-            raise ValueError("tensors must live on the GPU")
-        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-            raise TypeError("tensors must hold bf16 (bfloat16, or raw 16-bit patterns)")
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
-    if weight.dim() != 1:
-        raise ValueError("weight must be 1-D [hidden]")
-    hidden = weight.shape[0]
-    if x.dim() < 1 or x.shape[-1] != hidden:
-        raise ValueError("x must be [..., hidden] with hidden = weight.shape[0]")
-    return x.numel() // hidden if hidden else 0, hidden
+_DTYPES = None
 
 
-def _stream_handle(device, stream):
-    import torch
+def _dtypes():
+    global _DTYPES
+    if _DTYPES is None:
+        import torch
 
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+        _DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+    return _DTYPES
 
 
 def _marshal(out, residual_out, x, residual, weight):
-    for t in (out, residual_out, residual):
-        if t.shape != x.shape:
+    """Check the tensors and return (n_rows, hidden, device index)."""
+    import torch
+
+    dts = _dtypes()
+    if not isinstance(x, torch.Tensor) or not isinstance(weight, torch.Tensor):
+        raise TypeError("expected torch tensors")
+    if not x.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    dev = x.get_device()
+    shape = x.shape
+    for t in (x, out, residual_out, residual):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("expected torch tensors")
+        if t.shape != shape:
             raise ValueError("out, residual_out and residual must have x's shape %s"
-                             % (tuple(x.shape),))
-        if t.device != x.device or weight.device != x.device:
-            raise ValueError("all tensors must be on one device")
-    n_rows, hidden = _rows_hidden(x, weight)
-    for t in (out, residual_out, residual):
-        _rows_hidden(t, weight)
-    return n_rows, hidden
+                             % (tuple(shape),))
+        if t.get_device() != dev:
+            raise ValueError("all tensors must be on one GPU")
+        if t.dtype not in dts:
+            raise TypeError("tensors must hold bf16 (bfloat16, or raw 16-bit patterns)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if weight.get_device() != dev or weight.dtype not in dts or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous bf16 tensor on x's GPU")
+    if weight.dim() != 1 or len(shape) < 1 or shape[-1] != weight.shape[0]:
+        raise ValueError("x must be [..., hidden] and weight [hidden]")
+    hidden = weight.shape[0]
+    return (x.numel() // hidden if hidden else 0), hidden, dev
+
+
+def _stream_handle(dev, stream):
+    if stream is not None:
+        return stream.cuda_stream
+    import torch
+
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _on_device(dev, fn):
+    """Call fn with HIP's current device set to dev (switching only if needed)."""
+    import torch
+
+    if torch.cuda.current_device() == dev:
+        return fn()
+    with torch.cuda.device(dev):
+        return fn()
 
 
 def add_rmsnorm_fwd(out, residual_out, x, residual, weight, eps: float = 1e-6,
@@ -158,37 +182,50 @@ def add_rmsnorm_fwd(out, residual_out, x, residual, weight, eps: float = 1e-6,
     shape [..., hidden] and weight [hidden].  Enqueued on ``stream`` (default:
     torch's current stream for that device); does not synchronise.
     """
-    import torch
-
-    n_rows, hidden = _marshal(out, residual_out, x, residual, weight)
-    with torch.cuda.device(x.device):
-        _check(lib().add_rmsnorm_fwd(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
-                                     residual.data_ptr(), weight.data_ptr(), n_rows, hidden,
-                                     eps, _stream_handle(x.device, stream)))
+    n_rows, hidden, dev = _marshal(out, residual_out, x, residual, weight)
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_fwd(
+        out.data_ptr(), residual_out.data_ptr(), x.data_ptr(), residual.data_ptr(),
+        weight.data_ptr(), n_rows, hidden, eps, h)))
 
 
 def add_rmsnorm_fwd_cfg(out, residual_out, x, residual, weight, eps: float = 1e-6,
                         path: int = PATH_AUTO, block_threads: int = 0, grid_blocks: int = 0,
                         stream=None) -> None:
     """add_rmsnorm_fwd with an explicit launch configuration (same results)."""
-    import torch
-
-    n_rows, hidden = _marshal(out, residual_out, x, residual, weight)
+    n_rows, hidden, dev = _marshal(out, residual_out, x, residual, weight)
+    L = lib()
     cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
-    with torch.cuda.device(x.device):
-        _check(lib().add_rmsnorm_fwd_cfg(out.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
-                                         residual.data_ptr(), weight.data_ptr(), n_rows, hidden,
-                                         eps, ctypes.byref(cfg),
-                                         _stream_handle(x.device, stream)))
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_fwd_cfg(
+        out.data_ptr(), residual_out.data_ptr(), x.data_ptr(), residual.data_ptr(),
+        weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg), h)))
 
 
 def add_rmsnorm_test_cvt_range(out, start: int, stream=None) -> None:
     """out[i] <- bf16 (nearest-even, by the kernels' store routine) of the fp32
     bit pattern (start + i) mod 2^32.  out: contiguous 16-bit GPU tensor."""
-    import torch
-
     if not out.is_cuda or out.element_size() != 2 or not out.is_contiguous():
         raise ValueError("out must be a contiguous 16-bit GPU tensor")
-    with torch.cuda.device(out.device):
-        _check(lib().add_rmsnorm_test_cvt_range(out.data_ptr(), start & 0xFFFFFFFF, out.numel(),
-                                                _stream_handle(out.device, stream)))
+    dev = out.get_device()
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_test_cvt_range(
+        out.data_ptr(), start & 0xFFFFFFFF, out.numel(), h)))
+
+
+def add_rmsnorm_test_copy2(dst0, dst1, src0, src1, stream=None) -> None:
+    """dst0 <- src0, dst1 <- src1 with the fused kernels' streaming access
+    pattern and no arithmetic (a reference rate).  Contiguous 16-bit GPU
+    tensors of equal size."""
+    ts = (dst0, dst1, src0, src1)
+    n = src0.numel()
+    for t in ts:
+        if not t.is_cuda or t.element_size() != 2 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError("copy2 takes four contiguous 16-bit GPU tensors of equal size")
+    dev = src0.get_device()
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_test_copy2(
+        dst0.data_ptr(), dst1.data_ptr(), src0.data_ptr(), src1.data_ptr(), n, h)))

@@ -159,6 +159,24 @@ int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,
   return ADD_RMSNORM_OK;
 }
 
+int add_rmsnorm_test_copy2(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
+                           const uint16_t* src1, int64_t count, struct ihipStream_t* stream) {
+  if (count < 0) return ADD_RMSNORM_EINVAL;
+  if (count % 8 != 0) return ADD_RMSNORM_EALIGN;
+  if (count == 0) return ADD_RMSNORM_OK;
+  if (!dst0 || !dst1 || !src0 || !src1) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(dst0) || !aligned16(dst1) || !aligned16(src0) || !aligned16(src1))
+    return ADD_RMSNORM_EALIGN;
+  const uint64_t n = (uint64_t)count * 2;
+  if (overlap(dst0, n, dst1, n) || overlap(dst0, n, src0, n) || overlap(dst0, n, src1, n) ||
+      overlap(dst1, n, src0, n) || overlap(dst1, n, src1, n))
+    return ADD_RMSNORM_EALIAS;
+  hipError_t e = addrms::launch_copy2(dst0, dst1, src0, src1, count,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_failure(e);
+  return ADD_RMSNORM_OK;
+}
+
 const char* add_rmsnorm_strerror(int status) {
   switch (status) {
     case ADD_RMSNORM_OK: return "success";

@@ -76,6 +76,11 @@ DEV u32x4 load_seg(__amdgpu_buffer_rsrc_t r, int s) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, s * 16, 0, 2);
 }
 
+// Nontemporal 16-byte store of segment s; stores past the row are dropped.
+DEV void store_seg(__amdgpu_buffer_rsrc_t r, int s, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, s * 16, 0, 2);
+}
+
 // ---------------------------------------------------------------- numerics
 
 DEV void unpack8(u32x4 q, float (&a)[8]) {
@@ -166,6 +171,26 @@ DEV u32x4 normalise8(const float (&acc)[8], float rinv, u32x4 wq) {
   return pack8_rne(y);
 }
 
+// acc = x + r for one segment, without the sum of squares.
+DEV void add8(u32x4 xq, u32x4 rq, float (&acc)[8]) {
+  float xa[8], ra[8];
+  unpack8(xq, xa);
+  unpack8(rq, ra);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = xa[k] + ra[k];
+}
+
+// Hides a value from the optimiser.  The wavefront-per-row kernel keeps x and
+// residual in their packed bf16 form across the reduction and adds them again
+// afterwards (the same fp32 add, so the same bits): half the registers of
+// keeping the fp32 sums.  Without this the compiler would merge the two adds
+// and keep the sums live, or hoist loop-invariant LDS reads into registers.
+template <typename T>
+DEV T opaque(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // acc = x + r for one segment; returns its sum of squares.
 DEV float add_segment(u32x4 xq, u32x4 rq, float (&acc)[8]) {
   float xa[8], ra[8];
@@ -180,50 +205,50 @@ DEV float add_segment(u32x4 xq, u32x4 rq, float (&acc)[8]) {
 
 // WAVES rows per workgroup, one per wavefront; lane l holds segments
 // l, l + 64, ..., l + 64 (J - 1).  Block j of 64 segments is summed by one
-// butterfly; the J block sums finish the tree in registers.
+// butterfly; the J block sums finish the tree in registers.  The weight is
+// staged once per workgroup in LDS (the waves share it), which keeps the
+// per-lane register footprint small enough for more rows in flight per CU.
+// Rows are read and written through per-row buffer resources: segments past
+// the row read as zero and their stores are dropped, so nothing branches.
 template <int WAVES, int J>
 __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
+  __shared__ u32x4 wl[64 * J];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The wave index is the same in all 64 lanes; saying so keeps the row and
+  // its buffer resources in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int C = p.segs;
-
-  u32x4 wq[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int s = lane + 64 * j;
-    wq[j] = s < C ? p.weight[s] : u32x4{0, 0, 0, 0};
-  }
+  for (int i = threadIdx.x; i < 64 * J; i += WAVES * 64)
+    wl[i] = i < C ? p.weight[i] : u32x4{0, 0, 0, 0};
+  __syncthreads();
 
   const int64_t stride = (int64_t)gridDim.x * WAVES;
   for (int64_t row = (int64_t)blockIdx.x * WAVES + wave; row < p.n_rows; row += stride) {
-    const size_t base = (size_t)row * (size_t)C;
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, C, true);
+    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, C, true);
+    const __amdgpu_buffer_rsrc_t ro = row_rsrc(p.residual_out, row, C, true);
+    const __amdgpu_buffer_rsrc_t oo = row_rsrc(p.out, row, C, true);
     u32x4 xq[J], rq[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int s = lane + 64 * j;
-      if (s < C) {
-        xq[j] = load_stream(p.x + base + s);
-        rq[j] = load_stream(p.residual + base + s);
-      } else {
-        xq[j] = u32x4{0, 0, 0, 0};
-        rq[j] = u32x4{0, 0, 0, 0};
-      }
+      xq[j] = load_seg(rx, lane + 64 * j);
+      rq[j] = load_seg(rr, lane + 64 * j);
     }
-    float acc[J][8];
     float blk[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int s = lane + 64 * j;
-      blk[j] = add_segment(xq[j], rq[j], acc[j]);
-      if (s < C) store_stream(p.residual_out + base + s, pack8_rne(acc[j]));
+      float acc[8];
+      blk[j] = add_segment(xq[j], rq[j], acc);
+      store_seg(ro, lane + 64 * j, pack8_rne(acc));
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) blk[j] = wave_block_sum(blk[j]);
     const float rinv = row_rinv(pairwise_tree<J>(blk), p);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int s = lane + 64 * j;
-      if (s < C) store_stream(p.out + base + s, normalise8(acc[j], rinv, wq[j]));
+      float acc[8];
+      add8(opaque(xq[j]), opaque(rq[j]), acc);
+      store_seg(oo, lane + 64 * j, normalise8(acc, rinv, wl[opaque(lane + 64 * j)]));
     }
   }
 }
@@ -367,6 +392,22 @@ __global__ __launch_bounds__(256) void k_cvt_range(u32x4* out, uint32_t start, i
 #pragma unroll
     for (int k = 0; k < 8; ++k) a[k] = __builtin_bit_cast(float, u0 + (uint32_t)k);
     out[g] = pack8_rne(a);
+  }
+}
+
+// ---------------------------------------------------------------- copy reference
+
+// Two streaming copies with the fused kernels' access pattern (16-byte
+// nontemporal loads and stores) and no arithmetic: the reference rate for a
+// 50/50 read/write stream of the same bytes.  Grid-stride over segments.
+__global__ __launch_bounds__(256) void k_copy2(u32x4* d0, u32x4* d1, const u32x4* s0,
+                                               const u32x4* s1, int64_t segs) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < segs; i += stride) {
+    const u32x4 a = load_stream(s0 + i);
+    const u32x4 b = load_stream(s1 + i);
+    store_stream(d0 + i, a);
+    store_stream(d1 + i, b);
   }
 }
 
@@ -601,6 +642,24 @@ int64_t resident_blocks_lds_two_pass(int block_threads, int hidden) {
     case 1024: return res_two_pass<1024>(hidden);
   }
   return 0;
+}
+
+hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,
+                        int64_t count, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t segs = count / 8;
+  int64_t blocks = (int64_t)cus * 32;  // fastest grid of the copy sweeps on MI355X
+  const int64_t need = (segs + 255) / 256;
+  if (blocks > need) blocks = need;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_copy2, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<u32x4*>(d0),
+                     reinterpret_cast<u32x4*>(d1), reinterpret_cast<const u32x4*>(s0),
+                     reinterpret_cast<const u32x4*>(s1), segs);
+  return hipGetLastError();
 }
 
 hipError_t launch_cvt_range(uint16_t* out, uint32_t start, int64_t count, hipStream_t s) {

@@ -50,6 +50,10 @@ int64_t resident_blocks_wave_row(int block_threads, int segs_per_lane);
 int64_t resident_blocks_wg_row(int block_threads, int segs_per_thread);
 int64_t resident_blocks_lds_two_pass(int block_threads, int hidden);
 
+// Reference copy: d0 <- s0 and d1 <- s1, count 16-bit elements each.
+hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,
+                        int64_t count, hipStream_t stream);
+
 // Test hook: the store epilogue applied to consecutive fp32 bit patterns.
 hipError_t launch_cvt_range(uint16_t* out, uint32_t start, int64_t count, hipStream_t stream);
 

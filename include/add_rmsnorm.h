@@ -128,6 +128,17 @@ int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x
 int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,
                                struct ihipStream_t* stream);
 
+/*
+ * Measurement hook: dst0 <- src0 and dst1 <- src1, count 16-bit elements
+ * each, with the fused kernels' memory access pattern (16-byte nontemporal
+ * loads and stores) and no arithmetic.  Moving the same bytes as one fused
+ * call, it gives the streaming rate that call can at best reach on the
+ * device.  Device pointers, 16-byte aligned, count a multiple of 8; no
+ * buffer may overlap another (ADD_RMSNORM_EALIAS).  Enqueued on stream.
+ */
+int add_rmsnorm_test_copy2(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
+                           const uint16_t* src1, int64_t count, struct ihipStream_t* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* add_rmsnorm_strerror(int status);
 

@@ -172,6 +172,18 @@ def test_cvt_range_errors():
     assert L.add_rmsnorm_test_cvt_range(0, 0, 0, None) == arn.OK
 
 
+@fake_addresses
+def test_copy2_errors():
+    L = arn.lib()
+    assert L.add_rmsnorm_test_copy2(A, A + MB, A + 2 * MB, A + 3 * MB, -8, None) == arn.EINVAL
+    assert L.add_rmsnorm_test_copy2(A, A + MB, A + 2 * MB, A + 3 * MB, 12, None) == arn.EALIGN
+    assert L.add_rmsnorm_test_copy2(A + 2, A + MB, A + 2 * MB, A + 3 * MB, 16, None) == arn.EALIGN
+    assert L.add_rmsnorm_test_copy2(0, A + MB, A + 2 * MB, A + 3 * MB, 16, None) == arn.EINVAL
+    assert L.add_rmsnorm_test_copy2(A, A + 16, A + 2 * MB, A + 3 * MB, 16, None) == arn.EALIAS
+    assert L.add_rmsnorm_test_copy2(A, A + MB, A, A + 3 * MB, 16, None) == arn.EALIAS
+    assert L.add_rmsnorm_test_copy2(0, 0, 0, 0, 0, None) == arn.OK
+
+
 # ---------------------------------------------------------------- binding
 
 def test_binding_refuses_cpu_tensors():

@@ -171,3 +171,19 @@ def test_binding_rejects_aliasing_on_gpu():
         arn.add_rmsnorm_fwd(out, rd, xd, rd, wd)  # residual_out == residual
     assert e.value.status == arn.EALIAS
     assert (from_dev(out) == 0x7FC1).all()
+
+
+def test_copy_reference_copies_bit_exactly():
+    """The measurement hook (the streaming copy the benchmark uses as its
+    reference rate) must really move every byte."""
+    import torch
+
+    import bf16_rounding_numerics_amd as arn
+
+    announce("copy2 reference")
+    x, r, _ = synth.workload(91, 333, 1024)
+    xd, rd = to_dev(x), to_dev(r)
+    d0, d1 = poisoned_like(xd), poisoned_like(xd)
+    arn.add_rmsnorm_test_copy2(d0, d1, xd, rd)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(d0), x) and np.array_equal(from_dev(d1), r)
