@@ -91,12 +91,17 @@ int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x
   const uint64_t row_bytes = (uint64_t)hidden * 2;
   if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
   const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
+  // The outputs are disjoint from each other and from the weight.  Each is
+  // either disjoint from an input or exactly that input: every element is
+  // read and rewritten by the same thread, the stored value depending on the
+  // loaded one, so operating in place is safe; partial overlaps are not.
   if (overlap(out, t_bytes, residual_out, t_bytes)) return ADD_RMSNORM_EALIAS;
   const void* outs[2] = {out, residual_out};
+  const void* ins[2] = {x, residual};
   for (const void* o : outs) {
-    if (overlap(o, t_bytes, x, t_bytes) || overlap(o, t_bytes, residual, t_bytes) ||
-        overlap(o, t_bytes, weight, row_bytes))
-      return ADD_RMSNORM_EALIAS;
+    if (overlap(o, t_bytes, weight, row_bytes)) return ADD_RMSNORM_EALIAS;
+    for (const void* in : ins)
+      if (o != in && overlap(o, t_bytes, in, t_bytes)) return ADD_RMSNORM_EALIAS;
   }
 
   // Path and shape.
@@ -184,7 +189,8 @@ const char* add_rmsnorm_strerror(int status) {
       return "invalid argument (null pointer, negative rows, hidden <= 0, bad eps or launch "
              "configuration)";
     case ADD_RMSNORM_EALIGN: return "a pointer is not 16-byte aligned, or hidden % 8 != 0";
-    case ADD_RMSNORM_EALIAS: return "an output overlaps an input or the other output";
+    case ADD_RMSNORM_EALIAS:
+      return "an output partly overlaps an input, or overlaps the weight or the other output";
     case ADD_RMSNORM_ERANGE: return "hidden (or the problem size) is above what the path supports";
     case ADD_RMSNORM_EHIP: return "the HIP launch failed (see add_rmsnorm_last_hip_error)";
   }

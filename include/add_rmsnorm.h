@@ -57,7 +57,7 @@ struct ihipStream_t;
 #define ADD_RMSNORM_OK 0
 #define ADD_RMSNORM_EINVAL (-1) /* null pointer, n_rows < 0, hidden <= 0, eps < 0 or not finite, bad cfg */
 #define ADD_RMSNORM_EALIGN (-2) /* a pointer not 16-byte aligned, or hidden % 8 != 0 */
-#define ADD_RMSNORM_EALIAS (-3) /* an output overlaps an input or the other output */
+#define ADD_RMSNORM_EALIAS (-3) /* an output partly overlaps an input, or overlaps the weight or the other output */
 #define ADD_RMSNORM_ERANGE (-4) /* hidden above the maximum (of the library, the chosen path or the device) */
 #define ADD_RMSNORM_EHIP (-5)   /* the HIP launch failed; add_rmsnorm_last_hip_error() has the detail */
 
@@ -70,7 +70,10 @@ struct ihipStream_t;
  *   n_rows >= 0 (0 enqueues nothing and returns OK; pointers are not checked),
  *   8 <= hidden <= ADD_RMSNORM_MAX_HIDDEN with hidden % 8 == 0,
  *   eps finite and >= 0, added to the mean of squares inside the square root.
- * Outputs must not overlap inputs or each other (no in-place operation).
+ * In place: an output may be the very same buffer as x or residual (e.g.
+ * out == x and residual_out == residual, the usual residual-stream update);
+ * any other overlap of an output with an input, the weight or the other
+ * output is rejected with ADD_RMSNORM_EALIAS.
  * The kernel is chosen by hidden: one wavefront per row up to 2048, one
  * workgroup per row with the row held in registers up to 8192, and above
  * that one workgroup per row that stages the row's fp32 sums in LDS and

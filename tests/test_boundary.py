@@ -108,10 +108,12 @@ def call(out=A, res=A + MB, x=A + 2 * MB, r=A + 3 * MB, w=A + 4 * MB, n=4, h=64,
     (dict(w=0), arn.EINVAL),
     (dict(x=A + 2 * MB + 8), arn.EALIGN),
     (dict(w=A + 4 * MB + 2), arn.EALIGN),
-    (dict(out=A + 2 * MB), arn.EALIAS),                 # out == x
-    (dict(res=A + 3 * MB), arn.EALIAS),                 # residual_out == residual
+    (dict(out=A + 2 * MB + 16), arn.EALIAS),            # out partly overlaps x
+    (dict(res=A + 3 * MB - 16), arn.EALIAS),            # residual_out partly overlaps residual
     (dict(res=A + 4 * 64 * 2 - 16), arn.EALIAS),        # residual_out overlaps out's tail
     (dict(res=A + 4 * MB + 64), arn.EALIAS),            # residual_out overlaps weight
+    (dict(out=A + 4 * MB), arn.EALIAS),                 # out is the weight
+    (dict(out=A + 2 * MB, res=A + 2 * MB), arn.EALIAS), # both outputs in place on x
     (dict(n=1 << 62, h=8), arn.ERANGE),                 # byte count overflows
 ])
 @fake_addresses
@@ -135,6 +137,20 @@ def test_adjacent_buffers_are_not_overlap():
                 cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.ERANGE
     assert call(res=A + 4 * 8192 * 2 - 16, h=8192, x=A + 8 * MB, r=A + 9 * MB, w=A + 10 * MB,
                 cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.EALIAS
+
+
+@pytest.mark.parametrize("kw", [
+    dict(out=A + 2 * MB),                       # out == x
+    dict(res=A + 3 * MB),                       # residual_out == residual
+    dict(out=A + 2 * MB, res=A + 3 * MB),       # both in place
+    dict(out=A + 3 * MB, res=A + 2 * MB),       # crosswise
+])
+@fake_addresses
+def test_exact_in_place_aliases_pass_validation(kw):
+    # Exact aliases are accepted.  A forced path that cannot take hidden 8192
+    # is rejected after the alias checks, so ERANGE (not EALIAS) shows that
+    # they passed, and nothing is launched with the fake addresses.
+    assert call(h=8192, cfg=(arn.PATH_WAVE_ROW, 0, 0, 0), **kw) == arn.ERANGE
 
 
 @pytest.mark.parametrize("cfg,status", [

@@ -160,17 +160,20 @@ def test_side_stream_and_leading_dims():
     check_parity(x, r, w, 1e-6, from_dev(out).reshape(60, 2048), from_dev(res).reshape(60, 2048))
 
 
-def test_binding_rejects_aliasing_on_gpu():
+def test_binding_rejects_partial_aliasing_on_gpu():
     import bf16_rounding_numerics_amd as arn
 
-    announce("aliasing rejected")
-    x, r, w = synth.workload(61, 4, 1024)
-    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    announce("partial aliasing rejected")
+    x, r, w = synth.workload(61, 5, 1024)
+    buf = to_dev(np.concatenate([x, r]))          # rows 0-4 x, rows 5-9 residual
+    xd, wd = buf[:5], to_dev(w)
+    shifted = buf[1:6]                            # overlaps x by four rows
     out = poisoned_like(xd)
     with pytest.raises(arn.AddRmsnormError) as e:
-        arn.add_rmsnorm_fwd(out, rd, xd, rd, wd)  # residual_out == residual
+        arn.add_rmsnorm_fwd(out, shifted, xd, buf[5:10], wd)
     assert e.value.status == arn.EALIAS
     assert (from_dev(out) == 0x7FC1).all()
+    assert np.array_equal(from_dev(buf), np.concatenate([x, r]))
 
 
 def test_copy_reference_copies_bit_exactly():
