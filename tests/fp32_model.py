@@ -1,0 +1,62 @@
+"""ctypes front end of tests/pins/fp32_model.c (test code).
+
+The model reproduces, in IEEE binary32 on the CPU, the arithmetic contract
+the library documents for its kernels (fixed sum-of-squares tree, correctly
+rounded division and square root), so GPU results can be compared with it
+bit for bit.  It is pinned against the binary64 oracle by the CPU tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "pins", "fp32_model.c")
+LIBRARY = os.path.join(HERE, "pins", "libfp32model.so")
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-fno-tree-vectorize"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(LIBRARY) or (
+            os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+        tmp = LIBRARY + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, SOURCE, "-lm"], check=True)
+        os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = ctypes.CDLL(LIBRARY)
+        vp = ctypes.c_void_p
+        L.model_add_rmsnorm.restype = ctypes.c_int
+        L.model_add_rmsnorm.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_float]
+        _lib = L
+    return _lib
+
+
+def add_rmsnorm(x, residual, weight, eps=1e-6, want_sumsq=False):
+    """(out, residual_out[, sum of squares per row]) of the fp32 model."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    weight = np.ascontiguousarray(weight, dtype=np.uint16)
+    n, h = x.shape
+    out = np.empty_like(x)
+    res = np.empty_like(x)
+    ss = np.empty(n, dtype=np.float32) if want_sumsq else None
+    rc = lib().model_add_rmsnorm(out.ctypes.data, res.ctypes.data,
+                                 ss.ctypes.data if ss is not None else None, x.ctypes.data,
+                                 residual.ctypes.data, weight.ctypes.data, n, h,
+                                 ctypes.c_float(eps))
+    if rc != 0:
+        raise ValueError("fp32 model rejected its arguments")
+    return (out, res, ss) if want_sumsq else (out, res)

@@ -1,0 +1,91 @@
+/*
+ * fp32 model of the library's arithmetic contract (test code).
+ *
+ * The binary64 oracle defines what the fused add + RMSNorm computes; this
+ * model instead follows, step by step in IEEE binary32, the exact arithmetic
+ * the library documents for its kernels, so that a GPU result can be checked
+ * bit for bit rather than to within one bf16 ULP:
+ *   acc_j      = fl32(x_j + r_j)
+ *   segment s  = elements 8s .. 8s+7:  t = acc0*acc0, then t = fmaf(acck, acck, t)
+ *   S          = balanced pairwise sum of the segment sums in index order,
+ *                padded with +0 to a power of two
+ *   rinv       = 1 / sqrtf(S / hidden + eps)     (correctly rounded / and sqrt)
+ *   out_j      = bf16_rne((acc_j * rinv) * w_j)
+ * It shares no code with the GPU library.  Plain C, gcc -O2
+ * -ffp-contract=off, SSE binary32 arithmetic with the default MXCSR (no
+ * flush-to-zero); fmaf from the C library (correctly rounded).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static float f32_of(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static uint32_t bits_of(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+/* Nearest-even bf16 by comparing the dropped half with one half-ULP. */
+static uint16_t round_bf16(float f) {
+  uint32_t u = bits_of(f);
+  if (isnan(f)) return (uint16_t)((u >> 16) | 0x40);
+  uint32_t hi = u >> 16, lo = u & 0xFFFF;
+  if (lo > 0x8000 || (lo == 0x8000 && (hi & 1))) hi += 1;
+  return (uint16_t)hi;
+}
+
+/* Returns 0, or -1 on bad arguments (hidden not a positive multiple of 8). */
+int model_add_rmsnorm(uint16_t* out, uint16_t* residual_out, float* sumsq_out,
+                      const uint16_t* x, const uint16_t* r, const uint16_t* w, int64_t n_rows,
+                      int64_t hidden, float eps) {
+  if (hidden <= 0 || hidden % 8) return -1;
+  const int64_t segs = hidden / 8;
+  int64_t padded = 1;
+  while (padded < segs) padded *= 2;
+  float* seg = (float*)malloc(sizeof(float) * (size_t)padded);
+  float* acc = (float*)malloc(sizeof(float) * (size_t)hidden);
+  if (!seg || !acc) {
+    free(seg);
+    free(acc);
+    return -1;
+  }
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const uint16_t* xr = x + i * hidden;
+    const uint16_t* rr = r + i * hidden;
+    for (int64_t j = 0; j < hidden; ++j) {
+      acc[j] = f32_of((uint32_t)xr[j] << 16) + f32_of((uint32_t)rr[j] << 16);
+      residual_out[i * hidden + j] = round_bf16(acc[j]);
+    }
+    for (int64_t s = 0; s < padded; ++s) {
+      if (s >= segs) {
+        seg[s] = 0.0f;
+        continue;
+      }
+      const float* a = acc + 8 * s;
+      float t = a[0] * a[0];
+      for (int k = 1; k < 8; ++k) t = fmaf(a[k], a[k], t);
+      seg[s] = t;
+    }
+    for (int64_t width = padded; width > 1; width /= 2)
+      for (int64_t k = 0; k < width / 2; ++k) seg[k] = seg[2 * k] + seg[2 * k + 1];
+    const float S = seg[0];
+    if (sumsq_out) sumsq_out[i] = S;
+    const float m = S / (float)hidden;
+    const float v = m + eps;
+    const float rinv = 1.0f / sqrtf(v);
+    for (int64_t j = 0; j < hidden; ++j) {
+      const float y = (acc[j] * rinv) * f32_of((uint32_t)w[j] << 16);
+      out[i * hidden + j] = round_bf16(y);
+    }
+  }
+  free(seg);
+  free(acc);
+  return 0;
+}

@@ -1,0 +1,100 @@
+"""Pins for the fp32 model of the kernels' arithmetic contract (CPU only).
+
+The model (tests/pins/fp32_model.c) is what the GPU results are compared
+with bit for bit; these tests tie it to the binary64 oracle and to hand
+cases that fix its reduction order."""
+import numpy as np
+import pytest
+
+import fp32_model
+import oracle
+import synth
+from gpu_helpers import ulp_distance
+
+
+@pytest.mark.parametrize("n,h", [(64, 1024), (16, 4096), (8, 8200), (4, 16384), (33, 24)])
+def test_model_agrees_with_the_oracle(n, h):
+    x, r, w = synth.workload(600 + h, n, h)
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
+    o_out, o_res = oracle.add_rmsnorm(x, r, w, 1e-6)
+    assert np.array_equal(m_res, o_res)
+    d = ulp_distance(m_out, o_out)
+    assert d.max() <= 1
+    assert (d > 0).mean() < 1e-3
+
+
+def test_sum_of_squares_is_exact_for_small_integers():
+    rng = np.random.default_rng(3)
+    h = 4096
+    vals = rng.integers(-3, 4, size=(6, h)).astype(np.float32)
+    x = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    r = np.zeros_like(x)
+    w = np.full(h, 0x3F80, np.uint16)
+    _, _, ss = fp32_model.add_rmsnorm(x, r, w, 1e-6, want_sumsq=True)
+    assert np.array_equal(ss.astype(np.float64), (vals.astype(np.float64) ** 2).sum(axis=1))
+
+
+def _row(segment_values, h):
+    """A row whose segments have the given sums of squares: the first element
+    of segment s is sqrt(value), the rest zero."""
+    a = np.zeros(h, np.float32)
+    for s, v in enumerate(segment_values):
+        a[8 * s] = np.float32(np.sqrt(v))
+    assert ((a.view(np.uint32) & 0xFFFF) == 0).all()
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_reduction_is_pairwise_in_index_order():
+    # Segment sums (2^24, 1, 1, 0): pairs first give (2^24 + 1) + (1 + 0),
+    # where 2^24 + 1 rounds to 2^24 (tie to even) and the total stays 2^24.
+    # Sequential or other groupings reach 2^24 + 2.
+    h = 32
+    x = _row([2.0 ** 24, 1.0, 1.0, 0.0], h)[None]
+    _, _, ss = fp32_model.add_rmsnorm(x, np.zeros_like(x), np.full(h, 0x3F80, np.uint16),
+                                      1e-6, want_sumsq=True)
+    assert ss[0] == np.float32(2.0 ** 24)
+    # Segment sums (1, 1, 2^24, 0): (1 + 1) + (2^24 + 0) = 2^24 + 2, exact.
+    x = _row([1.0, 1.0, 2.0 ** 24, 0.0], h)[None]
+    _, _, ss = fp32_model.add_rmsnorm(x, np.zeros_like(x), np.full(h, 0x3F80, np.uint16),
+                                      1e-6, want_sumsq=True)
+    assert ss[0] == np.float32(2.0 ** 24 + 2)
+
+
+def test_segment_sum_uses_fused_multiply_add():
+    # acc = 1 + 2^-23 has 24 significant bits, so acc^2 is not an fp32 value
+    # and fma(acc, acc, t) differs from t + fl(acc * acc).  A
+    # segment of eight such values must give the fma chain t = acc*acc,
+    # t = fma(acc, acc, t) x 7, computed here exactly (each exact sum fits in
+    # binary64, so one rounding to fp32 is the fma's).
+    from fractions import Fraction
+
+    h = 8
+    x = np.full((1, h), 0x3F80, np.uint16)                       # 1
+    r = np.full((1, h), np.uint16(np.float32(2.0 ** -23).view(np.uint32) >> 16))
+    acc = np.float32(np.float32(1.0) + np.float32(2.0 ** -23))
+    a2 = Fraction(float(acc)) ** 2
+    t_fma = np.float32(acc * acc)
+    t_sep = t_fma
+    for _ in range(7):
+        t_fma = np.float32(float(a2 + Fraction(float(t_fma))))
+        t_sep = np.float32(t_sep + np.float32(acc * acc))
+    assert t_fma != t_sep  # the case tells the two apart
+    _, _, ss = fp32_model.add_rmsnorm(x, r, np.full(h, 0x3F80, np.uint16), 1e-6,
+                                      want_sumsq=True)
+    assert ss[0] == t_fma
+
+
+def test_special_rows_match_the_oracle():
+    h = 64
+    rng = np.random.default_rng(9)
+    base = synth.to_bf16_bits(rng.standard_normal((4, h)))
+    x = base.copy()
+    x[1, 3] = 0x7FC1
+    x[2, 5] = 0x7F80
+    x[3] = 0x62C0
+    r = np.zeros_like(x)
+    w = synth.to_bf16_bits(np.linspace(0.5, 2, h))
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
+    o_out, o_res = oracle.add_rmsnorm(x, r, w, 1e-6)
+    assert ulp_distance(m_res, o_res).max() == 0
+    assert ulp_distance(m_out, o_out).max() <= 1
