@@ -70,6 +70,11 @@ class Oracle:
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                       ctypes.c_int]
+        L.orc_add_rmsnorm_quant.restype = ctypes.c_int
+        L.orc_add_rmsnorm_quant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_float]
         self.path = path
         self.lib = L
 
@@ -135,6 +140,31 @@ class Oracle:
         return out, res_out
 
 
+    def add_rmsnorm_quant(self, x: np.ndarray, residual: np.ndarray, weight: np.ndarray,
+                          eps: float = 1e-6, want_exact: bool = False):
+        """Quantised variant: (codes int8 [n, hidden], scale fp32 [n],
+        residual_out uint16 [n, hidden]) plus the binary64 y when asked."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
+        weight = np.ascontiguousarray(weight, dtype=np.uint16)
+        if x.ndim != 2 or residual.shape != x.shape or weight.shape != (x.shape[1],):
+            raise ValueError("shape mismatch")
+        n, h = x.shape
+        q = np.empty(x.shape, dtype=np.int8)
+        sc = np.empty(n, dtype=np.float32)
+        res_out = np.empty_like(x)
+        y = np.empty(x.shape, dtype=np.float64) if want_exact else None
+        rc = self.lib.orc_add_rmsnorm_quant(_ptr(q), _ptr(sc), _ptr(res_out),
+                                            _ptr(y) if y is not None else None, _ptr(x),
+                                            _ptr(residual), _ptr(weight), n, h,
+                                            ctypes.c_float(eps))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+        if want_exact:
+            return q, sc, res_out, y
+        return q, sc, res_out
+
+
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
@@ -180,6 +210,10 @@ def rne16_from_f64_array(y: np.ndarray) -> np.ndarray:
 def add_rmsnorm(x, residual, weight, eps: float = 1e-6, rounding: int = RNE,
                 want_exact: bool = False):
     return default().add_rmsnorm(x, residual, weight, eps, rounding, want_exact)
+
+
+def add_rmsnorm_quant(x, residual, weight, eps: float = 1e-6, want_exact: bool = False):
+    return default().add_rmsnorm_quant(x, residual, weight, eps, want_exact)
 
 
 # ---------------------------------------------------------------- measurements

@@ -168,3 +168,75 @@ int orc_add_rmsnorm(uint16_t* out, uint16_t* residual_out, double* y_exact,
   }
   return 0;
 }
+
+/* NaN-propagating maximum: a NaN operand wins. */
+static float max_nan(float m, float v) {
+  if (isnan(m)) return m;
+  if (isnan(v) || v > m) return v;
+  return m;
+}
+
+/*
+ * Quantised out, the FUSE_QUANT sibling of the kernel in the aiter issue
+ * ("Cost of fixing": in the quantised configurations out goes through a
+ * scaled cast to int8/fp8/fp4 instead of fp32_to_bf16).  The pages do not
+ * give the cast itself; the reading taken is per-row symmetric int8:
+ *   y_j   = (acc_j * rinv) * w_j           (binary64, as in orc_add_rmsnorm)
+ *   amax  = max_j |y_j|
+ *   scale = amax / 127
+ *   q_j   = y_j / scale rounded to the nearest integer, ties to even,
+ *           kept within [-127, 127]
+ * A row whose amax is 0, Inf or NaN gets scale = amax / 127 (0, Inf or NaN)
+ * and all-zero codes.
+ * Floating point decides integers here, so those decisions are taken in the
+ * kernels' precision: y is rounded once to binary32, and the maximum, the
+ * scale, the quotient and its rounding are binary32 operations.
+ * residual_out is as in orc_add_rmsnorm.  y_exact (may be NULL) receives the
+ * binary64 y.  Returns 0, or -1 on a bad argument.
+ */
+int orc_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, double* y_exact,
+                          const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
+                          int64_t n_rows, int64_t hidden, float eps) {
+  if (n_rows < 0 || hidden <= 0) return -1;
+  if (n_rows == 0) return 0;
+  if (!q || !scale || !residual_out || !x || !residual || !weight) return -1;
+
+  const double f32_overflow = ldexp(2.0 - ldexp(1.0, -24), 127);
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const uint16_t* xr = x + i * hidden;
+    const uint16_t* rr = residual + i * hidden;
+    double s = 0.0;
+    for (int64_t j = 0; j < hidden; ++j) {
+      float acc = bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]);
+      residual_out[i * hidden + j] = orc_rne16(f32_bits(acc));
+      double a = (double)acc;
+      s += a * a;
+    }
+    if (s >= f32_overflow) s = INFINITY;
+    double rinv = 1.0 / sqrt(s / (double)hidden + (double)eps);
+
+    float amax = 0.0f;
+    for (int64_t j = 0; j < hidden; ++j) {
+      double a = (double)(bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]));
+      double y = (a * rinv) * (double)bf16_to_f32(weight[j]);
+      if (y_exact) y_exact[i * hidden + j] = y;
+      amax = max_nan(amax, fabsf((float)y));
+    }
+    const float sc = amax / 127.0f;
+    scale[i] = sc;
+    const int ok = isfinite(amax) && amax > 0.0f;
+    for (int64_t j = 0; j < hidden; ++j) {
+      int8_t code = 0;
+      if (ok) {
+        double a = (double)(bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]));
+        float y32 = (float)((a * rinv) * (double)bf16_to_f32(weight[j]));
+        float t = nearbyintf(y32 / sc);
+        if (t > 127.0f) t = 127.0f;
+        if (t < -127.0f) t = -127.0f;
+        code = (int8_t)t;
+      }
+      q[i * hidden + j] = code;
+    }
+  }
+  return 0;
+}
