@@ -183,14 +183,18 @@ static float max_nan(float m, float v) {
  * give the cast itself; the reading taken is per-row symmetric int8:
  *   y_j   = (acc_j * rinv) * w_j           (binary64, as in orc_add_rmsnorm)
  *   amax  = max_j |y_j|
- *   scale = amax / 127
- *   q_j   = y_j / scale rounded to the nearest integer, ties to even,
- *           kept within [-127, 127]
- * A row whose amax is 0, Inf or NaN gets scale = amax / 127 (0, Inf or NaN)
- * and all-zero codes.
+ *   scale = amax / 127                      (the dequantisation factor)
+ *   q_j   = y_j * (127 / amax) rounded to the nearest integer, ties to even,
+ *           kept within [-127, 127]  (the scaled cast multiplies by the
+ *           inverse scale, formed once per row)
+ * The inverse scale must be a finite fp32 number, so a row is quantised only
+ * when 2^-120 <= amax <= FLT_MAX; any other row (amax 0, tiny, Inf or NaN:
+ * every |y| there is below 2^-120, or the row holds no numbers) gets
+ * all-zero codes, and its scale is still amax / 127.
  * Floating point decides integers here, so those decisions are taken in the
  * kernels' precision: y is rounded once to binary32, and the maximum, the
- * scale, the quotient and its rounding are binary32 operations.
+ * scale, the inverse scale, the product and its rounding are binary32
+ * operations.
  * residual_out is as in orc_add_rmsnorm.  y_exact (may be NULL) receives the
  * binary64 y.  Returns 0, or -1 on a bad argument.
  */
@@ -223,14 +227,15 @@ int orc_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, doubl
       amax = max_nan(amax, fabsf((float)y));
     }
     const float sc = amax / 127.0f;
+    const float inv = 127.0f / amax;
     scale[i] = sc;
-    const int ok = isfinite(amax) && amax > 0.0f;
+    const int ok = isfinite(amax) && amax >= ldexpf(1.0f, -120);
     for (int64_t j = 0; j < hidden; ++j) {
       int8_t code = 0;
       if (ok) {
         double a = (double)(bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]));
         float y32 = (float)((a * rinv) * (double)bf16_to_f32(weight[j]));
-        float t = nearbyintf(y32 / sc);
+        float t = nearbyintf(y32 * inv);
         if (t > 127.0f) t = 127.0f;
         if (t < -127.0f) t = -127.0f;
         code = (int8_t)t;

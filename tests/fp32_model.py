@@ -40,6 +40,9 @@ def lib():
         L.model_add_rmsnorm.restype = ctypes.c_int
         L.model_add_rmsnorm.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_float]
+        L.model_add_rmsnorm_quant.restype = ctypes.c_int
+        L.model_add_rmsnorm_quant.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64,
+                                              ctypes.c_int64, ctypes.c_float]
         _lib = L
     return _lib
 
@@ -60,3 +63,20 @@ def add_rmsnorm(x, residual, weight, eps=1e-6, want_sumsq=False):
     if rc != 0:
         raise ValueError("fp32 model rejected its arguments")
     return (out, res, ss) if want_sumsq else (out, res)
+
+
+def add_rmsnorm_quant(x, residual, weight, eps=1e-6):
+    """(codes int8, scale fp32 per row, residual_out) of the fp32 model."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    weight = np.ascontiguousarray(weight, dtype=np.uint16)
+    n, h = x.shape
+    q = np.empty(x.shape, dtype=np.int8)
+    sc = np.empty(n, dtype=np.float32)
+    res = np.empty_like(x)
+    rc = lib().model_add_rmsnorm_quant(q.ctypes.data, sc.ctypes.data, res.ctypes.data,
+                                       x.ctypes.data, residual.ctypes.data, weight.ctypes.data,
+                                       n, h, ctypes.c_float(eps))
+    if rc != 0:
+        raise ValueError("fp32 model rejected its arguments")
+    return q, sc, res

@@ -41,14 +41,43 @@ static uint16_t round_bf16(float f) {
   return (uint16_t)hi;
 }
 
+/*
+ * One row's fp32 pipeline up to rinv: acc (into acc[]), residual_out, the
+ * tree sum of squares (returned through *sumsq) and rinv.
+ */
+static float row_rinv(float* acc, float* seg, int64_t padded, uint16_t* ro, const uint16_t* xr,
+                      const uint16_t* rr, int64_t hidden, float eps, float* sumsq) {
+  const int64_t segs = hidden / 8;
+  for (int64_t j = 0; j < hidden; ++j) {
+    acc[j] = f32_of((uint32_t)xr[j] << 16) + f32_of((uint32_t)rr[j] << 16);
+    ro[j] = round_bf16(acc[j]);
+  }
+  for (int64_t s = 0; s < padded; ++s) {
+    if (s >= segs) {
+      seg[s] = 0.0f;
+      continue;
+    }
+    const float* a = acc + 8 * s;
+    float t = a[0] * a[0];
+    for (int k = 1; k < 8; ++k) t = fmaf(a[k], a[k], t);
+    seg[s] = t;
+  }
+  for (int64_t width = padded; width > 1; width /= 2)
+    for (int64_t k = 0; k < width / 2; ++k) seg[k] = seg[2 * k] + seg[2 * k + 1];
+  const float S = seg[0];
+  if (sumsq) *sumsq = S;
+  const float m = S / (float)hidden;
+  const float v = m + eps;
+  return 1.0f / sqrtf(v);
+}
+
 /* Returns 0, or -1 on bad arguments (hidden not a positive multiple of 8). */
 int model_add_rmsnorm(uint16_t* out, uint16_t* residual_out, float* sumsq_out,
                       const uint16_t* x, const uint16_t* r, const uint16_t* w, int64_t n_rows,
                       int64_t hidden, float eps) {
   if (hidden <= 0 || hidden % 8) return -1;
-  const int64_t segs = hidden / 8;
   int64_t padded = 1;
-  while (padded < segs) padded *= 2;
+  while (padded < hidden / 8) padded *= 2;
   float* seg = (float*)malloc(sizeof(float) * (size_t)padded);
   float* acc = (float*)malloc(sizeof(float) * (size_t)hidden);
   if (!seg || !acc) {
@@ -57,32 +86,66 @@ int model_add_rmsnorm(uint16_t* out, uint16_t* residual_out, float* sumsq_out,
     return -1;
   }
   for (int64_t i = 0; i < n_rows; ++i) {
-    const uint16_t* xr = x + i * hidden;
-    const uint16_t* rr = r + i * hidden;
-    for (int64_t j = 0; j < hidden; ++j) {
-      acc[j] = f32_of((uint32_t)xr[j] << 16) + f32_of((uint32_t)rr[j] << 16);
-      residual_out[i * hidden + j] = round_bf16(acc[j]);
-    }
-    for (int64_t s = 0; s < padded; ++s) {
-      if (s >= segs) {
-        seg[s] = 0.0f;
-        continue;
-      }
-      const float* a = acc + 8 * s;
-      float t = a[0] * a[0];
-      for (int k = 1; k < 8; ++k) t = fmaf(a[k], a[k], t);
-      seg[s] = t;
-    }
-    for (int64_t width = padded; width > 1; width /= 2)
-      for (int64_t k = 0; k < width / 2; ++k) seg[k] = seg[2 * k] + seg[2 * k + 1];
-    const float S = seg[0];
-    if (sumsq_out) sumsq_out[i] = S;
-    const float m = S / (float)hidden;
-    const float v = m + eps;
-    const float rinv = 1.0f / sqrtf(v);
+    const float rinv = row_rinv(acc, seg, padded, residual_out + i * hidden, x + i * hidden,
+                                r + i * hidden, hidden, eps, sumsq_out ? sumsq_out + i : NULL);
     for (int64_t j = 0; j < hidden; ++j) {
       const float y = (acc[j] * rinv) * f32_of((uint32_t)w[j] << 16);
       out[i * hidden + j] = round_bf16(y);
+    }
+  }
+  free(seg);
+  free(acc);
+  return 0;
+}
+
+/* NaN-propagating maximum: a NaN operand wins. */
+static float max_nan(float m, float v) {
+  if (isnan(m)) return m;
+  if (isnan(v) || v > m) return v;
+  return m;
+}
+
+/*
+ * Quantised out: y_j = (acc_j * rinv) * w_j in fp32 as above, then
+ * amax = max |y_j| (NaN wins), scale = amax / 127, inv = 127 / amax, and
+ * codes q_j = nearbyintf(y_j * inv) within [-127, 127]; a row whose amax is
+ * not in [2^-120, FLT_MAX] (0, tiny, Inf or NaN) gets all-zero codes (its
+ * scale is still amax / 127).
+ */
+int model_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, const uint16_t* x,
+                            const uint16_t* r, const uint16_t* w, int64_t n_rows, int64_t hidden,
+                            float eps) {
+  if (hidden <= 0 || hidden % 8) return -1;
+  int64_t padded = 1;
+  while (padded < hidden / 8) padded *= 2;
+  float* seg = (float*)malloc(sizeof(float) * (size_t)padded);
+  float* acc = (float*)malloc(sizeof(float) * (size_t)hidden);
+  if (!seg || !acc) {
+    free(seg);
+    free(acc);
+    return -1;
+  }
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const float rinv = row_rinv(acc, seg, padded, residual_out + i * hidden, x + i * hidden,
+                                r + i * hidden, hidden, eps, NULL);
+    float amax = 0.0f;
+    for (int64_t j = 0; j < hidden; ++j) {
+      acc[j] = (acc[j] * rinv) * f32_of((uint32_t)w[j] << 16);
+      amax = max_nan(amax, fabsf(acc[j]));
+    }
+    const float sc = amax / 127.0f;
+    const float inv = 127.0f / amax;
+    scale[i] = sc;
+    const int ok = isfinite(amax) && amax >= ldexpf(1.0f, -120);
+    for (int64_t j = 0; j < hidden; ++j) {
+      int8_t code = 0;
+      if (ok) {
+        float t = nearbyintf(acc[j] * inv);
+        if (t > 127.0f) t = 127.0f;
+        if (t < -127.0f) t = -127.0f;
+        code = (int8_t)t;
+      }
+      q[i * hidden + j] = code;
     }
   }
   free(seg);

@@ -98,3 +98,25 @@ def test_special_rows_match_the_oracle():
     o_out, o_res = oracle.add_rmsnorm(x, r, w, 1e-6)
     assert ulp_distance(m_res, o_res).max() == 0
     assert ulp_distance(m_out, o_out).max() <= 1
+
+
+@pytest.mark.parametrize("n,h", [(64, 1024), (16, 4096), (4, 16384)])
+def test_quant_model_agrees_with_the_oracle(n, h):
+    x, r, w = synth.workload(700 + h, n, h)
+    mq, ms, mr = fp32_model.add_rmsnorm_quant(x, r, w, 1e-6)
+    oq, os_, orr = oracle.add_rmsnorm_quant(x, r, w, 1e-6)
+    assert np.array_equal(mr, orr)
+    assert np.allclose(ms, os_, rtol=2e-6, atol=0)
+    d = np.abs(mq.astype(np.int32) - oq.astype(np.int32))
+    assert d.max() <= 1 and (d > 0).mean() < 1e-3
+
+
+def test_quant_model_special_rows():
+    h = 64
+    w = synth.to_bf16_bits(np.linspace(0.5, 2.0, h))
+    x = np.zeros((3, h), np.uint16)
+    x[1] = 0x3F80
+    x[1, 3] = 0x7FC1
+    x[2] = 0x62C0
+    q, sc, _ = fp32_model.add_rmsnorm_quant(x, np.zeros_like(x), w, 1e-6)
+    assert sc[0] == 0 and np.isnan(sc[1]) and sc[2] == 0 and (q == 0).all()

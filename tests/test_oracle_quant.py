@@ -1,7 +1,7 @@
 """Pins for the oracle's quantised variant (CPU only).
 
-Per-row symmetric int8: scale = amax / 127, q = nearest-even(y / scale) in
-[-127, 127], decided in binary32 from the binary64 y.  The pins are closed
+Per-row symmetric int8: scale = amax / 127, q = nearest-even(y * (127/amax))
+in [-127, 127], decided in binary32 from the binary64 y.  The pins are closed
 forms (constant and one-hot rows), the documented special-value rules, and
 invariants any correct quantiser satisfies (range, the row maximum at +-127,
 dequantisation error within half a step, no bias).  Copies of the oracle
@@ -88,6 +88,15 @@ def pin_special_rows(orc):
     x = np.full((1, h), f32_to_bits16_exact([2.0 ** 70])[0], np.uint16)
     q, sc, _ = orc.add_rmsnorm_quant(x, z, w, 1e-6)
     assert sc[0] == 0 and (q == 0).all()
+    # A row whose amax is below 2^-120 (subnormal inputs, eps dominating) has
+    # no finite inverse scale: codes 0, scale amax / 127 (tiny, nonzero).  Just
+    # above the threshold the row is quantised as usual.
+    x = np.full((1, h), 0x0001, np.uint16)           # 2^-133: acc = 2^-132, y ~ 2^-122
+    q, sc, _ = orc.add_rmsnorm_quant(x, x, w, 1e-6)
+    assert 0 < sc[0] < 2.0 ** -120 / 127 and (q == 0).all()
+    x = np.full((1, h), 0x0100, np.uint16)           # 2^-125: y ~ 2^-115
+    q, sc, _ = orc.add_rmsnorm_quant(x, z, w, 1e-6)
+    assert sc[0] > 2.0 ** -120 / 127 and np.abs(q).max() == 127
 
 
 def pin_random_rows_invariants(orc):
@@ -120,12 +129,15 @@ def test_quant_pin(orc, pin):
 
 
 QUANT_MUTATIONS = {
-    "truncating_codes": ("float t = nearbyintf(y32 / sc);", "float t = truncf(y32 / sc);"),
+    "truncating_codes": ("float t = nearbyintf(y32 * inv);", "float t = truncf(y32 * inv);"),
+    "no_tiny_row_rule": ("isfinite(amax) && amax >= ldexpf(1.0f, -120)",
+                         "isfinite(amax) && amax > 0.0f"),
     "scale_128": ("const float sc = amax / 127.0f;", "const float sc = amax / 128.0f;"),
+    "inverse_128": ("const float inv = 127.0f / amax;", "const float inv = 128.0f / amax;"),
     "max_without_abs": ("amax = max_nan(amax, fabsf((float)y));",
                         "amax = max_nan(amax, (float)y);"),
-    "scale_from_rms": ("const float sc = amax / 127.0f;",
-                       "const float sc = (float)(1.0 / rinv) / 127.0f;"),
+    "scale_from_rms": ("const float inv = 127.0f / amax;",
+                       "const float inv = 127.0f * (float)rinv;"),
     "codes_from_acc": ("float y32 = (float)((a * rinv) * (double)bf16_to_f32(weight[j]));",
                        "float y32 = (float)(a * rinv);"),
 }
