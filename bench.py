@@ -33,9 +33,13 @@ PEAK_HBM_GBPS = 8000.0
 CACHE_DEFEAT_BYTES = 1 << 30  # rotate buffer sets until the footprint is >= 1 GiB
 
 
-def algorithmic_bytes(n_rows: int, hidden: int) -> int:
-    """Bytes the method must move per call: x, residual read; out, residual_out
-    written (2 bytes each per element); the weight read once."""
+def algorithmic_bytes(n_rows: int, hidden: int, op: str = "bf16") -> int:
+    """Bytes the method must move per call: x, residual read and residual_out
+    written (2 bytes each per element), out written (2 bytes per element, or
+    for the quantised variant 1 byte of code per element and a 4-byte scale
+    per row); the weight read once."""
+    if op == "quant":
+        return 7 * n_rows * hidden + 4 * n_rows + 2 * hidden
     return 8 * n_rows * hidden + 2 * hidden
 
 
@@ -45,6 +49,8 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="4096x8192")
+    p.add_argument("--op", choices=("bf16", "quant"), default="bf16",
+                   help="bf16 out (the benchmark) or the int8-quantised variant")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU oracle baseline")
@@ -105,7 +111,7 @@ def copy_ceiling(torch, arn, bufs, steps, n_rows, hidden):
     return 8 * n_rows * hidden / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s):
+def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s, op="bf16"):
     """The oracle (single-threaded C) over the whole workload, repeated until the
     time budget is spent."""
     import oracle
@@ -114,12 +120,15 @@ def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s):
     passes = 0
     t0 = time.perf_counter()
     while True:
-        oracle.add_rmsnorm(x, r, w, eps)
+        if op == "quant":
+            oracle.add_rmsnorm_quant(x, r, w, eps)
+        else:
+            oracle.add_rmsnorm(x, r, w, eps)
         passes += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    gbps = algorithmic_bytes(n_rows, hidden) * passes / el / 1e9
+    gbps = algorithmic_bytes(n_rows, hidden, op) * passes / el / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "%d full passes over the %dx%d workload in %.1f s (single thread)"
                       % (passes, n_rows, hidden, el)}
@@ -164,12 +173,24 @@ def main(argv=None):
         xd = xd0 if i == 0 else xd0.clone()
         rd = rd0 if i == 0 else rd0.clone()
         bufs.append((torch.empty_like(xd), torch.empty_like(xd), xd, rd))
+    qbufs = []
+    if args.op == "quant":
+        for i in range(sets):
+            qbufs.append((torch.empty(n_rows, hidden, dtype=torch.int8, device=dev),
+                          torch.empty(n_rows, dtype=torch.float32, device=dev)))
     torch.cuda.synchronize()
+
+    def step(i):
+        o, ro, xd, rd = bufs[i % sets]
+        if args.op == "quant":
+            q, sc = qbufs[i % sets]
+            arn.add_rmsnorm_quant_fwd(q, sc, ro, xd, rd, wd, eps)
+        else:
+            arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, eps)
 
     stream = torch.cuda.current_stream(dev)
     for i in range(args.warmup):
-        o, ro, xd, rd = bufs[i % sets]
-        arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, eps)
+        step(i)
     torch.cuda.synchronize()
 
     start = torch.cuda.Event(enable_timing=True)
@@ -178,27 +199,29 @@ def main(argv=None):
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        o, ro, xd, rd = bufs[i % sets]
-        arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, eps)
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
-    nbytes = algorithmic_bytes(n_rows, hidden)
+    nbytes = algorithmic_bytes(n_rows, hidden, args.op)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
     copy_gbps = copy_ceiling(torch, arn, bufs, min(args.steps, 500), n_rows, hidden)
 
     path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"
     digest = hip_build.source_digest()
-    traffic = traffic_from_profiles(path, args.workload, digest)
+    tag = path if args.op == "bf16" else path + "_quant"
+    traffic = traffic_from_profiles(tag, args.workload, digest)
     roofline = {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                 "traffic": traffic}
 
     line = {
-        "metric": "fused add+RMSNorm HBM GB/s and % of peak, n=4096 x hidden=8192 bf16",
+        "metric": "fused add+RMSNorm HBM GB/s and % of peak, n=4096 x hidden=8192 bf16"
+                  if args.op == "bf16" else
+                  "fused add+RMSNorm, int8-quantised out, HBM GB/s and % of peak",
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -210,19 +233,24 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "add_rmsnorm_fwd rows=%d hidden=%d bf16, eps=1e-6, "
-                               "x,residual~N(0,1), weight~1+0.1N(0,1)" % (n_rows, hidden),
+        "config": {"workload": "%s rows=%d hidden=%d bf16, eps=1e-6, "
+                               "x,residual~N(0,1), weight~1+0.1N(0,1)"
+                               % ("add_rmsnorm_fwd" if args.op == "bf16" else "add_rmsnorm_quant_fwd",
+                                  n_rows, hidden),
                    "n_rows": n_rows, "hidden": hidden, "kernel": path,
                    "buffer_sets": sets, "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                    "wall_s_timed_region": round(wall_s, 4)},
         "roofline": roofline,
-        "copy_ceiling": {"gbps": round(copy_gbps, 2), "kernel_frac_of_copy": round(gbps / copy_gbps, 4),
+        "copy_ceiling": {"gbps": round(copy_gbps, 2),
+                         "kernel_frac_of_copy": round(gbps / copy_gbps, 4) if args.op == "bf16"
+                         else None,
                          "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
                          "what": "add_rmsnorm_test_copy2 over the same bytes: two 16-byte "
                                  "nontemporal streaming copies, no arithmetic, same buffer rotation"},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x, r, w, eps, n_rows, hidden, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(x, r, w, eps, n_rows, hidden, args.cpu_seconds,
+                                            args.op)
     print(json.dumps(line))
     return 0
 

@@ -46,7 +46,8 @@ class LaunchCfg(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_test_cvt_range",
+EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_quant_fwd",
+           "add_rmsnorm_quant_fwd_cfg", "add_rmsnorm_test_cvt_range",
            "add_rmsnorm_test_copy2", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
            "add_rmsnorm_abi_version", "add_rmsnorm_build_info")
 
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
     L.add_rmsnorm_fwd_cfg.restype = i32
     L.add_rmsnorm_fwd_cfg.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32,
                                       ctypes.POINTER(LaunchCfg), vp]
+    L.add_rmsnorm_quant_fwd.restype = i32
+    L.add_rmsnorm_quant_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, vp]
+    L.add_rmsnorm_quant_fwd_cfg.restype = i32
+    L.add_rmsnorm_quant_fwd_cfg.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32,
+                                            ctypes.POINTER(LaunchCfg), vp]
     L.add_rmsnorm_test_cvt_range.restype = i32
     L.add_rmsnorm_test_cvt_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
     L.add_rmsnorm_test_copy2.restype = i32
@@ -201,6 +207,46 @@ def add_rmsnorm_fwd_cfg(out, residual_out, x, residual, weight, eps: float = 1e-
     _check(_on_device(dev, lambda: L.add_rmsnorm_fwd_cfg(
         out.data_ptr(), residual_out.data_ptr(), x.data_ptr(), residual.data_ptr(),
         weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg), h)))
+
+
+def _marshal_quant(out_q, out_scale, residual_out, x, residual, weight):
+    import torch
+
+    n_rows, hidden, dev = _marshal(residual_out, residual_out, x, residual, weight)
+    if not isinstance(out_q, torch.Tensor) or out_q.dtype != torch.int8 or \
+            out_q.shape != x.shape or not out_q.is_contiguous() or out_q.get_device() != dev:
+        raise ValueError("out_q must be a contiguous int8 tensor of x's shape on x's GPU")
+    if not isinstance(out_scale, torch.Tensor) or out_scale.dtype != torch.float32 or \
+            out_scale.numel() != n_rows or not out_scale.is_contiguous() or \
+            out_scale.get_device() != dev:
+        raise ValueError("out_scale must be a contiguous float32 tensor with one value per row")
+    return n_rows, hidden, dev
+
+
+def add_rmsnorm_quant_fwd(out_q, out_scale, residual_out, x, residual, weight,
+                          eps: float = 1e-6, stream=None) -> None:
+    """out_q (int8 codes), out_scale (fp32 per row), residual_out <- the
+    quantised fused add + RMSNorm.  out_q has x's shape, out_scale one value
+    per row (x.shape[:-1]); everything else as add_rmsnorm_fwd."""
+    n_rows, hidden, dev = _marshal_quant(out_q, out_scale, residual_out, x, residual, weight)
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fwd(
+        out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+        residual.data_ptr(), weight.data_ptr(), n_rows, hidden, eps, h)))
+
+
+def add_rmsnorm_quant_fwd_cfg(out_q, out_scale, residual_out, x, residual, weight,
+                              eps: float = 1e-6, path: int = PATH_AUTO, block_threads: int = 0,
+                              grid_blocks: int = 0, stream=None) -> None:
+    """add_rmsnorm_quant_fwd with an explicit launch configuration."""
+    n_rows, hidden, dev = _marshal_quant(out_q, out_scale, residual_out, x, residual, weight)
+    L = lib()
+    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fwd_cfg(
+        out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+        residual.data_ptr(), weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg), h)))
 
 
 def add_rmsnorm_test_cvt_range(out, start: int, stream=None) -> None:

@@ -32,7 +32,8 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
 
 bool valid_block(int b) { return b == 64 || b == 128 || b == 256 || b == 512 || b == 1024; }
 
@@ -61,6 +62,67 @@ int device_max_lds(int* out) {
   return ADD_RMSNORM_OK;
 }
 
+// Scalar arguments and the launch configuration, shared by both variants.
+int check_scalars(int64_t n_rows, int64_t hidden, float eps,
+                  const add_rmsnorm_launch_cfg* cfg, add_rmsnorm_launch_cfg* c) {
+  if (n_rows < 0 || hidden <= 0 || !std::isfinite(eps) || eps < 0.0f) return ADD_RMSNORM_EINVAL;
+  if (hidden % 8 != 0) return ADD_RMSNORM_EALIGN;
+  if (hidden > ADD_RMSNORM_MAX_HIDDEN) return ADD_RMSNORM_ERANGE;
+  *c = add_rmsnorm_launch_cfg{ADD_RMSNORM_PATH_AUTO, 0, 0, 0};
+  if (cfg) *c = *cfg;
+  if (c->flags != 0 || c->grid_blocks < -1) return ADD_RMSNORM_EINVAL;
+  if (c->path < ADD_RMSNORM_PATH_AUTO || c->path > ADD_RMSNORM_PATH_LDS_TWO_PASS)
+    return ADD_RMSNORM_EINVAL;
+  if (c->block_threads != 0 && !valid_block(c->block_threads)) return ADD_RMSNORM_EINVAL;
+  return ADD_RMSNORM_OK;
+}
+
+// A bf16 output against the inputs and the weight: disjoint, or exactly x or
+// residual (in place: every element is read and rewritten by the same thread,
+// the stored value depending on the loaded one).
+bool output_aliases_badly(const void* o, uint64_t t_bytes, const void* x, const void* residual,
+                          const void* weight, uint64_t row_bytes) {
+  if (overlap(o, t_bytes, weight, row_bytes)) return true;
+  if (o != x && overlap(o, t_bytes, x, t_bytes)) return true;
+  if (o != residual && overlap(o, t_bytes, residual, t_bytes)) return true;
+  return false;
+}
+
+// Kernel choice by hidden (or as forced) and launch.
+int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
+             struct ihipStream_t* stream) {
+  int path = c.path;
+  const int64_t hidden = a.hidden;
+  if (path == ADD_RMSNORM_PATH_AUTO) {
+    path = hidden <= kWaveRowMaxHidden ? ADD_RMSNORM_PATH_WAVE_ROW
+           : hidden <= kWgRowMaxHidden ? ADD_RMSNORM_PATH_WG_ROW
+                                       : ADD_RMSNORM_PATH_LDS_TWO_PASS;
+  }
+  const int64_t segs = hidden / 8;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (path == ADD_RMSNORM_PATH_WAVE_ROW) {
+    const int b = c.block_threads ? c.block_threads : kWaveRowThreads;
+    const int j = pow2_at_least((segs + 63) / 64);
+    if (j == 0 || !addrms::wave_row_supported(b, j)) return ADD_RMSNORM_ERANGE;
+    e = addrms::launch_wave_row(a, b, j, c.grid_blocks, s);
+  } else if (path == ADD_RMSNORM_PATH_WG_ROW) {
+    const int b = c.block_threads ? c.block_threads : kWgRowThreads;
+    const int j = pow2_at_least((segs + b - 1) / b);
+    if (j == 0 || !addrms::wg_row_supported(b, j)) return ADD_RMSNORM_ERANGE;
+    e = addrms::launch_wg_row(a, b, j, c.grid_blocks, s);
+  } else {
+    const int b = c.block_threads ? c.block_threads : kTwoPassThreads;
+    int max_lds = 0;
+    const int rc = device_max_lds(&max_lds);
+    if (rc != ADD_RMSNORM_OK) return rc;
+    if (addrms::lds_two_pass_lds_bytes((int)hidden) > (size_t)max_lds) return ADD_RMSNORM_ERANGE;
+    e = addrms::launch_lds_two_pass(a, b, c.grid_blocks, s);
+  }
+  if (e != hipSuccess) return hip_failure(e);
+  return ADD_RMSNORM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,21 +131,11 @@ int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x
                         const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
                         int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
                         struct ihipStream_t* stream) {
-  // Scalars first.
-  if (n_rows < 0 || hidden <= 0 || !std::isfinite(eps) || eps < 0.0f) return ADD_RMSNORM_EINVAL;
-  if (hidden % 8 != 0) return ADD_RMSNORM_EALIGN;
-  if (hidden > ADD_RMSNORM_MAX_HIDDEN) return ADD_RMSNORM_ERANGE;
-
-  add_rmsnorm_launch_cfg c = {ADD_RMSNORM_PATH_AUTO, 0, 0, 0};
-  if (cfg) c = *cfg;
-  if (c.flags != 0 || c.grid_blocks < -1) return ADD_RMSNORM_EINVAL;
-  if (c.path < ADD_RMSNORM_PATH_AUTO || c.path > ADD_RMSNORM_PATH_LDS_TWO_PASS)
-    return ADD_RMSNORM_EINVAL;
-  if (c.block_threads != 0 && !valid_block(c.block_threads)) return ADD_RMSNORM_EINVAL;
-
+  add_rmsnorm_launch_cfg c;
+  int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
+  if (rc != ADD_RMSNORM_OK) return rc;
   if (n_rows == 0) return ADD_RMSNORM_OK;
 
-  // Pointers.
   if (!out || !residual_out || !x || !residual || !weight) return ADD_RMSNORM_EINVAL;
   if (!aligned16(out) || !aligned16(residual_out) || !aligned16(x) || !aligned16(residual) ||
       !aligned16(weight))
@@ -91,58 +143,16 @@ int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x
   const uint64_t row_bytes = (uint64_t)hidden * 2;
   if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
   const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
-  // The outputs are disjoint from each other and from the weight.  Each is
-  // either disjoint from an input or exactly that input: every element is
-  // read and rewritten by the same thread, the stored value depending on the
-  // loaded one, so operating in place is safe; partial overlaps are not.
+  // The outputs are disjoint from each other and from the weight; each is
+  // either disjoint from an input or exactly that input (in place).
   if (overlap(out, t_bytes, residual_out, t_bytes)) return ADD_RMSNORM_EALIAS;
-  const void* outs[2] = {out, residual_out};
-  const void* ins[2] = {x, residual};
-  for (const void* o : outs) {
-    if (overlap(o, t_bytes, weight, row_bytes)) return ADD_RMSNORM_EALIAS;
-    for (const void* in : ins)
-      if (o != in && overlap(o, t_bytes, in, t_bytes)) return ADD_RMSNORM_EALIAS;
-  }
+  if (output_aliases_badly(out, t_bytes, x, residual, weight, row_bytes) ||
+      output_aliases_badly(residual_out, t_bytes, x, residual, weight, row_bytes))
+    return ADD_RMSNORM_EALIAS;
 
-  // Path and shape.
-  int path = c.path;
-  if (path == ADD_RMSNORM_PATH_AUTO) {
-    path = hidden <= kWaveRowMaxHidden ? ADD_RMSNORM_PATH_WAVE_ROW
-           : hidden <= kWgRowMaxHidden ? ADD_RMSNORM_PATH_WG_ROW
-                                       : ADD_RMSNORM_PATH_LDS_TWO_PASS;
-  }
-  const int64_t segs = hidden / 8;
-  const addrms::FwdArgs a = {out, residual_out, x, residual, weight, n_rows, (int32_t)hidden,
-                             eps};
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-
-  if (path == ADD_RMSNORM_PATH_WAVE_ROW) {
-    const int b = c.block_threads ? c.block_threads : kWaveRowThreads;
-    const int j = pow2_at_least((segs + 63) / 64);
-    if (j == 0 || !addrms::wave_row_supported(b, j)) return ADD_RMSNORM_ERANGE;
-    int64_t grid = c.grid_blocks;
-    if (grid == -1) grid = addrms::resident_blocks_wave_row(b, j);
-    e = addrms::launch_wave_row(a, b, j, grid, s);
-  } else if (path == ADD_RMSNORM_PATH_WG_ROW) {
-    const int b = c.block_threads ? c.block_threads : kWgRowThreads;
-    const int j = pow2_at_least((segs + b - 1) / b);
-    if (j == 0 || !addrms::wg_row_supported(b, j)) return ADD_RMSNORM_ERANGE;
-    int64_t grid = c.grid_blocks;
-    if (grid == -1) grid = addrms::resident_blocks_wg_row(b, j);
-    e = addrms::launch_wg_row(a, b, j, grid, s);
-  } else {
-    const int b = c.block_threads ? c.block_threads : kTwoPassThreads;
-    int max_lds = 0;
-    const int rc = device_max_lds(&max_lds);
-    if (rc != ADD_RMSNORM_OK) return rc;
-    if (addrms::lds_two_pass_lds_bytes((int)hidden) > (size_t)max_lds) return ADD_RMSNORM_ERANGE;
-    int64_t grid = c.grid_blocks;
-    if (grid == -1) grid = addrms::resident_blocks_lds_two_pass(b, (int)hidden);
-    e = addrms::launch_lds_two_pass(a, b, grid, s);
-  }
-  if (e != hipSuccess) return hip_failure(e);
-  return ADD_RMSNORM_OK;
+  const addrms::FwdArgs a = {out, nullptr, nullptr, residual_out, x, residual, weight,
+                             n_rows, (int32_t)hidden, eps};
+  return dispatch(a, c, stream);
 }
 
 int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
@@ -150,6 +160,53 @@ int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
                     int64_t hidden, float eps, struct ihipStream_t* stream) {
   return add_rmsnorm_fwd_cfg(out, residual_out, x, residual, weight, n_rows, hidden, eps,
                              nullptr, stream);
+}
+
+int add_rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, uint16_t* residual_out,
+                              const uint16_t* x, const uint16_t* residual,
+                              const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                              const struct add_rmsnorm_launch_cfg* cfg,
+                              struct ihipStream_t* stream) {
+  add_rmsnorm_launch_cfg c;
+  int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
+  if (rc != ADD_RMSNORM_OK) return rc;
+  if (n_rows == 0) return ADD_RMSNORM_OK;
+
+  if (!out_q || !out_scale || !residual_out || !x || !residual || !weight)
+    return ADD_RMSNORM_EINVAL;
+  if (!aligned16(out_q) || !aligned(out_scale, 4) || !aligned16(residual_out) || !aligned16(x) ||
+      !aligned16(residual) || !aligned16(weight))
+    return ADD_RMSNORM_EALIGN;
+  const uint64_t row_bytes = (uint64_t)hidden * 2;
+  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
+  const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
+  const uint64_t q_bytes = (uint64_t)n_rows * (uint64_t)hidden;
+  const uint64_t s_bytes = (uint64_t)n_rows * 4;
+  // Codes and scales overlap nothing; residual_out as in the bf16 variant.
+  const void* ins[3] = {x, residual, weight};
+  const uint64_t in_bytes[3] = {t_bytes, t_bytes, row_bytes};
+  if (overlap(out_q, q_bytes, out_scale, s_bytes) ||
+      overlap(out_q, q_bytes, residual_out, t_bytes) ||
+      overlap(out_scale, s_bytes, residual_out, t_bytes))
+    return ADD_RMSNORM_EALIAS;
+  for (int i = 0; i < 3; ++i)
+    if (overlap(out_q, q_bytes, ins[i], in_bytes[i]) ||
+        overlap(out_scale, s_bytes, ins[i], in_bytes[i]))
+      return ADD_RMSNORM_EALIAS;
+  if (output_aliases_badly(residual_out, t_bytes, x, residual, weight, row_bytes))
+    return ADD_RMSNORM_EALIAS;
+
+  const addrms::FwdArgs a = {nullptr, out_q, out_scale, residual_out, x, residual, weight,
+                             n_rows, (int32_t)hidden, eps};
+  return dispatch(a, c, stream);
+}
+
+int add_rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, uint16_t* residual_out,
+                          const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
+                          int64_t n_rows, int64_t hidden, float eps,
+                          struct ihipStream_t* stream) {
+  return add_rmsnorm_quant_fwd_cfg(out_q, out_scale, residual_out, x, residual, weight, n_rows,
+                                   hidden, eps, nullptr, stream);
 }
 
 int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,
@@ -188,9 +245,9 @@ const char* add_rmsnorm_strerror(int status) {
     case ADD_RMSNORM_EINVAL:
       return "invalid argument (null pointer, negative rows, hidden <= 0, bad eps or launch "
              "configuration)";
-    case ADD_RMSNORM_EALIGN: return "a pointer is not 16-byte aligned, or hidden % 8 != 0";
+    case ADD_RMSNORM_EALIGN: return "a pointer is misaligned, or hidden % 8 != 0";
     case ADD_RMSNORM_EALIAS:
-      return "an output partly overlaps an input, or overlaps the weight or the other output";
+      return "an output partly overlaps an input, or overlaps the weight or another output";
     case ADD_RMSNORM_ERANGE: return "hidden (or the problem size) is above what the path supports";
     case ADD_RMSNORM_EHIP: return "the HIP launch failed (see add_rmsnorm_last_hip_error)";
   }

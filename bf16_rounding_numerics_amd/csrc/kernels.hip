@@ -28,6 +28,14 @@
 //     and square root (HIP's defaults; no fast-math), once per row.
 //   * y = (acc * rinv) * w: two fp32 multiplies in that order; no contraction
 //     (built with -ffp-contract=off).
+//   * Quantised variant (template flag Q): instead of bf16 out, per-row int8
+//     codes and an fp32 scale.  amax = max |y| over the row (a maximum is
+//     exact, so its order is free; a NaN wins), scale = amax / 127 and
+//     inv = 127 / amax (each correctly rounded, once per row), and
+//     q = y * inv rounded to the nearest integer, ties to even, within
+//     [-127, 127].  The inverse must be finite, so a row is quantised only
+//     when 2^-120 <= amax <= FLT_MAX; other rows (amax 0, tiny, Inf or NaN)
+//     get all-zero codes, and their scale is still amax / 127.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,13 +45,16 @@ namespace addrms {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define DEV __device__ __forceinline__
 
 struct Params {
-  u32x4* out;
+  u32x4* out;           // bf16 out (plain variant)
+  u32x2* qout;          // int8 codes, 8 per segment (quantised variant)
+  float* qscale;        // per-row scale (quantised variant)
   u32x4* residual_out;
   const u32x4* x;
   const u32x4* residual;
@@ -80,6 +91,15 @@ DEV u32x4 load_seg(__amdgpu_buffer_rsrc_t r, int s) {
 DEV void store_seg(__amdgpu_buffer_rsrc_t r, int s, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, s * 16, 0, 2);
 }
+
+// The same for a row of int8 codes (8 bytes per segment).
+DEV __amdgpu_buffer_rsrc_t code_row_rsrc(u32x2* t, int64_t row, int segs) {
+  return __builtin_amdgcn_make_buffer_rsrc(t + row * segs, 0, segs * 8, 0x00020000);
+}
+DEV void store_codes(__amdgpu_buffer_rsrc_t r, int s, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, s * 8, 0, 2);
+}
+DEV void store_codes_stream(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 
 // ---------------------------------------------------------------- numerics
 
@@ -118,6 +138,9 @@ DEV float seg_sumsq(const float (&a)[8]) {
   return t;
 }
 
+// Maximum in which a NaN operand wins.  Exact and order-free otherwise.
+DEV float max_nan(float m, float v) { return (m != m) ? m : ((v != v) || v > m) ? v : m; }
+
 // Cross-lane moves.  Each level adds two aligned sibling sub-blocks; once a
 // sub-block holds one value in all its lanes, a mirror within the enclosing
 // block reaches the sibling just as an xor would.
@@ -137,6 +160,19 @@ DEV float wave_block_sum(float v) {
   float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
   float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
   return lo + hi;
+}
+
+// Maximum over the 64 lanes (NaN wins); the same in every lane.  Must be
+// called with all 64 lanes active.
+DEV float wave_max(float v) {
+  v = max_nan(v, ADDRMS_DPP(v, 0xB1));
+  v = max_nan(v, ADDRMS_DPP(v, 0x4E));
+  v = max_nan(v, ADDRMS_DPP(v, 0x141));
+  v = max_nan(v, ADDRMS_DPP(v, 0x140));
+  v = max_nan(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F)));
+  float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  return max_nan(lo, hi);
 }
 
 // Balanced pairwise tree over N (a power of two) values in index order.
@@ -162,13 +198,44 @@ DEV float row_rinv(float sumsq, const Params& p) {
   return 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
 }
 
-// out = bf16((acc * rinv) * w) for one segment.
-DEV u32x4 normalise8(const float (&acc)[8], float rinv, u32x4 wq) {
-  float w[8], y[8];
+// y = (acc * rinv) * w for one segment.
+DEV void scale8(const float (&acc)[8], float rinv, u32x4 wq, float (&y)[8]) {
+  float w[8];
   unpack8(wq, w);
 #pragma unroll
   for (int k = 0; k < 8; ++k) y[k] = (acc[k] * rinv) * w[k];
+}
+
+// out = bf16((acc * rinv) * w) for one segment.
+DEV u32x4 normalise8(const float (&acc)[8], float rinv, u32x4 wq) {
+  float y[8];
+  scale8(acc, rinv, wq, y);
   return pack8_rne(y);
+}
+
+DEV float max_abs8(float m, const float (&y)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = max_nan(m, __builtin_fabsf(y[k]));
+  return m;
+}
+
+// Whether a row's codes are taken from y * inv: 127 / amax must be finite,
+// so 2^-120 <= amax <= FLT_MAX (false for NaN).
+DEV bool quantisable(float amax) { return amax >= 0x1p-120f && amax <= 3.40282347e38f; }
+
+// int8 codes of one segment: nearest-even integer of y * inv, kept within
+// [-127, 127].
+DEV u32x2 quant8(const float (&y)[8], float inv) {
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float t = __builtin_rintf(y[k] * inv);
+    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+    const uint32_t c = (uint32_t)(int)t & 0xFFu;
+    if (k < 4) w0 |= c << (8 * k);
+    else w1 |= c << (8 * (k - 4));
+  }
+  return u32x2{w0, w1};
 }
 
 // acc = x + r for one segment, without the sum of squares.
@@ -210,7 +277,7 @@ DEV float add_segment(u32x4 xq, u32x4 rq, float (&acc)[8]) {
 // per-lane register footprint small enough for more rows in flight per CU.
 // Rows are read and written through per-row buffer resources: segments past
 // the row read as zero and their stores are dropped, so nothing branches.
-template <int WAVES, int J>
+template <int WAVES, int J, bool Q>
 __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
   __shared__ u32x4 wl[64 * J];
   const int lane = threadIdx.x & 63;
@@ -244,11 +311,37 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 #pragma unroll
     for (int j = 0; j < J; ++j) blk[j] = wave_block_sum(blk[j]);
     const float rinv = row_rinv(pairwise_tree<J>(blk), p);
+    if constexpr (!Q) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      float acc[8];
-      add8(opaque(xq[j]), opaque(rq[j]), acc);
-      store_seg(oo, lane + 64 * j, normalise8(acc, rinv, wl[opaque(lane + 64 * j)]));
+      for (int j = 0; j < J; ++j) {
+        float acc[8];
+        add8(opaque(xq[j]), opaque(rq[j]), acc);
+        store_seg(oo, lane + 64 * j, normalise8(acc, rinv, wl[opaque(lane + 64 * j)]));
+      }
+    } else {
+      // y twice (the same fp32 operations, so the same values): once for the
+      // row maximum, once for the codes.
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        float acc[8], y[8];
+        add8(opaque(xq[j]), opaque(rq[j]), acc);
+        scale8(acc, rinv, wl[opaque(lane + 64 * j)], y);
+        if (lane + 64 * j < C) m = max_abs8(m, y);
+      }
+      const float amax = wave_max(m);
+      const float scale = amax / 127.0f;
+      const float inv = 127.0f / amax;
+      const bool ok = quantisable(amax);
+      if (lane == 0) p.qscale[row] = scale;
+      const __amdgpu_buffer_rsrc_t qo = code_row_rsrc(p.qout, row, C);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        float acc[8], y[8];
+        add8(opaque(xq[j]), opaque(rq[j]), acc);
+        scale8(acc, rinv, wl[opaque(lane + 64 * j)], y);
+        store_codes(qo, lane + 64 * j, ok ? quant8(y, inv) : u32x2{0, 0});
+      }
     }
   }
 }
@@ -258,11 +351,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 // B threads per row; thread t holds segments t, t + B, ..., t + B (J - 1).
 // For each j, wave w's butterfly yields the sum of block w + j * (B / 64);
 // the B / 64 * J block sums meet in LDS and every thread finishes the tree.
-template <int B, int J>
+template <int B, int J, bool Q>
 __global__ __launch_bounds__(B) void k_wg_row(Params p) {
   constexpr int W = B / 64;
   constexpr int NB = W * J;
   __shared__ float blk[2][NB];  // alternates by row so one barrier per row suffices
+  __shared__ float mx[2][Q ? W : 1];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -306,10 +400,37 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
     }
     __syncthreads();
     const float rinv = row_rinv(pairwise_tree_lds<NB>(blk[parity]), p);
+    if constexpr (!Q) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int s = t + B * j;
-      if (s < C) store_stream(p.out + base + s, normalise8(acc[j], rinv, wq[j]));
+      for (int j = 0; j < J; ++j) {
+        const int s = t + B * j;
+        if (s < C) store_stream(p.out + base + s, normalise8(acc[j], rinv, wq[j]));
+      }
+    } else {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        float y[8];
+        scale8(acc[j], rinv, wq[j], y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[j][k] = y[k];
+        if (t + B * j < C) m = max_abs8(m, y);
+      }
+      m = wave_max(m);
+      if (lane == 0) mx[parity][wave] = m;
+      __syncthreads();
+      float amax = mx[parity][0];
+#pragma unroll
+      for (int i = 1; i < W; ++i) amax = max_nan(amax, mx[parity][i]);
+      const float scale = amax / 127.0f;
+      const float inv = 127.0f / amax;
+      const bool ok = quantisable(amax);
+      if (t == 0) p.qscale[row] = scale;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int s = t + B * j;
+        if (s < C) store_codes_stream(p.qout + base + s, ok ? quant8(acc[j], inv) : u32x2{0, 0});
+      }
     }
   }
 }
@@ -326,10 +447,11 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
 // each wavefront keeps U chunks of x and residual in flight.  Loads go
 // through a per-row buffer resource: segments past the row read as zero,
 // without a branch.
-template <int B, int NB, int U>
+template <int B, int NB, int U, bool Q>
 __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
   constexpr int W = B / 64;
   __shared__ float blk[NB];
+  __shared__ float mx[Q ? W : 1];
   extern __shared__ float4 stage[];  // [2][C]: elements 0-3, then 4-7, of each segment
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -370,15 +492,50 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
     }
     __syncthreads();
     const float rinv = row_rinv(pairwise_tree_lds<NB>(blk), p);
-    for (int c = 0; c < chunks; ++c) {
-      const int s = c * B + t;
-      if (s < C) {
-        const float4 l = lo[s], h = hi[s];
-        const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
-        store_stream(p.out + base + s, normalise8(acc, rinv, p.weight[s]));
+    if constexpr (!Q) {
+      for (int c = 0; c < chunks; ++c) {
+        const int s = c * B + t;
+        if (s < C) {
+          const float4 l = lo[s], h = hi[s];
+          const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
+          store_stream(p.out + base + s, normalise8(acc, rinv, p.weight[s]));
+        }
+      }
+    } else {
+      // y from the staged sums twice: for the row maximum, then for the codes.
+      float m = 0.0f;
+      for (int c = 0; c < chunks; ++c) {
+        const int s = c * B + t;
+        if (s < C) {
+          const float4 l = lo[s], h = hi[s];
+          const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
+          float y[8];
+          scale8(acc, rinv, p.weight[s], y);
+          m = max_abs8(m, y);
+        }
+      }
+      m = wave_max(m);
+      if (lane == 0) mx[wave] = m;
+      __syncthreads();
+      float amax = mx[0];
+#pragma unroll
+      for (int i = 1; i < W; ++i) amax = max_nan(amax, mx[i]);
+      const float scale = amax / 127.0f;
+      const float inv = 127.0f / amax;
+      const bool ok = quantisable(amax);
+      if (t == 0) p.qscale[row] = scale;
+      for (int c = 0; c < chunks; ++c) {
+        const int s = c * B + t;
+        if (s < C) {
+          const float4 l = lo[s], h = hi[s];
+          const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
+          float y[8];
+          scale8(acc, rinv, p.weight[s], y);
+          store_codes_stream(p.qout + base + s, ok ? quant8(y, inv) : u32x2{0, 0});
+        }
       }
     }
-    __syncthreads();  // blk is rewritten by the next row
+    __syncthreads();  // blk (and mx) are rewritten by the next row
   }
 }
 
@@ -416,6 +573,8 @@ __global__ __launch_bounds__(256) void k_copy2(u32x4* d0, u32x4* d1, const u32x4
 Params make_params(const FwdArgs& a) {
   Params p;
   p.out = reinterpret_cast<u32x4*>(a.out);
+  p.qout = reinterpret_cast<u32x2*>(a.qout);
+  p.qscale = a.qscale;
   p.residual_out = reinterpret_cast<u32x4*>(a.residual_out);
   p.x = reinterpret_cast<const u32x4*>(a.x);
   p.residual = reinterpret_cast<const u32x4*>(a.residual);
@@ -437,6 +596,7 @@ unsigned grid_for(int64_t grid_blocks, int64_t row_groups) {
   return (unsigned)g;
 }
 
+// Workgroups of a kernel that fit on the current device at once; 0 if unknown.
 template <typename K>
 int64_t resident(K kernel, int block_threads, size_t lds) {
   int dev = 0, per_cu = 0, cus = 0;
@@ -447,52 +607,6 @@ int64_t resident(K kernel, int block_threads, size_t lds) {
       hipSuccess)
     return 0;
   return (int64_t)per_cu * cus;
-}
-
-template <int WAVES, int J>
-hipError_t go_wave(const Params& p, int64_t grid_blocks, hipStream_t s) {
-  const int64_t groups = (p.n_rows + WAVES - 1) / WAVES;
-  hipLaunchKernelGGL((k_wave_row<WAVES, J>), dim3(grid_for(grid_blocks, groups)),
-                     dim3(WAVES * 64), 0, s, p);
-  return hipGetLastError();
-}
-
-// Combinations that would not fit the register file (segments held per thread
-// times threads per workgroup) are not built; wave_row_supported() and
-// wg_row_supported() say which exist.
-template <int WAVES>
-hipError_t go_wave_j(const Params& p, int j, int64_t grid_blocks, hipStream_t s) {
-  switch (j) {
-    case 1: return go_wave<WAVES, 1>(p, grid_blocks, s);
-    case 2: return go_wave<WAVES, 2>(p, grid_blocks, s);
-    case 4: return go_wave<WAVES, 4>(p, grid_blocks, s);
-    case 8:
-      if constexpr (WAVES < 16) return go_wave<WAVES, 8>(p, grid_blocks, s);
-      break;
-  }
-  return hipErrorInvalidValue;
-}
-
-template <int B, int J>
-hipError_t go_wg(const Params& p, int64_t grid_blocks, hipStream_t s) {
-  hipLaunchKernelGGL((k_wg_row<B, J>), dim3(grid_for(grid_blocks, p.n_rows)), dim3(B), 0, s,
-                     p);
-  return hipGetLastError();
-}
-
-template <int B>
-hipError_t go_wg_j(const Params& p, int j, int64_t grid_blocks, hipStream_t s) {
-  switch (j) {
-    case 1: return go_wg<B, 1>(p, grid_blocks, s);
-    case 2: return go_wg<B, 2>(p, grid_blocks, s);
-    case 4:
-      if constexpr (B * 4 <= 2048) return go_wg<B, 4>(p, grid_blocks, s);
-      break;
-    case 8:
-      if constexpr (B * 8 <= 2048) return go_wg<B, 8>(p, grid_blocks, s);
-      break;
-  }
-  return hipErrorInvalidValue;
 }
 
 // Padded block count of the two-pass tree: 32 blocks of 64 segments cover
@@ -506,18 +620,92 @@ constexpr int two_pass_batch() {
   return 2048 / B < 4 ? 2048 / B : 4;
 }
 
-template <int B, int NB>
-hipError_t go_two_pass(const Params& p, int64_t grid_blocks, hipStream_t s) {
-  const size_t lds = (size_t)p.segs * 32;
-  hipLaunchKernelGGL((k_lds_two_pass<B, NB, two_pass_batch<B>()>),
-                     dim3(grid_for(grid_blocks, p.n_rows)), dim3(B), lds, s, p);
+// A kernel instance and its launch: `grid_blocks` -1 asks for the resident
+// maximum, 0 for one workgroup per row group.
+template <typename K>
+hipError_t launch(K kernel, int block_threads, size_t lds, int64_t grid_blocks,
+                  int64_t row_groups, const Params& p, hipStream_t s) {
+  if (grid_blocks == -1) grid_blocks = resident(kernel, block_threads, lds);
+  hipLaunchKernelGGL(kernel, dim3(grid_for(grid_blocks, row_groups)), dim3(block_threads), lds,
+                     s, p);
   return hipGetLastError();
 }
 
-template <int B>
-hipError_t go_two_pass_nb(const Params& p, int hidden, int64_t grid_blocks, hipStream_t s) {
-  if (two_pass_nb(hidden) == 32) return go_two_pass<B, 32>(p, grid_blocks, s);
-  return go_two_pass<B, 64>(p, grid_blocks, s);
+// Combinations that would not fit the register file (segments held per thread
+// times threads per workgroup) are not built; wave_row_supported() and
+// wg_row_supported() say which exist.
+template <bool Q, int WAVES>
+hipError_t go_wave(const Params& p, int j, int64_t grid, hipStream_t s) {
+  const int64_t groups = (p.n_rows + WAVES - 1) / WAVES;
+  switch (j) {
+    case 1: return launch(k_wave_row<WAVES, 1, Q>, WAVES * 64, 0, grid, groups, p, s);
+    case 2: return launch(k_wave_row<WAVES, 2, Q>, WAVES * 64, 0, grid, groups, p, s);
+    case 4: return launch(k_wave_row<WAVES, 4, Q>, WAVES * 64, 0, grid, groups, p, s);
+    case 8:
+      if constexpr (WAVES < 16)
+        return launch(k_wave_row<WAVES, 8, Q>, WAVES * 64, 0, grid, groups, p, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool Q, int B>
+hipError_t go_wg(const Params& p, int j, int64_t grid, hipStream_t s) {
+  switch (j) {
+    case 1: return launch(k_wg_row<B, 1, Q>, B, 0, grid, p.n_rows, p, s);
+    case 2: return launch(k_wg_row<B, 2, Q>, B, 0, grid, p.n_rows, p, s);
+    case 4:
+      if constexpr (B * 4 <= 2048) return launch(k_wg_row<B, 4, Q>, B, 0, grid, p.n_rows, p, s);
+      break;
+    case 8:
+      if constexpr (B * 8 <= 2048) return launch(k_wg_row<B, 8, Q>, B, 0, grid, p.n_rows, p, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool Q, int B>
+hipError_t go_two_pass(const Params& p, int hidden, int64_t grid, hipStream_t s) {
+  const size_t lds = (size_t)p.segs * 32;
+  if (two_pass_nb(hidden) == 32)
+    return launch(k_lds_two_pass<B, 32, two_pass_batch<B>(), Q>, B, lds, grid, p.n_rows, p, s);
+  return launch(k_lds_two_pass<B, 64, two_pass_batch<B>(), Q>, B, lds, grid, p.n_rows, p, s);
+}
+
+template <bool Q>
+hipError_t wave_by_block(const Params& p, int b, int j, int64_t grid, hipStream_t s) {
+  switch (b) {
+    case 64: return go_wave<Q, 1>(p, j, grid, s);
+    case 128: return go_wave<Q, 2>(p, j, grid, s);
+    case 256: return go_wave<Q, 4>(p, j, grid, s);
+    case 512: return go_wave<Q, 8>(p, j, grid, s);
+    case 1024: return go_wave<Q, 16>(p, j, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool Q>
+hipError_t wg_by_block(const Params& p, int b, int j, int64_t grid, hipStream_t s) {
+  switch (b) {
+    case 64: return go_wg<Q, 64>(p, j, grid, s);
+    case 128: return go_wg<Q, 128>(p, j, grid, s);
+    case 256: return go_wg<Q, 256>(p, j, grid, s);
+    case 512: return go_wg<Q, 512>(p, j, grid, s);
+    case 1024: return go_wg<Q, 1024>(p, j, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool Q>
+hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, hipStream_t s) {
+  switch (b) {
+    case 64: return go_two_pass<Q, 64>(p, hidden, grid, s);
+    case 128: return go_two_pass<Q, 128>(p, hidden, grid, s);
+    case 256: return go_two_pass<Q, 256>(p, hidden, grid, s);
+    case 512: return go_two_pass<Q, 512>(p, hidden, grid, s);
+    case 1024: return go_two_pass<Q, 1024>(p, hidden, grid, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -527,40 +715,22 @@ hipError_t go_two_pass_nb(const Params& p, int hidden, int64_t grid_blocks, hipS
 hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
                            int64_t grid_blocks, hipStream_t s) {
   const Params p = make_params(a);
-  switch (block_threads) {
-    case 64: return go_wave_j<1>(p, segs_per_lane, grid_blocks, s);
-    case 128: return go_wave_j<2>(p, segs_per_lane, grid_blocks, s);
-    case 256: return go_wave_j<4>(p, segs_per_lane, grid_blocks, s);
-    case 512: return go_wave_j<8>(p, segs_per_lane, grid_blocks, s);
-    case 1024: return go_wave_j<16>(p, segs_per_lane, grid_blocks, s);
-  }
-  return hipErrorInvalidValue;
+  return a.qout ? wave_by_block<true>(p, block_threads, segs_per_lane, grid_blocks, s)
+                : wave_by_block<false>(p, block_threads, segs_per_lane, grid_blocks, s);
 }
 
 hipError_t launch_wg_row(const FwdArgs& a, int block_threads, int segs_per_thread,
                          int64_t grid_blocks, hipStream_t s) {
   const Params p = make_params(a);
-  switch (block_threads) {
-    case 64: return go_wg_j<64>(p, segs_per_thread, grid_blocks, s);
-    case 128: return go_wg_j<128>(p, segs_per_thread, grid_blocks, s);
-    case 256: return go_wg_j<256>(p, segs_per_thread, grid_blocks, s);
-    case 512: return go_wg_j<512>(p, segs_per_thread, grid_blocks, s);
-    case 1024: return go_wg_j<1024>(p, segs_per_thread, grid_blocks, s);
-  }
-  return hipErrorInvalidValue;
+  return a.qout ? wg_by_block<true>(p, block_threads, segs_per_thread, grid_blocks, s)
+                : wg_by_block<false>(p, block_threads, segs_per_thread, grid_blocks, s);
 }
 
 hipError_t launch_lds_two_pass(const FwdArgs& a, int block_threads, int64_t grid_blocks,
                                hipStream_t s) {
   const Params p = make_params(a);
-  switch (block_threads) {
-    case 64: return go_two_pass_nb<64>(p, a.hidden, grid_blocks, s);
-    case 128: return go_two_pass_nb<128>(p, a.hidden, grid_blocks, s);
-    case 256: return go_two_pass_nb<256>(p, a.hidden, grid_blocks, s);
-    case 512: return go_two_pass_nb<512>(p, a.hidden, grid_blocks, s);
-    case 1024: return go_two_pass_nb<1024>(p, a.hidden, grid_blocks, s);
-  }
-  return hipErrorInvalidValue;
+  return a.qout ? two_pass_by_block<true>(p, block_threads, a.hidden, grid_blocks, s)
+                : two_pass_by_block<false>(p, block_threads, a.hidden, grid_blocks, s);
 }
 
 bool wave_row_supported(int block_threads, int segs_per_lane) {
@@ -572,76 +742,7 @@ bool wg_row_supported(int block_threads, int segs_per_thread) {
 }
 
 size_t lds_two_pass_lds_bytes(int hidden) {
-  return (size_t)(hidden / 8) * 32 + (size_t)two_pass_nb(hidden) * sizeof(float);
-}
-
-namespace {
-template <int WAVES>
-int64_t res_wave(int j) {
-  switch (j) {
-    case 1: return resident(k_wave_row<WAVES, 1>, WAVES * 64, 0);
-    case 2: return resident(k_wave_row<WAVES, 2>, WAVES * 64, 0);
-    case 4: return resident(k_wave_row<WAVES, 4>, WAVES * 64, 0);
-    case 8:
-      if constexpr (WAVES < 16) return resident(k_wave_row<WAVES, 8>, WAVES * 64, 0);
-      break;
-  }
-  return 0;
-}
-template <int B>
-int64_t res_wg(int j) {
-  switch (j) {
-    case 1: return resident(k_wg_row<B, 1>, B, 0);
-    case 2: return resident(k_wg_row<B, 2>, B, 0);
-    case 4:
-      if constexpr (B * 4 <= 2048) return resident(k_wg_row<B, 4>, B, 0);
-      break;
-    case 8:
-      if constexpr (B * 8 <= 2048) return resident(k_wg_row<B, 8>, B, 0);
-      break;
-  }
-  return 0;
-}
-template <int B>
-int64_t res_two_pass(int hidden) {
-  const size_t lds = (size_t)(hidden / 8) * 32;
-  if (two_pass_nb(hidden) == 32)
-    return resident(k_lds_two_pass<B, 32, two_pass_batch<B>()>, B, lds);
-  return resident(k_lds_two_pass<B, 64, two_pass_batch<B>()>, B, lds);
-}
-}  // namespace
-
-int64_t resident_blocks_wave_row(int block_threads, int segs_per_lane) {
-  switch (block_threads) {
-    case 64: return res_wave<1>(segs_per_lane);
-    case 128: return res_wave<2>(segs_per_lane);
-    case 256: return res_wave<4>(segs_per_lane);
-    case 512: return res_wave<8>(segs_per_lane);
-    case 1024: return res_wave<16>(segs_per_lane);
-  }
-  return 0;
-}
-
-int64_t resident_blocks_wg_row(int block_threads, int segs_per_thread) {
-  switch (block_threads) {
-    case 64: return res_wg<64>(segs_per_thread);
-    case 128: return res_wg<128>(segs_per_thread);
-    case 256: return res_wg<256>(segs_per_thread);
-    case 512: return res_wg<512>(segs_per_thread);
-    case 1024: return res_wg<1024>(segs_per_thread);
-  }
-  return 0;
-}
-
-int64_t resident_blocks_lds_two_pass(int block_threads, int hidden) {
-  switch (block_threads) {
-    case 64: return res_two_pass<64>(hidden);
-    case 128: return res_two_pass<128>(hidden);
-    case 256: return res_two_pass<256>(hidden);
-    case 512: return res_two_pass<512>(hidden);
-    case 1024: return res_two_pass<1024>(hidden);
-  }
-  return 0;
+  return (size_t)(hidden / 8) * 32 + (size_t)two_pass_nb(hidden) * sizeof(float) + 64;
 }
 
 hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,

@@ -8,7 +8,9 @@
 namespace addrms {
 
 struct FwdArgs {
-  uint16_t* out;
+  uint16_t* out;           // bf16 out, or null for the quantised variant
+  int8_t* qout;            // int8 codes (quantised variant), else null
+  float* qscale;           // per-row scale (quantised variant), else null
   uint16_t* residual_out;
   const uint16_t* x;
   const uint16_t* residual;
@@ -23,7 +25,9 @@ constexpr int kMaxSegments = 32768 / 8;
 
 // One wavefront per row, block_threads / 64 rows per workgroup.  The row's
 // segments are spread over the 64 lanes, segs_per_lane (1, 2, 4 or 8) each.
-// grid_blocks > 0 launches that many workgroups, which loop over the rows.
+// grid_blocks > 0 launches that many workgroups, which loop over the rows;
+// -1 launches as many as fit on the device at once; 0 one per row group.
+// The quantised variant runs when FwdArgs::qout is set.
 hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
                            int64_t grid_blocks, hipStream_t stream);
 
@@ -43,12 +47,6 @@ size_t lds_two_pass_lds_bytes(int hidden);
 // per-thread row share fits the register file without spilling.
 bool wave_row_supported(int block_threads, int segs_per_lane);
 bool wg_row_supported(int block_threads, int segs_per_thread);
-
-// Workgroups of the given kernel that fit on the current device at once
-// (occupancy x compute units); 0 if the query fails.
-int64_t resident_blocks_wave_row(int block_threads, int segs_per_lane);
-int64_t resident_blocks_wg_row(int block_threads, int segs_per_thread);
-int64_t resident_blocks_lds_two_pass(int block_threads, int hidden);
 
 // Reference copy: d0 <- s0 and d1 <- s1, count 16-bit elements each.
 hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,

@@ -56,8 +56,8 @@ struct ihipStream_t;
 /* Status codes. */
 #define ADD_RMSNORM_OK 0
 #define ADD_RMSNORM_EINVAL (-1) /* null pointer, n_rows < 0, hidden <= 0, eps < 0 or not finite, bad cfg */
-#define ADD_RMSNORM_EALIGN (-2) /* a pointer not 16-byte aligned, or hidden % 8 != 0 */
-#define ADD_RMSNORM_EALIAS (-3) /* an output partly overlaps an input, or overlaps the weight or the other output */
+#define ADD_RMSNORM_EALIGN (-2) /* a pointer misaligned (16 bytes; 4 for scales), or hidden % 8 != 0 */
+#define ADD_RMSNORM_EALIAS (-3) /* an output partly overlaps an input, or overlaps the weight or another output */
 #define ADD_RMSNORM_ERANGE (-4) /* hidden above the maximum (of the library, the chosen path or the device) */
 #define ADD_RMSNORM_EHIP (-5)   /* the HIP launch failed; add_rmsnorm_last_hip_error() has the detail */
 
@@ -120,6 +120,38 @@ int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x
                         const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
                         int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
                         struct ihipStream_t* stream);
+
+/*
+ * Quantised variant: the same row computation with out replaced by per-row
+ * symmetric int8 codes, the FUSE_QUANT sibling of the fused kernel in the
+ * aiter issue ("Cost of fixing": in the quantised configurations out goes
+ * through a scaled cast instead of the bf16 conversion; the cast itself is
+ * not given there, this is the plain per-row int8 reading).  With
+ * y_j = (acc_j * rinv) * w_j as above (fp32):
+ *   amax          = max_j |y_j|                       (exact; NaN wins)
+ *   out_scale[i]  = amax / 127                        (fp32, correctly rounded)
+ *   inv           = 127 / amax                        (fp32, correctly rounded)
+ *   out_q[i, j]   = y_j * inv (fp32) rounded to the nearest integer, ties to
+ *                   even, within [-127, 127]
+ * inv must be finite, so a row is quantised only when 2^-120 <= amax <=
+ * FLT_MAX; any other row (amax 0, tiny, Inf or NaN) gets all-zero codes, and
+ * its scale is still amax / 127.  residual_out is exactly as in
+ * add_rmsnorm_fwd and may be residual itself (in place).
+ *   out_q      [n_rows, hidden] int8, written, 16-byte aligned.
+ *   out_scale  [n_rows] fp32, written, 4-byte aligned.
+ * Codes and scales must not overlap any other buffer (ADD_RMSNORM_EALIAS).
+ * Everything else (sizes, alignment, errors, stream) as add_rmsnorm_fwd.
+ */
+int add_rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, uint16_t* residual_out,
+                          const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
+                          int64_t n_rows, int64_t hidden, float eps, struct ihipStream_t* stream);
+
+/* add_rmsnorm_quant_fwd with an explicit launch configuration (same results). */
+int add_rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, uint16_t* residual_out,
+                              const uint16_t* x, const uint16_t* residual,
+                              const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                              const struct add_rmsnorm_launch_cfg* cfg,
+                              struct ihipStream_t* stream);
 
 /*
  * Test hook for the store epilogue: out[i] = bf16_rne of the fp32 whose bit

@@ -188,6 +188,44 @@ def test_cvt_range_errors():
     assert L.add_rmsnorm_test_cvt_range(0, 0, 0, None) == arn.OK
 
 
+def qcall(q=A + 5 * MB, sc=A + 6 * MB, res=A + MB, x=A + 2 * MB, r=A + 3 * MB, w=A + 4 * MB,
+          n=4, h=64, eps=1e-6, cfg=None):
+    L = arn.lib()
+    if cfg is None:
+        return L.add_rmsnorm_quant_fwd(q, sc, res, x, r, w, n, h, eps, None)
+    c = arn.LaunchCfg(*cfg)
+    return L.add_rmsnorm_quant_fwd_cfg(q, sc, res, x, r, w, n, h, eps, ctypes.byref(c), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), arn.EINVAL),
+    (dict(h=12), arn.EALIGN),
+    (dict(h=32776), arn.ERANGE),
+    (dict(eps=math.nan), arn.EINVAL),
+    (dict(q=0), arn.EINVAL),
+    (dict(sc=0), arn.EINVAL),
+    (dict(q=A + 5 * MB + 8), arn.EALIGN),
+    (dict(sc=A + 6 * MB + 2), arn.EALIGN),
+    (dict(q=A + 2 * MB), arn.EALIAS),                   # codes on x
+    (dict(sc=A + 3 * MB + 64), arn.EALIAS),             # scales inside residual
+    (dict(sc=A + 5 * MB + 16), arn.EALIAS),             # scales inside the codes
+    (dict(q=A + MB + 128), arn.EALIAS),                 # codes inside residual_out
+    (dict(res=A + 3 * MB - 16), arn.EALIAS),            # residual_out partly on residual
+    (dict(res=A + 4 * MB), arn.EALIAS),                 # residual_out on the weight
+])
+@fake_addresses
+def test_quant_argument_errors(kw, status):
+    assert qcall(**kw) == status
+
+
+@fake_addresses
+def test_quant_zero_rows_and_in_place_validation():
+    assert qcall(q=0, sc=0, res=0, x=0, r=0, w=0, n=0) == arn.OK
+    # residual_out == residual passes the alias checks (ERANGE from the forced
+    # path comes after them; nothing is launched).
+    assert qcall(res=A + 3 * MB, h=8192, cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.ERANGE
+
+
 @fake_addresses
 def test_copy2_errors():
     L = arn.lib()
