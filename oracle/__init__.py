@@ -165,6 +165,49 @@ class Oracle:
         return q, sc, res_out
 
 
+    # ------------------------------------------------------------ plain RMSNorm
+
+    def rmsnorm(self, x: np.ndarray, weight: np.ndarray, eps: float = 1e-6,
+                rounding: int = RNE, want_exact: bool = False):
+        """Plain RMSNorm (no residual): acc = fp32(x), the rest as add_rmsnorm.
+
+        Returns out (uint16 [n, hidden]), plus the binary64 out values when
+        ``want_exact`` is set.
+        """
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        weight = np.ascontiguousarray(weight, dtype=np.uint16)
+        if x.ndim != 2 or weight.shape != (x.shape[1],):
+            raise ValueError("shape mismatch: x %s weight %s" % (x.shape, weight.shape))
+        n, h = x.shape
+        out = np.empty_like(x)
+        y = np.empty(x.shape, dtype=np.float64) if want_exact else None
+        rc = self.lib.orc_add_rmsnorm(_ptr(out), None, _ptr(y) if y is not None else None,
+                                      _ptr(x), None, _ptr(weight), n, h, ctypes.c_float(eps),
+                                      rounding)
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+        return (out, y) if want_exact else out
+
+    def rmsnorm_quant(self, x: np.ndarray, weight: np.ndarray, eps: float = 1e-6,
+                      want_exact: bool = False):
+        """Plain RMSNorm with int8 out: (codes, scale), plus the binary64 y
+        when asked."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        weight = np.ascontiguousarray(weight, dtype=np.uint16)
+        if x.ndim != 2 or weight.shape != (x.shape[1],):
+            raise ValueError("shape mismatch")
+        n, h = x.shape
+        q = np.empty(x.shape, dtype=np.int8)
+        sc = np.empty(n, dtype=np.float32)
+        y = np.empty(x.shape, dtype=np.float64) if want_exact else None
+        rc = self.lib.orc_add_rmsnorm_quant(_ptr(q), _ptr(sc), None,
+                                            _ptr(y) if y is not None else None, _ptr(x), None,
+                                            _ptr(weight), n, h, ctypes.c_float(eps))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+        return (q, sc, y) if want_exact else (q, sc)
+
+
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
@@ -214,6 +257,14 @@ def add_rmsnorm(x, residual, weight, eps: float = 1e-6, rounding: int = RNE,
 
 def add_rmsnorm_quant(x, residual, weight, eps: float = 1e-6, want_exact: bool = False):
     return default().add_rmsnorm_quant(x, residual, weight, eps, want_exact)
+
+
+def rmsnorm(x, weight, eps: float = 1e-6, rounding: int = RNE, want_exact: bool = False):
+    return default().rmsnorm(x, weight, eps, rounding, want_exact)
+
+
+def rmsnorm_quant(x, weight, eps: float = 1e-6, want_exact: bool = False):
+    return default().rmsnorm_quant(x, weight, eps, want_exact)
 
 
 # ---------------------------------------------------------------- measurements

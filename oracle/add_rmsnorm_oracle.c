@@ -22,6 +22,13 @@
  * correctly, from the binary64 value.  The GPU path works in fp32 and may land
  * one bf16 ULP away from this value near a rounding boundary.
  *
+ * Plain RMSNorm (no residual): the same row computation with acc = fp32(x)
+ * and no residual_out.  The issue's notes list other norm kernels with bf16
+ * stores (the q/k norms, the norm kernel used above hidden 8192) beside the
+ * fused one; their normalisation is the part of reference() after the add.
+ * Passing residual = residual_out = NULL selects it.  acc is then x itself,
+ * with no addition at all: adding +0 would turn -0 into +0.
+ *
  * The truncation mode (rounding = 1) is the negative control from the same
  * issue (its bf16_truncate helper and "mode 2" of fp32_to_bf16): it keeps the
  * high 16 bits of the fp32 value.  It exists only to show that the tests can
@@ -109,6 +116,13 @@ void orc_rne16_from_f64_array(const double* in, uint16_t* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_rne16_from_f64(in[i]);
 }
 
+/* Step 1 for element j of a row: x + residual in fp32, or x alone when the
+ * row has no residual (plain RMSNorm). */
+static float row_acc(const uint16_t* xr, const uint16_t* rr, int64_t j) {
+  if (!rr) return bf16_to_f32(xr[j]);
+  return bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]);
+}
+
 /*
  * The fused op over n_rows x hidden, row-major, contiguous; weight is [hidden].
  * All arrays hold raw bf16 bit patterns.  y_exact (may be NULL) receives the
@@ -129,6 +143,8 @@ void orc_rne16_from_f64_array(const double* in, uint16_t* out, int64_t n) {
  *   7. out_j = bf16(y_j), rounded once from binary64.
  * In truncation mode steps 2 and 7 keep the high half of the fp32 value
  * instead (for step 7, of y_j first rounded to fp32, as an fp32 kernel would).
+ * Plain RMSNorm: residual and residual_out both NULL; step 1 is acc_j =
+ * fp32(x_j) and step 2 is skipped.
  */
 int orc_add_rmsnorm(uint16_t* out, uint16_t* residual_out, double* y_exact,
                     const uint16_t* x, const uint16_t* residual,
@@ -137,20 +153,22 @@ int orc_add_rmsnorm(uint16_t* out, uint16_t* residual_out, double* y_exact,
   if (n_rows < 0 || hidden <= 0) return -1;
   if (rounding != ORC_RNE && rounding != ORC_TRUNC) return -1;
   if (n_rows == 0) return 0;
-  if (!out || !residual_out || !x || !residual || !weight) return -1;
+  if (!out || !x || !weight || !residual != !residual_out) return -1;
 
   const double f32_overflow = ldexp(2.0 - ldexp(1.0, -24), 127);
   for (int64_t i = 0; i < n_rows; ++i) {
     const uint16_t* xr = x + i * hidden;
-    const uint16_t* rr = residual + i * hidden;
-    uint16_t* ro = residual_out + i * hidden;
+    const uint16_t* rr = residual ? residual + i * hidden : NULL;
+    uint16_t* ro = residual_out ? residual_out + i * hidden : NULL;
     uint16_t* orow = out + i * hidden;
 
     double s = 0.0;
     for (int64_t j = 0; j < hidden; ++j) {
-      float acc = bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]);
-      uint32_t ab = f32_bits(acc);
-      ro[j] = rounding == ORC_RNE ? orc_rne16(ab) : orc_trunc16(ab);
+      float acc = row_acc(xr, rr, j);
+      if (ro) {
+        uint32_t ab = f32_bits(acc);
+        ro[j] = rounding == ORC_RNE ? orc_rne16(ab) : orc_trunc16(ab);
+      }
       double a = (double)acc;
       s += a * a;
     }
@@ -159,7 +177,7 @@ int orc_add_rmsnorm(uint16_t* out, uint16_t* residual_out, double* y_exact,
 
     for (int64_t j = 0; j < hidden; ++j) {
       /* acc again, as in step 1: recomputing is cheaper than a row buffer. */
-      double a = (double)(bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]));
+      double a = (double)row_acc(xr, rr, j);
       double y = (a * rinv) * (double)bf16_to_f32(weight[j]);
       if (y_exact) y_exact[i * hidden + j] = y;
       orow[j] = rounding == ORC_RNE ? orc_rne16_from_f64(y)
@@ -196,23 +214,24 @@ static float max_nan(float m, float v) {
  * scale, the inverse scale, the product and its rounding are binary32
  * operations.
  * residual_out is as in orc_add_rmsnorm.  y_exact (may be NULL) receives the
- * binary64 y.  Returns 0, or -1 on a bad argument.
+ * binary64 y.  Plain RMSNorm as in orc_add_rmsnorm: residual and
+ * residual_out both NULL.  Returns 0, or -1 on a bad argument.
  */
 int orc_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, double* y_exact,
                           const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
                           int64_t n_rows, int64_t hidden, float eps) {
   if (n_rows < 0 || hidden <= 0) return -1;
   if (n_rows == 0) return 0;
-  if (!q || !scale || !residual_out || !x || !residual || !weight) return -1;
+  if (!q || !scale || !x || !weight || !residual != !residual_out) return -1;
 
   const double f32_overflow = ldexp(2.0 - ldexp(1.0, -24), 127);
   for (int64_t i = 0; i < n_rows; ++i) {
     const uint16_t* xr = x + i * hidden;
-    const uint16_t* rr = residual + i * hidden;
+    const uint16_t* rr = residual ? residual + i * hidden : NULL;
     double s = 0.0;
     for (int64_t j = 0; j < hidden; ++j) {
-      float acc = bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]);
-      residual_out[i * hidden + j] = orc_rne16(f32_bits(acc));
+      float acc = row_acc(xr, rr, j);
+      if (residual_out) residual_out[i * hidden + j] = orc_rne16(f32_bits(acc));
       double a = (double)acc;
       s += a * a;
     }
@@ -221,7 +240,7 @@ int orc_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, doubl
 
     float amax = 0.0f;
     for (int64_t j = 0; j < hidden; ++j) {
-      double a = (double)(bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]));
+      double a = (double)row_acc(xr, rr, j);
       double y = (a * rinv) * (double)bf16_to_f32(weight[j]);
       if (y_exact) y_exact[i * hidden + j] = y;
       amax = max_nan(amax, fabsf((float)y));
@@ -233,7 +252,7 @@ int orc_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, doubl
     for (int64_t j = 0; j < hidden; ++j) {
       int8_t code = 0;
       if (ok) {
-        double a = (double)(bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]));
+        double a = (double)row_acc(xr, rr, j);
         float y32 = (float)((a * rinv) * (double)bf16_to_f32(weight[j]));
         float t = nearbyintf(y32 * inv);
         if (t > 127.0f) t = 127.0f;

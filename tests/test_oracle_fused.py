@@ -63,8 +63,8 @@ FUSED_MUTATIONS = {
     "abs_not_square": ("s += a * a;", "s += fabs(a);"),
     "sqrt_not_rsqrt": ("1.0 / sqrt(", "sqrt("),
     "weight_shifted": ("weight[j]", "weight[(j + 1) % hidden]"),
-    "acc_from_x_only": ("double a = (double)(bf16_to_f32(xr[j]) + bf16_to_f32(rr[j]));",
-                        "double a = (double)bf16_to_f32(xr[j]);"),
+    "acc_from_x_only": ("double a = (double)row_acc(xr, rr, j);",
+                        "double a = (double)row_acc(xr, NULL, j);"),
     "out_truncated": ("orc_rne16_from_f64(y)", "orc_trunc16(f32_bits((float)y))"),
     "residual_out_truncated": ("ro[j] = rounding == ORC_RNE ? orc_rne16(ab)",
                                "ro[j] = rounding == ORC_RNE ? orc_trunc16(ab)"),
