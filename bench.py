@@ -1,5 +1,8 @@
 """Benchmark of the fused residual-add + RMSNorm forward on one MI355X.
 
+(--op selects the int8-quantised variant or plain RMSNorm instead; the
+default is the fused bf16 op.)
+
 A step is one add_rmsnorm_fwd call over the 4096 x 8192 bf16 workload
 (x, residual ~ N(0,1), weight ~ 1 + 0.1 N(0,1), eps = 1e-6), with the inputs
 already resident in HBM.  The timed region is K back-to-back steps on one
@@ -14,6 +17,7 @@ the weight once), the HBM roofline fraction against 8 TB/s, and the CPU
 oracle timed on the host as a baseline.
 
   python bench.py [--steps K] [--warmup W] [--workload 4096x8192]
+                  [--op bf16|quant|plain|plain_quant]
                   [--no-cpu-baseline] [--calibrate-copy]
 """
 from __future__ import annotations
@@ -33,14 +37,20 @@ PEAK_HBM_GBPS = 8000.0
 CACHE_DEFEAT_BYTES = 1 << 30  # rotate buffer sets until the footprint is >= 1 GiB
 
 
+OPS = ("bf16", "quant", "plain", "plain_quant")
+ENTRY = {"bf16": "add_rmsnorm_fwd", "quant": "add_rmsnorm_quant_fwd", "plain": "rmsnorm_fwd",
+         "plain_quant": "rmsnorm_quant_fwd"}
+
+
 def algorithmic_bytes(n_rows: int, hidden: int, op: str = "bf16") -> int:
     """Bytes the method must move per call: x, residual read and residual_out
     written (2 bytes each per element), out written (2 bytes per element, or
-    for the quantised variant 1 byte of code per element and a 4-byte scale
-    per row); the weight read once."""
-    if op == "quant":
-        return 7 * n_rows * hidden + 4 * n_rows + 2 * hidden
-    return 8 * n_rows * hidden + 2 * hidden
+    for the quantised variants 1 byte of code per element and a 4-byte scale
+    per row); the weight read once.  Plain RMSNorm has no residual and no
+    residual_out."""
+    per_elem = {"bf16": 8, "quant": 7, "plain": 4, "plain_quant": 3}[op]
+    per_row = 4 if op in ("quant", "plain_quant") else 0
+    return per_elem * n_rows * hidden + per_row * n_rows + 2 * hidden
 
 
 def parse_args(argv=None):
@@ -49,8 +59,9 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="4096x8192")
-    p.add_argument("--op", choices=("bf16", "quant"), default="bf16",
-                   help="bf16 out (the benchmark) or the int8-quantised variant")
+    p.add_argument("--op", choices=OPS, default="bf16",
+                   help="bf16: the fused op (the benchmark); quant: its int8-quantised "
+                        "variant; plain, plain_quant: RMSNorm without the residual add")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU oracle baseline")
@@ -89,26 +100,35 @@ def run_copy_calibration(torch, nbytes=1 << 30, reps=20):
     print(json.dumps({"calibration_copy_bytes": nbytes, "reps": reps}))
 
 
-def copy_ceiling(torch, arn, bufs, steps, n_rows, hidden):
+def copy_ceiling(torch, arn, bufs, steps, n_rows, hidden, plain=False):
     """The same bytes moved by the library's reference copy (x -> one output
     buffer, residual -> the other; 16-byte nontemporal loads and stores, no
     arithmetic), rotated like the kernel's buffers: the streaming rate this
-    device gives the fused kernel's read/write mix."""
+    device gives the kernel's 50/50 read/write mix.  For plain RMSNorm the
+    copy moves x alone (its two halves), the bytes that op moves."""
     sets = len(bufs)
-    for i in range(min(steps, 20)):
+    half = n_rows * hidden // 2
+
+    def one(i):
         o, ro, xd, rd = bufs[i % sets]
-        arn.add_rmsnorm_test_copy2(ro, o, xd, rd)
+        if plain:
+            ov, xv = o.view(-1), xd.view(-1)
+            arn.add_rmsnorm_test_copy2(ov[:half], ov[half:], xv[:half], xv[half:])
+        else:
+            arn.add_rmsnorm_test_copy2(ro, o, xd, rd)
+
+    for i in range(min(steps, 20)):
+        one(i)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        o, ro, xd, rd = bufs[i % sets]
-        arn.add_rmsnorm_test_copy2(ro, o, xd, rd)
+        one(i)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    return 8 * n_rows * hidden / (ms * 1e-3) / 1e9
+    return (4 if plain else 8) * n_rows * hidden / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s, op="bf16"):
@@ -122,6 +142,10 @@ def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s, op="bf16"):
     while True:
         if op == "quant":
             oracle.add_rmsnorm_quant(x, r, w, eps)
+        elif op == "plain":
+            oracle.rmsnorm(x, w, eps)
+        elif op == "plain_quant":
+            oracle.rmsnorm_quant(x, w, eps)
         else:
             oracle.add_rmsnorm(x, r, w, eps)
         passes += 1
@@ -164,7 +188,9 @@ def main(argv=None):
     eps = 1e-6
     x, r, w = synth.workload(cfg["seed"], n_rows, hidden)
     tensor_bytes = n_rows * hidden * 2
-    sets = max(1, -(-CACHE_DEFEAT_BYTES // (4 * tensor_bytes)))
+    plain = args.op in ("plain", "plain_quant")
+    touched = (2 if plain else 4) * tensor_bytes   # bf16 tensors one step reads or writes
+    sets = max(1, -(-CACHE_DEFEAT_BYTES // touched))
     xd0 = torch.from_numpy(x.view(np.int16)).to(dev)
     rd0 = torch.from_numpy(r.view(np.int16)).to(dev)
     wd = torch.from_numpy(w.view(np.int16)).to(dev)
@@ -174,7 +200,7 @@ def main(argv=None):
         rd = rd0 if i == 0 else rd0.clone()
         bufs.append((torch.empty_like(xd), torch.empty_like(xd), xd, rd))
     qbufs = []
-    if args.op == "quant":
+    if args.op in ("quant", "plain_quant"):
         for i in range(sets):
             qbufs.append((torch.empty(n_rows, hidden, dtype=torch.int8, device=dev),
                           torch.empty(n_rows, dtype=torch.float32, device=dev)))
@@ -185,6 +211,11 @@ def main(argv=None):
         if args.op == "quant":
             q, sc = qbufs[i % sets]
             arn.add_rmsnorm_quant_fwd(q, sc, ro, xd, rd, wd, eps)
+        elif args.op == "plain":
+            arn.rmsnorm_fwd(o, xd, wd, eps)
+        elif args.op == "plain_quant":
+            q, sc = qbufs[i % sets]
+            arn.rmsnorm_quant_fwd(q, sc, xd, wd, eps)
         else:
             arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, eps)
 
@@ -208,20 +239,22 @@ def main(argv=None):
     nbytes = algorithmic_bytes(n_rows, hidden, args.op)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
-    copy_gbps = copy_ceiling(torch, arn, bufs, min(args.steps, 500), n_rows, hidden)
+    copy_gbps = copy_ceiling(torch, arn, bufs, min(args.steps, 500), n_rows, hidden, plain)
 
     path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"
     digest = hip_build.source_digest()
-    tag = path if args.op == "bf16" else path + "_quant"
+    tag = path if args.op == "bf16" else path + "_" + args.op
     traffic = traffic_from_profiles(tag, args.workload, digest)
     roofline = {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                 "traffic": traffic}
 
     line = {
-        "metric": "fused add+RMSNorm HBM GB/s and % of peak, n=4096 x hidden=8192 bf16"
-                  if args.op == "bf16" else
-                  "fused add+RMSNorm, int8-quantised out, HBM GB/s and % of peak",
+        "metric": {"bf16": "fused add+RMSNorm HBM GB/s and % of peak, n=4096 x hidden=8192 bf16",
+                   "quant": "fused add+RMSNorm, int8-quantised out, HBM GB/s and % of peak",
+                   "plain": "RMSNorm (no residual add), HBM GB/s and % of peak",
+                   "plain_quant": "RMSNorm (no residual add), int8-quantised out, HBM GB/s "
+                                  "and % of peak"}[args.op],
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -235,15 +268,14 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": "%s rows=%d hidden=%d bf16, eps=1e-6, "
                                "x,residual~N(0,1), weight~1+0.1N(0,1)"
-                               % ("add_rmsnorm_fwd" if args.op == "bf16" else "add_rmsnorm_quant_fwd",
-                                  n_rows, hidden),
+                               % (ENTRY[args.op], n_rows, hidden),
                    "n_rows": n_rows, "hidden": hidden, "kernel": path,
                    "buffer_sets": sets, "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                    "wall_s_timed_region": round(wall_s, 4)},
         "roofline": roofline,
         "copy_ceiling": {"gbps": round(copy_gbps, 2),
-                         "kernel_frac_of_copy": round(gbps / copy_gbps, 4) if args.op == "bf16"
-                         else None,
+                         "kernel_frac_of_copy": round(gbps / copy_gbps, 4)
+                         if args.op in ("bf16", "plain") else None,
                          "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
                          "what": "add_rmsnorm_test_copy2 over the same bytes: two 16-byte "
                                  "nontemporal streaming copies, no arithmetic, same buffer rotation"},

@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -47,7 +47,8 @@ class LaunchCfg(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_quant_fwd",
-           "add_rmsnorm_quant_fwd_cfg", "add_rmsnorm_test_cvt_range",
+           "add_rmsnorm_quant_fwd_cfg", "rmsnorm_fwd", "rmsnorm_fwd_cfg", "rmsnorm_quant_fwd",
+           "rmsnorm_quant_fwd_cfg", "add_rmsnorm_test_cvt_range",
            "add_rmsnorm_test_copy2", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
            "add_rmsnorm_abi_version", "add_rmsnorm_build_info")
 
@@ -73,6 +74,15 @@ def lib() -> ctypes.CDLL:
     L.add_rmsnorm_quant_fwd_cfg.restype = i32
     L.add_rmsnorm_quant_fwd_cfg.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32,
                                             ctypes.POINTER(LaunchCfg), vp]
+    L.rmsnorm_fwd.restype = i32
+    L.rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, vp]
+    L.rmsnorm_fwd_cfg.restype = i32
+    L.rmsnorm_fwd_cfg.argtypes = [vp, vp, vp, i64, i64, f32, ctypes.POINTER(LaunchCfg), vp]
+    L.rmsnorm_quant_fwd.restype = i32
+    L.rmsnorm_quant_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
+    L.rmsnorm_quant_fwd_cfg.restype = i32
+    L.rmsnorm_quant_fwd_cfg.argtypes = [vp, vp, vp, vp, i64, i64, f32,
+                                        ctypes.POINTER(LaunchCfg), vp]
     L.add_rmsnorm_test_cvt_range.restype = i32
     L.add_rmsnorm_test_cvt_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
     L.add_rmsnorm_test_copy2.restype = i32
@@ -247,6 +257,51 @@ def add_rmsnorm_quant_fwd_cfg(out_q, out_scale, residual_out, x, residual, weigh
     _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
         residual.data_ptr(), weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg), h)))
+
+
+def rmsnorm_fwd(out, x, weight, eps: float = 1e-6, stream=None) -> None:
+    """out <- RMSNorm of x with weight (no residual add); out may be x.
+    Tensors and stream as add_rmsnorm_fwd."""
+    n_rows, hidden, dev = _marshal(out, out, x, x, weight)
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.rmsnorm_fwd(
+        out.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden, eps, h)))
+
+
+def rmsnorm_fwd_cfg(out, x, weight, eps: float = 1e-6, path: int = PATH_AUTO,
+                    block_threads: int = 0, grid_blocks: int = 0, stream=None) -> None:
+    """rmsnorm_fwd with an explicit launch configuration (same results)."""
+    n_rows, hidden, dev = _marshal(out, out, x, x, weight)
+    L = lib()
+    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.rmsnorm_fwd_cfg(
+        out.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden, eps,
+        ctypes.byref(cfg), h)))
+
+
+def rmsnorm_quant_fwd(out_q, out_scale, x, weight, eps: float = 1e-6, stream=None) -> None:
+    """out_q (int8 codes), out_scale (fp32 per row) <- quantised RMSNorm of x
+    (no residual add).  Shapes as add_rmsnorm_quant_fwd."""
+    n_rows, hidden, dev = _marshal_quant(out_q, out_scale, x, x, x, weight)
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.rmsnorm_quant_fwd(
+        out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
+        eps, h)))
+
+
+def rmsnorm_quant_fwd_cfg(out_q, out_scale, x, weight, eps: float = 1e-6, path: int = PATH_AUTO,
+                          block_threads: int = 0, grid_blocks: int = 0, stream=None) -> None:
+    """rmsnorm_quant_fwd with an explicit launch configuration."""
+    n_rows, hidden, dev = _marshal_quant(out_q, out_scale, x, x, x, weight)
+    L = lib()
+    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.rmsnorm_quant_fwd_cfg(
+        out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
+        eps, ctypes.byref(cfg), h)))
 
 
 def add_rmsnorm_test_cvt_range(out, start: int, stream=None) -> None:

@@ -1,4 +1,5 @@
-// C entry points of the fused residual-add + RMSNorm forward: argument
+// C entry points of the fused residual-add + RMSNorm forward and of plain
+// RMSNorm (bf16 or int8 out): argument
 // validation (on the host, before anything is enqueued), kernel choice by
 // hidden size, launch on the caller's stream.  The contract is documented in
 // include/add_rmsnorm.h.
@@ -207,6 +208,65 @@ int add_rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, uint16_t* residual_ou
                           struct ihipStream_t* stream) {
   return add_rmsnorm_quant_fwd_cfg(out_q, out_scale, residual_out, x, residual, weight, n_rows,
                                    hidden, eps, nullptr, stream);
+}
+
+int rmsnorm_fwd_cfg(uint16_t* out, const uint16_t* x, const uint16_t* weight, int64_t n_rows,
+                    int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                    struct ihipStream_t* stream) {
+  add_rmsnorm_launch_cfg c;
+  int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
+  if (rc != ADD_RMSNORM_OK) return rc;
+  if (n_rows == 0) return ADD_RMSNORM_OK;
+
+  if (!out || !x || !weight) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(out) || !aligned16(x) || !aligned16(weight)) return ADD_RMSNORM_EALIGN;
+  const uint64_t row_bytes = (uint64_t)hidden * 2;
+  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
+  const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
+  // out is disjoint from the weight, and disjoint from x or exactly x.
+  if (output_aliases_badly(out, t_bytes, x, x, weight, row_bytes)) return ADD_RMSNORM_EALIAS;
+
+  const addrms::FwdArgs a = {out, nullptr, nullptr, nullptr, x, nullptr, weight,
+                             n_rows, (int32_t)hidden, eps};
+  return dispatch(a, c, stream);
+}
+
+int rmsnorm_fwd(uint16_t* out, const uint16_t* x, const uint16_t* weight, int64_t n_rows,
+                int64_t hidden, float eps, struct ihipStream_t* stream) {
+  return rmsnorm_fwd_cfg(out, x, weight, n_rows, hidden, eps, nullptr, stream);
+}
+
+int rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, const uint16_t* x,
+                          const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                          const struct add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream) {
+  add_rmsnorm_launch_cfg c;
+  int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
+  if (rc != ADD_RMSNORM_OK) return rc;
+  if (n_rows == 0) return ADD_RMSNORM_OK;
+
+  if (!out_q || !out_scale || !x || !weight) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(out_q) || !aligned(out_scale, 4) || !aligned16(x) || !aligned16(weight))
+    return ADD_RMSNORM_EALIGN;
+  const uint64_t row_bytes = (uint64_t)hidden * 2;
+  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
+  const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
+  const uint64_t q_bytes = (uint64_t)n_rows * (uint64_t)hidden;
+  const uint64_t s_bytes = (uint64_t)n_rows * 4;
+  // Codes and scales overlap nothing.
+  if (overlap(out_q, q_bytes, out_scale, s_bytes) || overlap(out_q, q_bytes, x, t_bytes) ||
+      overlap(out_q, q_bytes, weight, row_bytes) || overlap(out_scale, s_bytes, x, t_bytes) ||
+      overlap(out_scale, s_bytes, weight, row_bytes))
+    return ADD_RMSNORM_EALIAS;
+
+  const addrms::FwdArgs a = {nullptr, out_q, out_scale, nullptr, x, nullptr, weight,
+                             n_rows, (int32_t)hidden, eps};
+  return dispatch(a, c, stream);
+}
+
+int rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, const uint16_t* x, const uint16_t* weight,
+                      int64_t n_rows, int64_t hidden, float eps, struct ihipStream_t* stream) {
+  return rmsnorm_quant_fwd_cfg(out_q, out_scale, x, weight, n_rows, hidden, eps, nullptr,
+                               stream);
 }
 
 int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,

@@ -36,6 +36,9 @@
 //     [-127, 127].  The inverse must be finite, so a row is quantised only
 //     when 2^-120 <= amax <= FLT_MAX; other rows (amax 0, tiny, Inf or NaN)
 //     get all-zero codes, and their scale is still amax / 127.
+//   * Plain variant (template flag R false): RMSNorm without the residual
+//     add.  acc = x exactly (no add at all: adding a zero would turn -0 into
+//     +0), and there is no residual_out; everything after acc is the same.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -238,13 +241,19 @@ DEV u32x2 quant8(const float (&y)[8], float inv) {
   return u32x2{w0, w1};
 }
 
-// acc = x + r for one segment, without the sum of squares.
+// acc = x + r for one segment (acc = x in the plain variant), without the
+// sum of squares.
+template <bool R>
 DEV void add8(u32x4 xq, u32x4 rq, float (&acc)[8]) {
-  float xa[8], ra[8];
-  unpack8(xq, xa);
-  unpack8(rq, ra);
+  if constexpr (R) {
+    float xa[8], ra[8];
+    unpack8(xq, xa);
+    unpack8(rq, ra);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = xa[k] + ra[k];
+    for (int k = 0; k < 8; ++k) acc[k] = xa[k] + ra[k];
+  } else {
+    unpack8(xq, acc);
+  }
 }
 
 // Hides a value from the optimiser.  The wavefront-per-row kernel keeps x and
@@ -258,13 +267,11 @@ DEV T opaque(T v) {
   return v;
 }
 
-// acc = x + r for one segment; returns its sum of squares.
+// acc = x + r for one segment (acc = x in the plain variant); returns its
+// sum of squares.
+template <bool R>
 DEV float add_segment(u32x4 xq, u32x4 rq, float (&acc)[8]) {
-  float xa[8], ra[8];
-  unpack8(xq, xa);
-  unpack8(rq, ra);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = xa[k] + ra[k];
+  add8<R>(xq, rq, acc);
   return seg_sumsq(acc);
 }
 
@@ -277,7 +284,7 @@ DEV float add_segment(u32x4 xq, u32x4 rq, float (&acc)[8]) {
 // per-lane register footprint small enough for more rows in flight per CU.
 // Rows are read and written through per-row buffer resources: segments past
 // the row read as zero and their stores are dropped, so nothing branches.
-template <int WAVES, int J, bool Q>
+template <int WAVES, int J, bool Q, bool R>
 __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
   __shared__ u32x4 wl[64 * J];
   const int lane = threadIdx.x & 63;
@@ -292,21 +299,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
   const int64_t stride = (int64_t)gridDim.x * WAVES;
   for (int64_t row = (int64_t)blockIdx.x * WAVES + wave; row < p.n_rows; row += stride) {
     const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, C, true);
-    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, C, true);
-    const __amdgpu_buffer_rsrc_t ro = row_rsrc(p.residual_out, row, C, true);
-    const __amdgpu_buffer_rsrc_t oo = row_rsrc(p.out, row, C, true);
+    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, C, R);
+    const __amdgpu_buffer_rsrc_t ro = row_rsrc(p.residual_out, row, C, R);
+    const __amdgpu_buffer_rsrc_t oo = row_rsrc(p.out, row, C, !Q);
     u32x4 xq[J], rq[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       xq[j] = load_seg(rx, lane + 64 * j);
-      rq[j] = load_seg(rr, lane + 64 * j);
+      rq[j] = R ? load_seg(rr, lane + 64 * j) : u32x4{0, 0, 0, 0};
     }
     float blk[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       float acc[8];
-      blk[j] = add_segment(xq[j], rq[j], acc);
-      store_seg(ro, lane + 64 * j, pack8_rne(acc));
+      blk[j] = add_segment<R>(xq[j], rq[j], acc);
+      if constexpr (R) store_seg(ro, lane + 64 * j, pack8_rne(acc));
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) blk[j] = wave_block_sum(blk[j]);
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         float acc[8];
-        add8(opaque(xq[j]), opaque(rq[j]), acc);
+        add8<R>(opaque(xq[j]), opaque(rq[j]), acc);
         store_seg(oo, lane + 64 * j, normalise8(acc, rinv, wl[opaque(lane + 64 * j)]));
       }
     } else {
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         float acc[8], y[8];
-        add8(opaque(xq[j]), opaque(rq[j]), acc);
+        add8<R>(opaque(xq[j]), opaque(rq[j]), acc);
         scale8(acc, rinv, wl[opaque(lane + 64 * j)], y);
         if (lane + 64 * j < C) m = max_abs8(m, y);
       }
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         float acc[8], y[8];
-        add8(opaque(xq[j]), opaque(rq[j]), acc);
+        add8<R>(opaque(xq[j]), opaque(rq[j]), acc);
         scale8(acc, rinv, wl[opaque(lane + 64 * j)], y);
         store_codes(qo, lane + 64 * j, ok ? quant8(y, inv) : u32x2{0, 0});
       }
@@ -351,7 +358,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 // B threads per row; thread t holds segments t, t + B, ..., t + B (J - 1).
 // For each j, wave w's butterfly yields the sum of block w + j * (B / 64);
 // the B / 64 * J block sums meet in LDS and every thread finishes the tree.
-template <int B, int J, bool Q>
+template <int B, int J, bool Q, bool R>
 __global__ __launch_bounds__(B) void k_wg_row(Params p) {
   constexpr int W = B / 64;
   constexpr int NB = W * J;
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
       const int s = t + B * j;
       if (s < C) {
         xq[j] = load_stream(p.x + base + s);
-        rq[j] = load_stream(p.residual + base + s);
+        rq[j] = R ? load_stream(p.residual + base + s) : u32x4{0, 0, 0, 0};
       } else {
         xq[j] = u32x4{0, 0, 0, 0};
         rq[j] = u32x4{0, 0, 0, 0};
@@ -389,8 +396,8 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int s = t + B * j;
-      bs[j] = add_segment(xq[j], rq[j], acc[j]);
-      if (s < C) store_stream(p.residual_out + base + s, pack8_rne(acc[j]));
+      bs[j] = add_segment<R>(xq[j], rq[j], acc[j]);
+      if (R && s < C) store_stream(p.residual_out + base + s, pack8_rne(acc[j]));
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) bs[j] = wave_block_sum(bs[j]);
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
 // each wavefront keeps U chunks of x and residual in flight.  Loads go
 // through a per-row buffer resource: segments past the row read as zero,
 // without a branch.
-template <int B, int NB, int U, bool Q>
+template <int B, int NB, int U, bool Q, bool R>
 __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
   constexpr int W = B / 64;
   __shared__ float blk[NB];
@@ -464,7 +471,7 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
     const size_t base = (size_t)row * (size_t)C;
     const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, C, true);
-    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, C, true);
+    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, C, R);
     // Blocks past the row's last chunk are +0.
     for (int i = chunks * W + t; i < NB; i += B) blk[i] = 0.0f;
     for (int c0 = 0; c0 < chunks; c0 += U) {
@@ -472,7 +479,7 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         xq[u] = load_seg(rx, (c0 + u) * B + t);
-        rq[u] = load_seg(rr, (c0 + u) * B + t);
+        rq[u] = R ? load_seg(rr, (c0 + u) * B + t) : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -480,9 +487,9 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
         if (c >= chunks) break;  // uniform across the workgroup
         const int s = c * B + t;
         float acc[8];
-        float bs = add_segment(xq[u], rq[u], acc);
+        float bs = add_segment<R>(xq[u], rq[u], acc);
         if (s < C) {
-          store_stream(p.residual_out + base + s, pack8_rne(acc));
+          if constexpr (R) store_stream(p.residual_out + base + s, pack8_rne(acc));
           lo[s] = make_float4(acc[0], acc[1], acc[2], acc[3]);
           hi[s] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
@@ -634,76 +641,79 @@ hipError_t launch(K kernel, int block_threads, size_t lds, int64_t grid_blocks,
 // Combinations that would not fit the register file (segments held per thread
 // times threads per workgroup) are not built; wave_row_supported() and
 // wg_row_supported() say which exist.
-template <bool Q, int WAVES>
+template <bool Q, bool R, int WAVES>
 hipError_t go_wave(const Params& p, int j, int64_t grid, hipStream_t s) {
   const int64_t groups = (p.n_rows + WAVES - 1) / WAVES;
   switch (j) {
-    case 1: return launch(k_wave_row<WAVES, 1, Q>, WAVES * 64, 0, grid, groups, p, s);
-    case 2: return launch(k_wave_row<WAVES, 2, Q>, WAVES * 64, 0, grid, groups, p, s);
-    case 4: return launch(k_wave_row<WAVES, 4, Q>, WAVES * 64, 0, grid, groups, p, s);
+    case 1: return launch(k_wave_row<WAVES, 1, Q, R>, WAVES * 64, 0, grid, groups, p, s);
+    case 2: return launch(k_wave_row<WAVES, 2, Q, R>, WAVES * 64, 0, grid, groups, p, s);
+    case 4: return launch(k_wave_row<WAVES, 4, Q, R>, WAVES * 64, 0, grid, groups, p, s);
     case 8:
       if constexpr (WAVES < 16)
-        return launch(k_wave_row<WAVES, 8, Q>, WAVES * 64, 0, grid, groups, p, s);
+        return launch(k_wave_row<WAVES, 8, Q, R>, WAVES * 64, 0, grid, groups, p, s);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template <bool Q, int B>
+template <bool Q, bool R, int B>
 hipError_t go_wg(const Params& p, int j, int64_t grid, hipStream_t s) {
   switch (j) {
-    case 1: return launch(k_wg_row<B, 1, Q>, B, 0, grid, p.n_rows, p, s);
-    case 2: return launch(k_wg_row<B, 2, Q>, B, 0, grid, p.n_rows, p, s);
+    case 1: return launch(k_wg_row<B, 1, Q, R>, B, 0, grid, p.n_rows, p, s);
+    case 2: return launch(k_wg_row<B, 2, Q, R>, B, 0, grid, p.n_rows, p, s);
     case 4:
-      if constexpr (B * 4 <= 2048) return launch(k_wg_row<B, 4, Q>, B, 0, grid, p.n_rows, p, s);
+      if constexpr (B * 4 <= 2048)
+        return launch(k_wg_row<B, 4, Q, R>, B, 0, grid, p.n_rows, p, s);
       break;
     case 8:
-      if constexpr (B * 8 <= 2048) return launch(k_wg_row<B, 8, Q>, B, 0, grid, p.n_rows, p, s);
+      if constexpr (B * 8 <= 2048)
+        return launch(k_wg_row<B, 8, Q, R>, B, 0, grid, p.n_rows, p, s);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template <bool Q, int B>
+template <bool Q, bool R, int B>
 hipError_t go_two_pass(const Params& p, int hidden, int64_t grid, hipStream_t s) {
   const size_t lds = (size_t)p.segs * 32;
   if (two_pass_nb(hidden) == 32)
-    return launch(k_lds_two_pass<B, 32, two_pass_batch<B>(), Q>, B, lds, grid, p.n_rows, p, s);
-  return launch(k_lds_two_pass<B, 64, two_pass_batch<B>(), Q>, B, lds, grid, p.n_rows, p, s);
+    return launch(k_lds_two_pass<B, 32, two_pass_batch<B>(), Q, R>, B, lds, grid, p.n_rows, p,
+                  s);
+  return launch(k_lds_two_pass<B, 64, two_pass_batch<B>(), Q, R>, B, lds, grid, p.n_rows, p, s);
 }
 
-template <bool Q>
+template <bool Q, bool R>
 hipError_t wave_by_block(const Params& p, int b, int j, int64_t grid, hipStream_t s) {
   switch (b) {
-    case 64: return go_wave<Q, 1>(p, j, grid, s);
-    case 128: return go_wave<Q, 2>(p, j, grid, s);
-    case 256: return go_wave<Q, 4>(p, j, grid, s);
-    case 512: return go_wave<Q, 8>(p, j, grid, s);
-    case 1024: return go_wave<Q, 16>(p, j, grid, s);
+    case 64: return go_wave<Q, R, 1>(p, j, grid, s);
+    case 128: return go_wave<Q, R, 2>(p, j, grid, s);
+    case 256: return go_wave<Q, R, 4>(p, j, grid, s);
+    case 512: return go_wave<Q, R, 8>(p, j, grid, s);
+    case 1024: return go_wave<Q, R, 16>(p, j, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <bool Q>
+template <bool Q, bool R>
 hipError_t wg_by_block(const Params& p, int b, int j, int64_t grid, hipStream_t s) {
   switch (b) {
-    case 64: return go_wg<Q, 64>(p, j, grid, s);
-    case 128: return go_wg<Q, 128>(p, j, grid, s);
-    case 256: return go_wg<Q, 256>(p, j, grid, s);
-    case 512: return go_wg<Q, 512>(p, j, grid, s);
-    case 1024: return go_wg<Q, 1024>(p, j, grid, s);
+    case 64: return go_wg<Q, R, 64>(p, j, grid, s);
+    case 128: return go_wg<Q, R, 128>(p, j, grid, s);
+    case 256: return go_wg<Q, R, 256>(p, j, grid, s);
+    case 512: return go_wg<Q, R, 512>(p, j, grid, s);
+    case 1024: return go_wg<Q, R, 1024>(p, j, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <bool Q>
+template <bool Q, bool R>
 hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, hipStream_t s) {
   switch (b) {
-    case 64: return go_two_pass<Q, 64>(p, hidden, grid, s);
-    case 128: return go_two_pass<Q, 128>(p, hidden, grid, s);
-    case 256: return go_two_pass<Q, 256>(p, hidden, grid, s);
-    case 512: return go_two_pass<Q, 512>(p, hidden, grid, s);
-    case 1024: return go_two_pass<Q, 1024>(p, hidden, grid, s);
+    case 64: return go_two_pass<Q, R, 64>(p, hidden, grid, s);
+    case 128: return go_two_pass<Q, R, 128>(p, hidden, grid, s);
+    case 256: return go_two_pass<Q, R, 256>(p, hidden, grid, s);
+    case 512: return go_two_pass<Q, R, 512>(p, hidden, grid, s);
+    case 1024: return go_two_pass<Q, R, 1024>(p, hidden, grid, s);
   }
   return hipErrorInvalidValue;
 }
@@ -712,25 +722,39 @@ hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, h
 
 // ---------------------------------------------------------------- internal API
 
+// The variant is chosen by which outputs and inputs are set: quantised when
+// codes are requested, plain when there is no residual.
 hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
                            int64_t grid_blocks, hipStream_t s) {
   const Params p = make_params(a);
-  return a.qout ? wave_by_block<true>(p, block_threads, segs_per_lane, grid_blocks, s)
-                : wave_by_block<false>(p, block_threads, segs_per_lane, grid_blocks, s);
+  const int b = block_threads, j = segs_per_lane;
+  if (a.qout)
+    return a.residual ? wave_by_block<true, true>(p, b, j, grid_blocks, s)
+                      : wave_by_block<true, false>(p, b, j, grid_blocks, s);
+  return a.residual ? wave_by_block<false, true>(p, b, j, grid_blocks, s)
+                    : wave_by_block<false, false>(p, b, j, grid_blocks, s);
 }
 
 hipError_t launch_wg_row(const FwdArgs& a, int block_threads, int segs_per_thread,
                          int64_t grid_blocks, hipStream_t s) {
   const Params p = make_params(a);
-  return a.qout ? wg_by_block<true>(p, block_threads, segs_per_thread, grid_blocks, s)
-                : wg_by_block<false>(p, block_threads, segs_per_thread, grid_blocks, s);
+  const int b = block_threads, j = segs_per_thread;
+  if (a.qout)
+    return a.residual ? wg_by_block<true, true>(p, b, j, grid_blocks, s)
+                      : wg_by_block<true, false>(p, b, j, grid_blocks, s);
+  return a.residual ? wg_by_block<false, true>(p, b, j, grid_blocks, s)
+                    : wg_by_block<false, false>(p, b, j, grid_blocks, s);
 }
 
 hipError_t launch_lds_two_pass(const FwdArgs& a, int block_threads, int64_t grid_blocks,
                                hipStream_t s) {
   const Params p = make_params(a);
-  return a.qout ? two_pass_by_block<true>(p, block_threads, a.hidden, grid_blocks, s)
-                : two_pass_by_block<false>(p, block_threads, a.hidden, grid_blocks, s);
+  const int b = block_threads, h = a.hidden;
+  if (a.qout)
+    return a.residual ? two_pass_by_block<true, true>(p, b, h, grid_blocks, s)
+                      : two_pass_by_block<true, false>(p, b, h, grid_blocks, s);
+  return a.residual ? two_pass_by_block<false, true>(p, b, h, grid_blocks, s)
+                    : two_pass_by_block<false, false>(p, b, h, grid_blocks, s);
 }
 
 bool wave_row_supported(int block_threads, int segs_per_lane) {

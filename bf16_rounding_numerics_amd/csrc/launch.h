@@ -11,9 +11,9 @@ struct FwdArgs {
   uint16_t* out;           // bf16 out, or null for the quantised variant
   int8_t* qout;            // int8 codes (quantised variant), else null
   float* qscale;           // per-row scale (quantised variant), else null
-  uint16_t* residual_out;
+  uint16_t* residual_out;  // null for plain RMSNorm
   const uint16_t* x;
-  const uint16_t* residual;
+  const uint16_t* residual;  // null for plain RMSNorm (acc = x, no residual_out)
   const uint16_t* weight;
   int64_t n_rows;
   int32_t hidden;  // multiple of 8
@@ -27,7 +27,8 @@ constexpr int kMaxSegments = 32768 / 8;
 // segments are spread over the 64 lanes, segs_per_lane (1, 2, 4 or 8) each.
 // grid_blocks > 0 launches that many workgroups, which loop over the rows;
 // -1 launches as many as fit on the device at once; 0 one per row group.
-// The quantised variant runs when FwdArgs::qout is set.
+// The quantised variant runs when FwdArgs::qout is set, plain RMSNorm when
+// FwdArgs::residual is null.
 hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
                            int64_t grid_blocks, hipStream_t stream);
 

@@ -48,7 +48,7 @@ extern "C" {
 /* hipStream_t is a pointer to this opaque struct. */
 struct ihipStream_t;
 
-#define ADD_RMSNORM_ABI_VERSION 1
+#define ADD_RMSNORM_ABI_VERSION 2
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768
@@ -152,6 +152,43 @@ int add_rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, uint16_t* residua
                               const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
                               const struct add_rmsnorm_launch_cfg* cfg,
                               struct ihipStream_t* stream);
+
+/*
+ * Plain RMSNorm: the row computation above without the residual add, for the
+ * other norms with bf16 stores that the aiter issue's "Notes" list beside the
+ * fused kernel (the q/k norms, the norm kernel used above hidden 8192).  Per
+ * row: acc_j = fp32(x[i,j]) exactly (no addition, so -0 stays -0), then S,
+ * rinv and out as in add_rmsnorm_fwd, with the same fixed reduction tree and
+ * round-to-nearest-even store.  The result is bit for bit add_rmsnorm_fwd's
+ * out with a residual of all -0 (x + -0 = x in IEEE arithmetic).
+ *   out     [n_rows, hidden] bf16, written; may be x itself (in place), any
+ *           other overlap with x or the weight is ADD_RMSNORM_EALIAS.
+ *   x       [n_rows, hidden] bf16, read.  weight [hidden] bf16, read.
+ * Sizes, alignment, eps, errors, kernel choice and stream as add_rmsnorm_fwd.
+ */
+int rmsnorm_fwd(uint16_t* out, const uint16_t* x, const uint16_t* weight, int64_t n_rows,
+                int64_t hidden, float eps, struct ihipStream_t* stream);
+
+/* rmsnorm_fwd with an explicit launch configuration (same results). */
+int rmsnorm_fwd_cfg(uint16_t* out, const uint16_t* x, const uint16_t* weight, int64_t n_rows,
+                    int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                    struct ihipStream_t* stream);
+
+/*
+ * Plain RMSNorm with int8 out: rmsnorm_fwd's row computation followed by the
+ * per-row quantisation of add_rmsnorm_quant_fwd (same scale, inverse scale,
+ * rounding and zero-code rule).  Codes and scales must not overlap x, the
+ * weight or each other (ADD_RMSNORM_EALIAS).
+ *   out_q      [n_rows, hidden] int8, written, 16-byte aligned.
+ *   out_scale  [n_rows] fp32, written, 4-byte aligned.
+ */
+int rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, const uint16_t* x, const uint16_t* weight,
+                      int64_t n_rows, int64_t hidden, float eps, struct ihipStream_t* stream);
+
+/* rmsnorm_quant_fwd with an explicit launch configuration (same results). */
+int rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, const uint16_t* x,
+                          const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                          const struct add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream);
 
 /*
  * Test hook for the store epilogue: out[i] = bf16_rne of the fp32 whose bit

@@ -47,36 +47,42 @@ def lib():
     return _lib
 
 
+def _ptr(a):
+    return a.ctypes.data if a is not None else None
+
+
 def add_rmsnorm(x, residual, weight, eps=1e-6, want_sumsq=False):
-    """(out, residual_out[, sum of squares per row]) of the fp32 model."""
+    """(out, residual_out[, sum of squares per row]) of the fp32 model.
+    residual None is plain RMSNorm; residual_out is then None."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
-    residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    if residual is not None:
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
     weight = np.ascontiguousarray(weight, dtype=np.uint16)
     n, h = x.shape
     out = np.empty_like(x)
-    res = np.empty_like(x)
+    res = np.empty_like(x) if residual is not None else None
     ss = np.empty(n, dtype=np.float32) if want_sumsq else None
-    rc = lib().model_add_rmsnorm(out.ctypes.data, res.ctypes.data,
-                                 ss.ctypes.data if ss is not None else None, x.ctypes.data,
-                                 residual.ctypes.data, weight.ctypes.data, n, h,
-                                 ctypes.c_float(eps))
+    rc = lib().model_add_rmsnorm(out.ctypes.data, _ptr(res), _ptr(ss), x.ctypes.data,
+                                 _ptr(residual), weight.ctypes.data, n, h, ctypes.c_float(eps))
     if rc != 0:
         raise ValueError("fp32 model rejected its arguments")
     return (out, res, ss) if want_sumsq else (out, res)
 
 
 def add_rmsnorm_quant(x, residual, weight, eps=1e-6):
-    """(codes int8, scale fp32 per row, residual_out) of the fp32 model."""
+    """(codes int8, scale fp32 per row, residual_out) of the fp32 model.
+    residual None is plain RMSNorm; residual_out is then None."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
-    residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    if residual is not None:
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
     weight = np.ascontiguousarray(weight, dtype=np.uint16)
     n, h = x.shape
     q = np.empty(x.shape, dtype=np.int8)
     sc = np.empty(n, dtype=np.float32)
-    res = np.empty_like(x)
-    rc = lib().model_add_rmsnorm_quant(q.ctypes.data, sc.ctypes.data, res.ctypes.data,
-                                       x.ctypes.data, residual.ctypes.data, weight.ctypes.data,
-                                       n, h, ctypes.c_float(eps))
+    res = np.empty_like(x) if residual is not None else None
+    rc = lib().model_add_rmsnorm_quant(q.ctypes.data, sc.ctypes.data, _ptr(res), x.ctypes.data,
+                                       _ptr(residual), weight.ctypes.data, n, h,
+                                       ctypes.c_float(eps))
     if rc != 0:
         raise ValueError("fp32 model rejected its arguments")
     return q, sc, res

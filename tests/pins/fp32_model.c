@@ -11,6 +11,7 @@
  *                padded with +0 to a power of two
  *   rinv       = 1 / sqrtf(S / hidden + eps)     (correctly rounded / and sqrt)
  *   out_j      = bf16_rne((acc_j * rinv) * w_j)
+ * Plain RMSNorm (r and residual_out NULL): acc_j = fp32(x_j), no addition.
  * It shares no code with the GPU library.  Plain C, gcc -O2
  * -ffp-contract=off, SSE binary32 arithmetic with the default MXCSR (no
  * flush-to-zero); fmaf from the C library (correctly rounded).
@@ -49,8 +50,9 @@ static float row_rinv(float* acc, float* seg, int64_t padded, uint16_t* ro, cons
                       const uint16_t* rr, int64_t hidden, float eps, float* sumsq) {
   const int64_t segs = hidden / 8;
   for (int64_t j = 0; j < hidden; ++j) {
-    acc[j] = f32_of((uint32_t)xr[j] << 16) + f32_of((uint32_t)rr[j] << 16);
-    ro[j] = round_bf16(acc[j]);
+    acc[j] = f32_of((uint32_t)xr[j] << 16);
+    if (rr) acc[j] = acc[j] + f32_of((uint32_t)rr[j] << 16);
+    if (ro) ro[j] = round_bf16(acc[j]);
   }
   for (int64_t s = 0; s < padded; ++s) {
     if (s >= segs) {
@@ -75,7 +77,7 @@ static float row_rinv(float* acc, float* seg, int64_t padded, uint16_t* ro, cons
 int model_add_rmsnorm(uint16_t* out, uint16_t* residual_out, float* sumsq_out,
                       const uint16_t* x, const uint16_t* r, const uint16_t* w, int64_t n_rows,
                       int64_t hidden, float eps) {
-  if (hidden <= 0 || hidden % 8) return -1;
+  if (hidden <= 0 || hidden % 8 || !r != !residual_out) return -1;
   int64_t padded = 1;
   while (padded < hidden / 8) padded *= 2;
   float* seg = (float*)malloc(sizeof(float) * (size_t)padded);
@@ -86,8 +88,9 @@ int model_add_rmsnorm(uint16_t* out, uint16_t* residual_out, float* sumsq_out,
     return -1;
   }
   for (int64_t i = 0; i < n_rows; ++i) {
-    const float rinv = row_rinv(acc, seg, padded, residual_out + i * hidden, x + i * hidden,
-                                r + i * hidden, hidden, eps, sumsq_out ? sumsq_out + i : NULL);
+    const float rinv = row_rinv(acc, seg, padded, residual_out ? residual_out + i * hidden : NULL,
+                                x + i * hidden, r ? r + i * hidden : NULL, hidden, eps,
+                                sumsq_out ? sumsq_out + i : NULL);
     for (int64_t j = 0; j < hidden; ++j) {
       const float y = (acc[j] * rinv) * f32_of((uint32_t)w[j] << 16);
       out[i * hidden + j] = round_bf16(y);
@@ -115,7 +118,7 @@ static float max_nan(float m, float v) {
 int model_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, const uint16_t* x,
                             const uint16_t* r, const uint16_t* w, int64_t n_rows, int64_t hidden,
                             float eps) {
-  if (hidden <= 0 || hidden % 8) return -1;
+  if (hidden <= 0 || hidden % 8 || !r != !residual_out) return -1;
   int64_t padded = 1;
   while (padded < hidden / 8) padded *= 2;
   float* seg = (float*)malloc(sizeof(float) * (size_t)padded);
@@ -126,8 +129,8 @@ int model_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, con
     return -1;
   }
   for (int64_t i = 0; i < n_rows; ++i) {
-    const float rinv = row_rinv(acc, seg, padded, residual_out + i * hidden, x + i * hidden,
-                                r + i * hidden, hidden, eps, NULL);
+    const float rinv = row_rinv(acc, seg, padded, residual_out ? residual_out + i * hidden : NULL,
+                                x + i * hidden, r ? r + i * hidden : NULL, hidden, eps, NULL);
     float amax = 0.0f;
     for (int64_t j = 0; j < hidden; ++j) {
       acc[j] = (acc[j] * rinv) * f32_of((uint32_t)w[j] << 16);

@@ -226,6 +226,72 @@ def test_quant_zero_rows_and_in_place_validation():
     assert qcall(res=A + 3 * MB, h=8192, cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.ERANGE
 
 
+def pcall(out=A, x=A + 2 * MB, w=A + 4 * MB, n=4, h=64, eps=1e-6, cfg=None):
+    L = arn.lib()
+    if cfg is None:
+        return L.rmsnorm_fwd(out, x, w, n, h, eps, None)
+    c = arn.LaunchCfg(*cfg)
+    return L.rmsnorm_fwd_cfg(out, x, w, n, h, eps, ctypes.byref(c), None)
+
+
+def pqcall(q=A + 5 * MB, sc=A + 6 * MB, x=A + 2 * MB, w=A + 4 * MB, n=4, h=64, eps=1e-6,
+           cfg=None):
+    L = arn.lib()
+    if cfg is None:
+        return L.rmsnorm_quant_fwd(q, sc, x, w, n, h, eps, None)
+    c = arn.LaunchCfg(*cfg)
+    return L.rmsnorm_quant_fwd_cfg(q, sc, x, w, n, h, eps, ctypes.byref(c), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), arn.EINVAL),
+    (dict(h=0), arn.EINVAL),
+    (dict(eps=-1.0), arn.EINVAL),
+    (dict(h=12), arn.EALIGN),
+    (dict(h=32776), arn.ERANGE),
+    (dict(out=0), arn.EINVAL),
+    (dict(x=0), arn.EINVAL),
+    (dict(w=0), arn.EINVAL),
+    (dict(out=A + 8), arn.EALIGN),
+    (dict(out=A + 2 * MB + 16), arn.EALIAS),            # out partly overlaps x
+    (dict(out=A + 4 * MB - 16), arn.EALIAS),            # out's tail on the weight
+    (dict(n=1 << 62, h=8), arn.ERANGE),
+    (dict(cfg=(0, 0, 0, 1)), arn.EINVAL),
+    (dict(cfg=(arn.PATH_WAVE_ROW, 0, 0, 0), h=8192), arn.ERANGE),
+])
+@fake_addresses
+def test_plain_argument_errors(kw, status):
+    assert pcall(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), arn.EINVAL),
+    (dict(h=12), arn.EALIGN),
+    (dict(q=0), arn.EINVAL),
+    (dict(sc=0), arn.EINVAL),
+    (dict(x=0), arn.EINVAL),
+    (dict(q=A + 5 * MB + 8), arn.EALIGN),
+    (dict(sc=A + 6 * MB + 2), arn.EALIGN),
+    (dict(q=A + 2 * MB), arn.EALIAS),                   # codes on x
+    (dict(sc=A + 2 * MB + 64), arn.EALIAS),             # scales inside x
+    (dict(sc=A + 5 * MB + 16), arn.EALIAS),             # scales inside the codes
+    (dict(q=A + 4 * MB - 64), arn.EALIAS),              # codes reach the weight
+    (dict(cfg=(arn.PATH_WG_ROW, 64, 0, 0), h=8192), arn.ERANGE),
+])
+@fake_addresses
+def test_plain_quant_argument_errors(kw, status):
+    assert pqcall(**kw) == status
+
+
+@fake_addresses
+def test_plain_zero_rows_and_in_place_validation():
+    assert pcall(out=0, x=0, w=0, n=0) == arn.OK
+    assert pqcall(q=0, sc=0, x=0, w=0, n=0) == arn.OK
+    # out == x passes the alias checks; the forced path's ERANGE comes after
+    # them, so nothing is launched.
+    assert pcall(out=A + 2 * MB, h=8192, cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.ERANGE
+
+
 @fake_addresses
 def test_copy2_errors():
     L = arn.lib()

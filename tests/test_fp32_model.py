@@ -120,3 +120,25 @@ def test_quant_model_special_rows():
     x[2] = 0x62C0
     q, sc, _ = fp32_model.add_rmsnorm_quant(x, np.zeros_like(x), w, 1e-6)
     assert sc[0] == 0 and np.isnan(sc[1]) and sc[2] == 0 and (q == 0).all()
+
+
+@pytest.mark.parametrize("n,h", [(64, 1024), (8, 8200), (4, 16384)])
+def test_plain_model_agrees_with_the_oracle(n, h):
+    x, _, w = synth.workload(800 + h, n, h)
+    x[0, ::5] = 0x8000                      # -0 must stay -0 (no addition)
+    m_out, m_res = fp32_model.add_rmsnorm(x, None, w, 1e-6)
+    assert m_res is None
+    o_out = oracle.rmsnorm(x, w, 1e-6)
+    d = ulp_distance(m_out, o_out)
+    assert d.max() <= 1 and (d > 0).mean() < 1e-3
+    assert np.array_equal(m_out[0, ::5], o_out[0, ::5])
+    # and it is the fused model over an all -0 residual, bit for bit
+    f_out, _ = fp32_model.add_rmsnorm(x, np.full_like(x, 0x8000), w, 1e-6)
+    assert np.array_equal(m_out, f_out)
+    mq, ms, _ = fp32_model.add_rmsnorm_quant(x, None, w, 1e-6)
+    fq, fs, _ = fp32_model.add_rmsnorm_quant(x, np.full_like(x, 0x8000), w, 1e-6)
+    assert np.array_equal(mq, fq) and np.array_equal(ms.view(np.uint32), fs.view(np.uint32))
+    oq, os_ = oracle.rmsnorm_quant(x, w, 1e-6)
+    assert np.allclose(ms, os_, rtol=2e-6, atol=0)
+    dq = np.abs(mq.astype(np.int32) - oq.astype(np.int32))
+    assert dq.max() <= 1 and (dq > 0).mean() < 1e-3
