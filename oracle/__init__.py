@@ -23,6 +23,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "add_rmsnorm_oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
+LOG1P_SOURCE = os.path.join(HERE, "log1p_oracle.c")
+LOG1P_LIBRARY = os.path.join(HERE, "liblog1p_oracle.so")
 
 RNE = 0
 TRUNC = 1
@@ -32,10 +34,13 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc into ``liboracle.so`` next to its source."""
+    """Compile the C oracles with gcc into shared libraries next to their sources."""
     if force or not os.path.exists(LIBRARY) or (
             os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
         compile_library(SOURCE, LIBRARY)
+    if force or not os.path.exists(LOG1P_LIBRARY) or (
+            os.path.getmtime(LOG1P_LIBRARY) < os.path.getmtime(LOG1P_SOURCE)):
+        compile_log1p_library(LOG1P_SOURCE, LOG1P_LIBRARY)
     return LIBRARY
 
 
@@ -43,6 +48,15 @@ def compile_library(source: str, target: str) -> str:
     """Compile an oracle source file into a shared library at ``target``."""
     tmp = target + ".tmp%d" % os.getpid()
     subprocess.run(["gcc", *CFLAGS, "-o", tmp, source, "-lm"], check=True)
+    os.replace(tmp, target)
+    return target
+
+
+def compile_log1p_library(source: str, target: str) -> str:
+    """Compile the log1p oracle (binary128 through libquadmath)."""
+    tmp = target + ".tmp%d" % os.getpid()
+    flags = [f if f != "-std=c11" else "-std=gnu11" for f in CFLAGS]
+    subprocess.run(["gcc", *flags, "-o", tmp, source, "-lquadmath", "-lm"], check=True)
     os.replace(tmp, target)
     return target
 
@@ -315,3 +329,105 @@ def cosine_similarity(a: np.ndarray, b: np.ndarray) -> float:
 def chain_fp64_step(residual64: np.ndarray, x_bf16: np.ndarray) -> np.ndarray:
     """One step of the never-rounded residual stream: R + x in binary64."""
     return residual64 + bf16_to_f64(x_bf16)
+
+
+# ---------------------------------------------------------------- log1p
+
+class Log1pOracle:
+    """ctypes front end of one build of the log1p oracle (log1p_oracle.c):
+    ln(1 + x) of binary32 inputs, correctly rounded to binary32."""
+
+    def __init__(self, path: str):
+        L = ctypes.CDLL(path)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.orc_log1p_f32.restype = ctypes.c_int
+        L.orc_log1p_f32.argtypes = [vp, vp, i64]
+        L.orc_log1p_f64.restype = ctypes.c_int
+        L.orc_log1p_f64.argtypes = [vp, vp, i64]
+        L.orc_log1p_f32_fast.restype = ctypes.c_int
+        L.orc_log1p_f32_fast.argtypes = [vp, vp, i64, vp]
+        self.path = path
+        self.lib = L
+
+    @staticmethod
+    def _in(x):
+        return np.ascontiguousarray(x, dtype=np.float32)
+
+    def log1p_f32(self, x) -> np.ndarray:
+        """Correctly rounded binary32 log1p (binary128 evaluation)."""
+        x = self._in(x)
+        out = np.empty_like(x)
+        if self.lib.orc_log1p_f32(_ptr(out), _ptr(x), x.size) != 0:
+            raise ValueError("log1p oracle rejected its arguments")
+        return out
+
+    def log1p_f64(self, x) -> np.ndarray:
+        """binary64 rounding of the binary128 log1p of binary32 inputs."""
+        x = self._in(x)
+        out = np.empty(x.shape, dtype=np.float64)
+        if self.lib.orc_log1p_f64(_ptr(out), _ptr(x), x.size) != 0:
+            raise ValueError("log1p oracle rejected its arguments")
+        return out
+
+    def log1p_f32_fast(self, x, threads: int = 1):
+        """Same results as log1p_f32 (binary64 decides where it can, binary128
+        otherwise); returns (out, number of inputs decided in binary128).
+        ``threads`` > 1 splits the array over that many host threads."""
+        x = self._in(x)
+        out = np.empty_like(x)
+        flat_x, flat_o = x.reshape(-1), out.reshape(-1)
+        n = flat_x.size
+        parts = max(1, min(threads, n // 65536 or 1))
+        bounds = [n * k // parts for k in range(parts + 1)]
+        counts = [0] * parts
+
+        def run(k):
+            lo, hi = bounds[k], bounds[k + 1]
+            esc = ctypes.c_int64(0)
+            rc = self.lib.orc_log1p_f32_fast(flat_o[lo:].ctypes.data, flat_x[lo:].ctypes.data,
+                                             hi - lo, ctypes.byref(esc))
+            if rc != 0:
+                raise ValueError("log1p oracle rejected its arguments")
+            counts[k] = esc.value
+
+        if parts == 1:
+            run(0)
+        else:
+            from concurrent.futures import ThreadPoolExecutor
+
+            with ThreadPoolExecutor(parts) as pool:
+                list(pool.map(run, range(parts)))
+        return out, sum(counts)
+
+
+_default_log1p = None
+
+
+def default_log1p() -> Log1pOracle:
+    global _default_log1p
+    if _default_log1p is None:
+        if not os.path.exists(LOG1P_LIBRARY) or (
+                os.path.getmtime(LOG1P_LIBRARY) < os.path.getmtime(LOG1P_SOURCE)):
+            compile_log1p_library(LOG1P_SOURCE, LOG1P_LIBRARY)
+        _default_log1p = Log1pOracle(LOG1P_LIBRARY)
+    return _default_log1p
+
+
+def log1p_f32(x) -> np.ndarray:
+    return default_log1p().log1p_f32(x)
+
+
+def log1p_f64(x) -> np.ndarray:
+    return default_log1p().log1p_f64(x)
+
+
+def log1p_f32_fast(x, threads: int = 1):
+    return default_log1p().log1p_f32_fast(x, threads)
+
+
+def ulp_error_f32(got, ref64) -> np.ndarray:
+    """|got - ref| in units of binary32 epsilon times |ref|, the measure of
+    the TE issue's reproducer (finfo(float32).eps * |ref|)."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref64, dtype=np.float64)
+    return np.abs(g - r) / (np.finfo(np.float32).eps * np.abs(r))
