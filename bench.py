@@ -37,9 +37,9 @@ PEAK_HBM_GBPS = 8000.0
 CACHE_DEFEAT_BYTES = 1 << 30  # rotate buffer sets until the footprint is >= 1 GiB
 
 
-OPS = ("bf16", "quant", "plain", "plain_quant")
+OPS = ("bf16", "quant", "plain", "plain_quant", "log1p")
 ENTRY = {"bf16": "add_rmsnorm_fwd", "quant": "add_rmsnorm_quant_fwd", "plain": "rmsnorm_fwd",
-         "plain_quant": "rmsnorm_quant_fwd"}
+         "plain_quant": "rmsnorm_quant_fwd", "log1p": "log1p_f32"}
 
 
 def algorithmic_bytes(n_rows: int, hidden: int, op: str = "bf16") -> int:
@@ -61,7 +61,8 @@ def parse_args(argv=None):
     p.add_argument("--workload", default="4096x8192")
     p.add_argument("--op", choices=OPS, default="bf16",
                    help="bf16: the fused op (the benchmark); quant: its int8-quantised "
-                        "variant; plain, plain_quant: RMSNorm without the residual add")
+                        "variant; plain, plain_quant: RMSNorm without the residual add; "
+                        "log1p: the correctly rounded binary32 log1p")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU oracle baseline")
@@ -158,6 +159,82 @@ def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s, op="bf16"):
                       % (passes, n_rows, hidden, el)}
 
 
+def time_steps(torch, step, steps, warmup, stream):
+    """Average milliseconds of `step` over `steps` back-to-back calls on one
+    stream (HIP events), after `warmup` untimed ones; also the wall time."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, time.perf_counter() - t_wall
+
+
+def bench_log1p(args, torch, arn, hip_build, synth):
+    """One step: log1p_f32 over 2^28 binary32 inputs uniform on [0, 1) (the TE
+    issue's reproducer distribution at a size that streams from HBM).  8 bytes
+    per element: read x, write out."""
+    n = synth.LOG1P_BENCH_N
+    dev = torch.device("cuda:0")
+    x = synth.uniform_f32(synth.LOG1P_SEED, 1, n)
+    xd = torch.from_numpy(x).to(dev)
+    out = torch.empty_like(xd)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ms, wall_s = time_steps(torch, lambda i: arn.log1p_f32(out, xd), args.steps, args.warmup,
+                            stream)
+    nbytes = 8 * n
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    # the same bytes through the reference copy: x's halves into out's halves
+    xv, ov = xd.view(torch.int16), out.view(torch.int16)
+    cms, _ = time_steps(torch, lambda i: arn.add_rmsnorm_test_copy2(
+        ov[:n], ov[n:], xv[:n], xv[n:]), min(args.steps, 200), 10, stream)
+    copy_gbps = nbytes / (cms * 1e-3) / 1e9
+    traffic = traffic_from_profiles("log1p", "n%d" % n, hip_build.source_digest())
+    line = {
+        "metric": "log1p_f32 (correctly rounded binary32 log1p) HBM GB/s and % of peak",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "log1p_f32 n=%d fp32, x uniform on [0, 1)" % n, "n": n,
+                   "elements_per_s": round(n / (ms * 1e-3), 1),
+                   "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+                   "wall_s_timed_region": round(wall_s, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic},
+        "copy_ceiling": {"gbps": round(copy_gbps, 2),
+                         "kernel_frac_of_copy": round(gbps / copy_gbps, 4),
+                         "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+                         "what": "add_rmsnorm_test_copy2 moving x's two halves into out"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        lo = oracle.default_log1p()
+        sample = x[: 1 << 20]
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            lo.log1p_f32(sample)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        line["cpu_baseline"] = {
+            "value": round(8 * sample.size * passes / el / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d passes over the first 2^20 inputs of the workload in %.1f s "
+                      "(binary128 log1pq, single thread)" % (passes, el)}
+    print(json.dumps(line))
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -182,6 +259,8 @@ def main(argv=None):
     if args.calibrate_copy:
         run_copy_calibration(torch)
         return 0
+    if args.op == "log1p":
+        return bench_log1p(args, torch, arn, hip_build, synth)
 
     n_rows, hidden = (int(v) for v in args.workload.split("x"))
     cfg = synth.CONFIGS.get(args.workload, dict(seed=3, n_rows=n_rows, hidden=hidden))

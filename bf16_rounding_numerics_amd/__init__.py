@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -38,6 +38,15 @@ class AddRmsnormError(RuntimeError):
         self.status = status
 
 
+LOG1P_FLAG_ACCURATE_ONLY = 1
+
+
+class Log1pCfg(ctypes.Structure):
+    """struct log1p_launch_cfg."""
+    _fields_ = [("block_threads", ctypes.c_int32), ("elems_per_thread", ctypes.c_int32),
+                ("grid_blocks", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
 class LaunchCfg(ctypes.Structure):
     """struct add_rmsnorm_launch_cfg."""
     _fields_ = [("path", ctypes.c_int32), ("block_threads", ctypes.c_int32),
@@ -48,7 +57,7 @@ _lib = None
 
 EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_quant_fwd",
            "add_rmsnorm_quant_fwd_cfg", "rmsnorm_fwd", "rmsnorm_fwd_cfg", "rmsnorm_quant_fwd",
-           "rmsnorm_quant_fwd_cfg", "add_rmsnorm_test_cvt_range",
+           "rmsnorm_quant_fwd_cfg", "log1p_f32", "log1p_f32_cfg", "add_rmsnorm_test_cvt_range",
            "add_rmsnorm_test_copy2", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
            "add_rmsnorm_abi_version", "add_rmsnorm_build_info")
 
@@ -83,6 +92,10 @@ def lib() -> ctypes.CDLL:
     L.rmsnorm_quant_fwd_cfg.restype = i32
     L.rmsnorm_quant_fwd_cfg.argtypes = [vp, vp, vp, vp, i64, i64, f32,
                                         ctypes.POINTER(LaunchCfg), vp]
+    L.log1p_f32.restype = i32
+    L.log1p_f32.argtypes = [vp, vp, i64, vp]
+    L.log1p_f32_cfg.restype = i32
+    L.log1p_f32_cfg.argtypes = [vp, vp, i64, ctypes.POINTER(Log1pCfg), vp]
     L.add_rmsnorm_test_cvt_range.restype = i32
     L.add_rmsnorm_test_cvt_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
     L.add_rmsnorm_test_copy2.restype = i32
@@ -302,6 +315,38 @@ def rmsnorm_quant_fwd_cfg(out_q, out_scale, x, weight, eps: float = 1e-6, path: 
     _check(_on_device(dev, lambda: L.rmsnorm_quant_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
         eps, ctypes.byref(cfg), h)))
+
+
+def _marshal_log1p(out, x):
+    import torch
+
+    for t in (out, x):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("expected torch tensors")
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("out and x must be contiguous float32 GPU tensors")
+    if out.shape != x.shape or out.get_device() != x.get_device():
+        raise ValueError("out must have x's shape and GPU")
+    return x.numel(), x.get_device()
+
+
+def log1p_f32(out, x, stream=None) -> None:
+    """out <- log1p(x), correctly rounded binary32 (out may be x)."""
+    n, dev = _marshal_log1p(out, x)
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.log1p_f32(out.data_ptr(), x.data_ptr(), n, h)))
+
+
+def log1p_f32_cfg(out, x, block_threads: int = 0, elems_per_thread: int = 0,
+                  grid_blocks: int = 0, flags: int = 0, stream=None) -> None:
+    """log1p_f32 with an explicit launch configuration (same results)."""
+    n, dev = _marshal_log1p(out, x)
+    L = lib()
+    cfg = Log1pCfg(block_threads, elems_per_thread, grid_blocks, flags)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.log1p_f32_cfg(out.data_ptr(), x.data_ptr(), n,
+                                                   ctypes.byref(cfg), h)))
 
 
 def add_rmsnorm_test_cvt_range(out, start: int, stream=None) -> None:

@@ -15,8 +15,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
-HEADERS = [os.path.join(CSRC, "launch.h"), os.path.join(INCLUDE, "add_rmsnorm.h")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "log1p.hip"),
+           os.path.join(CSRC, "api.cpp")]
+HEADERS = [os.path.join(CSRC, "launch.h"), os.path.join(INCLUDE, "add_rmsnorm.h"),
+           os.path.join(INCLUDE, "log1p_f32.h")]
 
 ARCH = "gfx950"
 # Numerics flags: no contraction (every fma is written out), IEEE denormals,

@@ -1,9 +1,10 @@
-// C entry points of the fused residual-add + RMSNorm forward and of plain
-// RMSNorm (bf16 or int8 out): argument
-// validation (on the host, before anything is enqueued), kernel choice by
-// hidden size, launch on the caller's stream.  The contract is documented in
-// include/add_rmsnorm.h.
+// C entry points of the fused residual-add + RMSNorm forward, of plain
+// RMSNorm (bf16 or int8 out) and of the correctly rounded binary32 log1p:
+// argument validation (on the host, before anything is enqueued), kernel
+// choice, launch on the caller's stream.  The contracts are documented in
+// include/add_rmsnorm.h and include/log1p_f32.h.
 #include "add_rmsnorm.h"
+#include "log1p_f32.h"
 
 #include <hip/hip_runtime.h>
 
@@ -49,6 +50,10 @@ int pow2_at_least(int64_t need) {
 constexpr int kWaveRowThreads = 256;
 constexpr int kWgRowThreads = 512;
 constexpr int kTwoPassThreads = 512;
+
+// Default launch of log1p_f32: 256 threads, 4 consecutive elements each.
+constexpr int kLog1pThreads = 256;
+constexpr int kLog1pElems = 4;
 
 // Upper hidden sizes of the automatic choice.
 constexpr int64_t kWaveRowMaxHidden = 2048;
@@ -267,6 +272,33 @@ int rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, const uint16_t* x, const 
                       int64_t n_rows, int64_t hidden, float eps, struct ihipStream_t* stream) {
   return rmsnorm_quant_fwd_cfg(out_q, out_scale, x, weight, n_rows, hidden, eps, nullptr,
                                stream);
+}
+
+int log1p_f32_cfg(float* out, const float* x, int64_t n, const struct log1p_launch_cfg* cfg,
+                  struct ihipStream_t* stream) {
+  log1p_launch_cfg c = {0, 0, 0, 0};
+  if (cfg) c = *cfg;
+  if (n < 0) return ADD_RMSNORM_EINVAL;
+  if (c.block_threads != 0 && !valid_block(c.block_threads)) return ADD_RMSNORM_EINVAL;
+  const int e = c.elems_per_thread;
+  if (e != 0 && e != 1 && e != 2 && e != 4 && e != 8) return ADD_RMSNORM_EINVAL;
+  if (c.grid_blocks < -1 || (c.flags & ~LOG1P_FLAG_ACCURATE_ONLY) != 0) return ADD_RMSNORM_EINVAL;
+  if (n == 0) return ADD_RMSNORM_OK;
+  if (!out || !x) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(out) || !aligned16(x)) return ADD_RMSNORM_EALIGN;
+  if ((uint64_t)n > (uint64_t)INT64_MAX / 4) return ADD_RMSNORM_ERANGE;
+  const uint64_t bytes = (uint64_t)n * 4;
+  if (out != x && overlap(out, bytes, x, bytes)) return ADD_RMSNORM_EALIAS;
+  const int b = c.block_threads ? c.block_threads : kLog1pThreads;
+  hipError_t err = addrms::launch_log1p(out, x, n, b, e ? e : kLog1pElems, c.grid_blocks,
+                                        (c.flags & LOG1P_FLAG_ACCURATE_ONLY) != 0,
+                                        reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_failure(err);
+  return ADD_RMSNORM_OK;
+}
+
+int log1p_f32(float* out, const float* x, int64_t n, struct ihipStream_t* stream) {
+  return log1p_f32_cfg(out, x, n, nullptr, stream);
 }
 
 int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,

@@ -49,6 +49,14 @@ size_t lds_two_pass_lds_bytes(int hidden);
 bool wave_row_supported(int block_threads, int segs_per_lane);
 bool wg_row_supported(int block_threads, int segs_per_thread);
 
+// Correctly rounded binary32 log1p of n elements (log1p.hip): E =
+// elems_per_thread (1, 2, 4 or 8) consecutive elements per thread,
+// block_threads * E per tile; grid_blocks as above (0: one workgroup per
+// tile).  accurate_only sends every element through the double-double path.
+hipError_t launch_log1p(float* out, const float* x, int64_t n, int block_threads,
+                        int elems_per_thread, int64_t grid_blocks, bool accurate_only,
+                        hipStream_t stream);
+
 // Reference copy: d0 <- s0 and d1 <- s1, count 16-bit elements each.
 hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,
                         int64_t count, hipStream_t stream);

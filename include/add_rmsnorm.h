@@ -48,7 +48,7 @@ extern "C" {
 /* hipStream_t is a pointer to this opaque struct. */
 struct ihipStream_t;
 
-#define ADD_RMSNORM_ABI_VERSION 2
+#define ADD_RMSNORM_ABI_VERSION 3
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768

@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs: counter-based SplitMix64 + Box-Muller normals -> bf16.
+"""Seeded synthetic inputs: counter-based SplitMix64 + Box-Muller normals -> bf16,
+and uniform binary32 values for the log1p workload.
 
 This module is shared by the tests, the smoke check and the benchmark, and by
 both sides of every parity comparison.  It holds none of the arithmetic of the
@@ -140,12 +141,25 @@ def chain_delta(seed: int, step: int, n_rows: int, hidden: int, std: float) -> n
     return bf16_normal(seed, STREAM_CHAIN_BASE + step, (n_rows, hidden), 0.0, std)
 
 
+def uniform_f32(seed: int, stream: int, n: int) -> np.ndarray:
+    """n binary32 values uniform on [0, 1): the top 24 bits of each SplitMix64
+    output times 2^-24 (exact in binary32), like torch.rand's binary32 draws."""
+    z = splitmix64(stream_key(seed, stream), 0, n)
+    return ((z >> np.uint64(40)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
+
+
 def sha256(*arrays: np.ndarray) -> str:
     h = hashlib.sha256()
     for a in arrays:
         h.update(np.ascontiguousarray(a).tobytes())
     return h.hexdigest()
 
+
+# The log1p workload of the TE issue's reproducer: N binary32 inputs uniform on
+# [0, 1) (its torch.rand(N)); the benchmark uses a larger N of the same kind.
+LOG1P_N = 225280
+LOG1P_BENCH_N = 1 << 28
+LOG1P_SEED = 7
 
 # The five workloads, named rows x hidden.  Distributions as in workload().
 CONFIGS = {

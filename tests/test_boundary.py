@@ -330,3 +330,42 @@ def test_status_codes_match_header():
     for name in ("AUTO", "WAVE_ROW", "WG_ROW", "LDS_TWO_PASS"):
         m = re.search(r"#define ADD_RMSNORM_PATH_%s (\d+)" % name, hdr)
         assert int(m.group(1)) == getattr(arn, "PATH_" + name), name
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), arn.EINVAL),
+    (dict(out=0), arn.EINVAL),
+    (dict(x=0), arn.EINVAL),
+    (dict(out=A + 4), arn.EALIGN),
+    (dict(x=A + 2 * MB + 8), arn.EALIGN),
+    (dict(out=A + 2 * MB + 16), arn.EALIAS),            # out partly overlaps x
+    (dict(cfg=(100, 0, 0, 0)), arn.EINVAL),             # workgroup size
+    (dict(cfg=(0, 3, 0, 0)), arn.EINVAL),               # elements per thread
+    (dict(cfg=(0, 0, -2, 0)), arn.EINVAL),              # grid
+    (dict(cfg=(0, 0, 0, 2)), arn.EINVAL),               # unknown flag
+    (dict(n=1 << 62), arn.ERANGE),
+])
+@fake_addresses
+def test_log1p_argument_errors(kw, status):
+    L = arn.lib()
+    out, x, n = kw.get("out", A), kw.get("x", A + 2 * MB), kw.get("n", 64)
+    if "cfg" in kw:
+        c = arn.Log1pCfg(*kw["cfg"])
+        assert L.log1p_f32_cfg(out, x, n, ctypes.byref(c), None) == status
+    else:
+        assert L.log1p_f32(out, x, n, None) == status
+
+
+@fake_addresses
+def test_log1p_zero_length_is_a_no_op():
+    L = arn.lib()
+    assert L.log1p_f32(0, 0, 0, None) == arn.OK
+    assert L.log1p_f32_cfg(0, 0, 0, None, None) == arn.OK
+
+
+def test_log1p_binding_refuses_cpu_tensors():
+    import torch
+
+    x = torch.zeros(16, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        arn.log1p_f32(torch.empty_like(x), x)

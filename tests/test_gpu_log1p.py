@@ -1,0 +1,175 @@
+"""The launch-invariant binary32 log1p on the GPU.
+
+Bars:
+  * bit-exact against the oracle's correctly rounded log1p (binary128 rounded
+    once), on the TE issue's reproducer workload (225280 inputs uniform on
+    [0, 1)), on inputs over every binade, on the special cases, and on every
+    one of the 2^32 binary32 bit patterns;
+  * one result group over every launch configuration (the issue's sweep of 48
+    block shapes found two): workgroup size x elements per thread x grid;
+  * the ULP error against the binary64 reference, measured as the reproducer
+    measures it, at most half a unit.
+"""
+import numpy as np
+import pytest
+
+import bf16_rounding_numerics_amd as arn
+import oracle
+import synth
+from gpu_helpers import announce, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS = (64, 128, 256, 512, 1024)
+ELEMS = (1, 2, 4, 8)
+GRIDS = (0, 7, -1)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def gpu_log1p(x, block=0, elems=0, grid=0, flags=0, xd=None):
+    import torch
+
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda:0") if xd is None else xd
+    out = torch.full_like(xd, float("nan"))
+    if block or elems or grid or flags:
+        arn.log1p_f32_cfg(out, xd, block_threads=block, elems_per_thread=elems,
+                          grid_blocks=grid, flags=flags)
+    else:
+        arn.log1p_f32(out, xd)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def assert_same(got, exp, label):
+    gn, en = np.isnan(got), np.isnan(exp)
+    assert np.array_equal(gn, en), "%s: NaN pattern differs" % label
+    bad = bits(got)[~gn] != bits(exp)[~en]
+    assert not bad.any(), "%s: %d elements differ, first x index %s" % (
+        label, int(bad.sum()), np.flatnonzero(bad)[:3].tolist())
+
+
+def page_workload():
+    return synth.uniform_f32(synth.LOG1P_SEED, 0, synth.LOG1P_N)
+
+
+def test_reproducer_workload_is_correctly_rounded():
+    x = page_workload()
+    announce("log1p reproducer workload, %d inputs" % x.size)
+    got = gpu_log1p(x)
+    assert_same(got, oracle.log1p_f32(x), "default launch")
+    ref = oracle.log1p_f64(x)
+    err = oracle.ulp_error_f32(got, ref)
+    announce("  ULP error vs binary64: max %.4f mean %.4f" % (err.max(), err.mean()))
+    assert err.max() <= 0.5 + 1e-6
+
+
+def test_reproducer_launch_shapes_agree():
+    """The reproducer's two launches: 1 and 4 elements per thread, 256 threads."""
+    x = page_workload()
+    announce("log1p reproducer shapes")
+    a = gpu_log1p(x, block=256, elems=1)
+    b = gpu_log1p(x, block=256, elems=4)
+    assert int((bits(a) != bits(b)).sum()) == 0
+
+
+def test_every_launch_configuration_gives_one_result_group():
+    import torch
+
+    x = page_workload()
+    xd = torch.from_numpy(x).to("cuda:0")
+    groups = {}
+    for b in BLOCKS:
+        for e in ELEMS:
+            for g in GRIDS:
+                out = gpu_log1p(x, block=b, elems=e, grid=g, xd=xd)
+                groups.setdefault(synth.sha256(out), []).append((b, e, g))
+    announce("log1p sweep: %d configurations, %d result groups"
+             % (sum(len(v) for v in groups.values()), len(groups)))
+    assert len(groups) == 1, list(groups.values())
+
+
+def test_every_binade_and_the_special_cases():
+    rng = np.random.default_rng(71)
+    pos = (2.0 ** rng.uniform(-149, 127.99, 400000)).astype(np.float32)
+    neg = -(2.0 ** rng.uniform(-149, -0.0001, 200000)).astype(np.float32)
+    near_m1 = (-1.0 + 2.0 ** rng.uniform(-24, -1, 100000)).astype(np.float32)
+    specials = np.array([0.0, -0.0, -1.0, -1.0000001, -2.0, -np.inf, np.inf, np.nan,
+                         -np.nan, 3.4028235e38, 1.4e-45, -1.4e-45, 1.0, -0.5, 2.0 ** -24,
+                         -(2.0 ** -25), 2.0 ** 52, 2.0 ** 53, 2.0 ** 24], np.float32)
+    x = np.concatenate([specials, pos, neg, near_m1])
+    announce("log1p binades and specials, %d inputs" % x.size)
+    got = gpu_log1p(x)
+    assert_same(got, oracle.log1p_f32(x), "binades")
+    assert bits(got[0]) == 0 and bits(got[1]) == 0x80000000 and got[2] == -np.inf
+
+
+def test_accurate_path_alone_gives_the_same_results():
+    """Every element through the double-double path (the flag) must give the
+    correctly rounded result too."""
+    rng = np.random.default_rng(72)
+    x = np.concatenate([page_workload()[:50000],
+                        (2.0 ** rng.uniform(-149, 127.99, 50000)).astype(np.float32),
+                        (-1.0 + 2.0 ** rng.uniform(-24, -0.01, 20000)).astype(np.float32)])
+    announce("log1p accurate path only, %d inputs" % x.size)
+    got = gpu_log1p(x, flags=arn.LOG1P_FLAG_ACCURATE_ONLY)
+    assert_same(got, oracle.log1p_f32(x), "accurate only")
+
+
+def test_near_midpoint_inputs():
+    """Inputs whose binary64 log1p lies within 2^-20 of a binary32 rounding
+    quantum from a midpoint, found by scanning four ranges."""
+    from test_oracle_log1p import HARD_SCANS, near_midpoint_inputs
+
+    hard = np.concatenate([near_midpoint_inputs(lo, n) for lo, n in HARD_SCANS])
+    announce("log1p near-midpoint inputs: %d" % hard.size)
+    assert_same(gpu_log1p(hard), oracle.log1p_f32(hard), "near midpoints")
+    assert_same(gpu_log1p(hard, block=64, elems=1), oracle.log1p_f32(hard), "near, 64x1")
+
+
+@pytest.mark.parametrize("n", [1, 3, 255, 1025, 4097, 65536 + 5, (1 << 20) + 3])
+def test_ragged_lengths(n):
+    x = synth.uniform_f32(73, 1, n) * np.float32(4.0) - np.float32(0.9)
+    announce("log1p n=%d" % n)
+    exp = oracle.log1p_f32(x)
+    for b, e in ((256, 4), (64, 8), (1024, 1), (128, 2)):
+        assert_same(gpu_log1p(x, block=b, elems=e), exp, "n=%d %dx%d" % (n, b, e))
+
+
+def test_in_place():
+    import torch
+
+    x = page_workload()
+    xd = torch.from_numpy(x.copy()).to("cuda:0")
+    arn.log1p_f32(xd, xd)
+    torch.cuda.synchronize()
+    assert_same(xd.cpu().numpy(), oracle.log1p_f32(x), "in place")
+
+
+def test_all_binary32_inputs():
+    """Every one of the 2^32 bit patterns, in chunks, against the oracle's fast
+    form (binary64 where its bound decides, binary128 otherwise)."""
+    import torch
+
+    chunk = 1 << 26
+    threads = 16
+    total_esc = 0
+    for c in range((1 << 32) // chunk):
+        lo = c * chunk
+        u = torch.arange(lo, lo + chunk, dtype=torch.int64, device="cuda:0").to(torch.int32)
+        xd = u.view(torch.float32)
+        got = gpu_log1p(None, xd=xd)
+        x = xd.cpu().numpy()
+        exp, esc = oracle.log1p_f32_fast(x, threads=threads)
+        total_esc += esc
+        assert_same(got, exp, "chunk %d (bit patterns 0x%08x..)" % (c, lo))
+        if c % 8 == 7:
+            announce("  all inputs: %d of 64 chunks agree" % (c + 1))
+    announce("  all 2^32 inputs agree; %d decided by the oracle in binary128" % total_esc)
