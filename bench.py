@@ -177,24 +177,30 @@ def time_steps(torch, step, steps, warmup, stream):
 
 
 def bench_log1p(args, torch, arn, hip_build, synth):
-    """One step: log1p_f32 over 2^28 binary32 inputs uniform on [0, 1) (the TE
-    issue's reproducer distribution at a size that streams from HBM).  8 bytes
-    per element: read x, write out."""
+    """One step: log1p_f32 over 2^26 binary32 inputs uniform on [0, 1) (the TE
+    issue's reproducer distribution at a size that streams from HBM), rotating
+    over buffer sets like the norm benchmark.  8 bytes per element: read x,
+    write out."""
     n = synth.LOG1P_BENCH_N
     dev = torch.device("cuda:0")
     x = synth.uniform_f32(synth.LOG1P_SEED, 1, n)
-    xd = torch.from_numpy(x).to(dev)
-    out = torch.empty_like(xd)
+    sets = max(1, -(-CACHE_DEFEAT_BYTES // (8 * n)))
+    xs = [torch.from_numpy(x).to(dev)]
+    xs += [xs[0].clone() for _ in range(sets - 1)]
+    outs = [torch.empty_like(xs[0]) for _ in range(sets)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ms, wall_s = time_steps(torch, lambda i: arn.log1p_f32(out, xd), args.steps, args.warmup,
-                            stream)
+    ms, wall_s = time_steps(torch, lambda i: arn.log1p_f32(outs[i % sets], xs[i % sets]),
+                            args.steps, args.warmup, stream)
     nbytes = 8 * n
     gbps = nbytes / (ms * 1e-3) / 1e9
+
     # the same bytes through the reference copy: x's halves into out's halves
-    xv, ov = xd.view(torch.int16), out.view(torch.int16)
-    cms, _ = time_steps(torch, lambda i: arn.add_rmsnorm_test_copy2(
-        ov[:n], ov[n:], xv[:n], xv[n:]), min(args.steps, 200), 10, stream)
+    def copy(i):
+        xv, ov = xs[i % sets].view(torch.int16), outs[i % sets].view(torch.int16)
+        arn.add_rmsnorm_test_copy2(ov[:n], ov[n:], xv[:n], xv[n:])
+
+    cms, _ = time_steps(torch, copy, min(args.steps, 500), 10, stream)
     copy_gbps = nbytes / (cms * 1e-3) / 1e9
     traffic = traffic_from_profiles("log1p", "n%d" % n, hip_build.source_digest())
     line = {
@@ -203,6 +209,7 @@ def bench_log1p(args, torch, arn, hip_build, synth):
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "log1p_f32 n=%d fp32, x uniform on [0, 1)" % n, "n": n,
+                   "buffer_sets": sets,
                    "elements_per_s": round(n / (ms * 1e-3), 1),
                    "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                    "wall_s_timed_region": round(wall_s, 4)},

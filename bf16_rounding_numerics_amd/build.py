@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "log1p.hip"),
            os.path.join(CSRC, "api.cpp")]
-HEADERS = [os.path.join(CSRC, "launch.h"), os.path.join(INCLUDE, "add_rmsnorm.h"),
-           os.path.join(INCLUDE, "log1p_f32.h")]
+HEADERS = [os.path.join(CSRC, "launch.h"), os.path.join(CSRC, "log1p_table.h"),
+           os.path.join(INCLUDE, "add_rmsnorm.h"), os.path.join(INCLUDE, "log1p_f32.h")]
 
 ARCH = "gfx950"
 # Numerics flags: no contraction (every fma is written out), IEEE denormals,

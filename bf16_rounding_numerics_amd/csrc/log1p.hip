@@ -11,34 +11,39 @@
 // the build passes -ffp-contract=off and every fused multiply-add below is
 // written out, so no code-generation choice can change an operation.
 //
-// Fast path, in binary64 (x is binary32, so X = x is exact):
-//   u  = fl(1 + X); c = X - (u - 1), the rounding error of u, kept when u <= 2.
-//        u is exact for 2^-29 <= |X| < 2^52, so c != 0 only when |u - 1| <= 2^-29.
-//   u  = 2^k m with m in [sqrt(1/2), sqrt(2)); f = m - 1 (exact: Sterbenz).
-//   s  = f / (2 + f), |s| <= 3 - 2 sqrt(2) < 0.1716, and
-//        ln m = 2 atanh(s) = 2s + 2s^3/3 + 2s^5/5 + ..., summed to s^19
-//        (the first term left out is below 2^-55 of the sum).
-//   ln(1 + X) = k ln2_hi + (k ln2_lo + (ln m + c (2 - u))), where c (2 - u)
-//        is c / u to within (u - 1)^2 relative, and k ln2_hi is exact.
-// The rounding errors add up to less than 2^-50 of the result (division and
-// 2 + f: 2 ulp; the series and the three sums: at most 3 more; the truncation
-// 2^-55; relative to |result| >= 0.346 when k != 0).
+// Regular inputs are x in (-1, +Inf) with |x| > 2^-25; the others are IEEE
+// special cases or round to x itself (|x| <= 2^-25: ln(1 + x) = x - x^2/2 + ...
+// lies within x^2/2 <= 2^-26 |x| of x, less than half the spacing around x).
 //
-// Rounding test: y is rounded to binary32 r.  If y lies farther than 2^-47 |y|
-// from both midpoints between r and its binary32 neighbours, the exact value
-// is on the same side of them and r is the correctly rounded result.  Other
-// inputs (about one in four million) take the accurate path.
+// Fast path, in binary64 (X = x exactly):
+//   u = 1 + X, exact here: X has 24 significant bits between 2^-48 and 2^51
+//       (for X >= 2^52 the rounding of u moves ln u by under 2^-58 relative).
+//   u = 2^k m with m in [sqrt(1/2), sqrt(2)).
+//   i = round((m - 1) * 256) in [-75, 106]; from the table, inv_i = fl(1/c_i)
+//       with c_i = 1 + i/256, and -ln(inv_i).  r = m * inv_i - 1 (one fma),
+//       |r| <= 2^-8.5.
+//   ln(1 + X) = k ln 2 + (-ln inv_i) + log1p(r), with log1p(r) = r - r^2/2 +
+//       ... + r^7/7 (the next term is below 2^-62 of r).  k ln2_hi is exact.
+// The result y is within 2^-49.5 of ln(1 + X) relative (a host sweep of all
+// regular inputs against glibc's log1p finds at most 2^-51).
+//
+// Rounding test: the binary32 rounding of y drops the low 29 of y's 52
+// fraction bits; y is within 128 binary64 ulps (at least 2^-46 |y|) of a
+// binary32 midpoint exactly when those bits are within 128 of 2^28.  Outside
+// that window the exact value rounds like y.  Inside it (about one input in
+// two million) the accurate path decides.
 //
 // Accurate path: the same steps in double-double arithmetic (unevaluated sums
-// hi + lo with |lo| <= ulp(hi) / 2; Knuth's two-sum, the fma two-product,
-// Dekker-style products and quotients), 1 + X held exactly, the atanh series
-// to s^39 with double-double coefficients, ln 2 in three parts.  Its error is
-// about 2^-100 relative; the double-double result is rounded to binary32 by
-// comparing its distance from r with half the neighbouring binary32 spacing.
+// hi + lo with |lo| <= ulp(hi) / 2; Knuth's two-sum and the fma two-product),
+// with m * inv_i - 1 held exactly, -ln(inv_i) in two parts, log1p(r) to r^13
+// and ln 2 in three parts: about 2^-100 relative.  The double-double result
+// is rounded to binary32 by comparing its distance from the nearest binary32
+// with half the spacing on that side.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "launch.h"
+#include "log1p_table.h"
 
 namespace addrms {
 namespace {
@@ -49,6 +54,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // ln 2 in parts.  LN2_HI has 44 significant bits, so k * LN2_HI is exact for
 // |k| < 2^9; LN2_LO is the binary64 rounding of ln 2 - LN2_HI.  For the
@@ -60,9 +66,13 @@ constexpr double LN2_P1 = 0x1.62e42fefa3a00p-1;
 constexpr double LN2_P2 = -0x1.0ca86c3898c00p-49;
 constexpr double LN2_P3 = -0x1.ff0342542fc33p-94;
 constexpr double SQRT_HALF = 0.70710678118654752440;
+// fma(m, 256, ROUND_MAGIC) = 1.5 * 2^52 + round((m - 1) * 256): the low word
+// of the result is that integer (two's complement).
+constexpr double ROUND_MAGIC = 0x1.8p52 - 256.0;
 
 DEV uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
 DEV float ffrom(uint32_t b) { return __builtin_bit_cast(float, b); }
+DEV uint32_t low_word(double v) { return (uint32_t)__builtin_bit_cast(uint64_t, v); }
 
 // u = 2^k m, m in [sqrt(1/2), sqrt(2)); u > 0 and finite.
 DEV double reduce(double u, int* k) {
@@ -76,46 +86,42 @@ DEV double reduce(double u, int* k) {
   return m;
 }
 
-// ---------------------------------------------------------------- fast path
-
-// ln(1 + X) in binary64 for X in (-1, FLT_MAX], relative error below 2^-50.
-DEV double log1p_fast(double X) {
-  const double u = X + 1.0;
-  const double c = u <= 2.0 ? X - (u - 1.0) : 0.0;
-  int k;
-  const double m = reduce(u, &k);
-  const double f = m - 1.0;
-  const double s = f / (2.0 + f);
-  const double z = s * s;
-  // 2/3 + 2z/5 + ... + 2z^8/19
-  double R = 2.0 / 19.0;
-  R = __builtin_fma(R, z, 2.0 / 17.0);
-  R = __builtin_fma(R, z, 2.0 / 15.0);
-  R = __builtin_fma(R, z, 2.0 / 13.0);
-  R = __builtin_fma(R, z, 2.0 / 11.0);
-  R = __builtin_fma(R, z, 2.0 / 9.0);
-  R = __builtin_fma(R, z, 2.0 / 7.0);
-  R = __builtin_fma(R, z, 2.0 / 5.0);
-  R = __builtin_fma(R, z, 2.0 / 3.0);
-  const double ln_m = __builtin_fma(s * z, R, s + s);
-  const double kd = (double)k;
-  const double t1 = ln_m + c * (2.0 - u);
-  const double t2 = __builtin_fma(kd, LN2_LO, t1);
-  return __builtin_fma(kd, LN2_HI, t2);
+// Table row of m: round((m - 1) * 256) - LOG1P_TABLE_MIN, in [0, 181].
+DEV int table_row(double m) {
+  return (int)low_word(__builtin_fma(m, 256.0, ROUND_MAGIC)) - LOG1P_TABLE_MIN;
 }
 
-// The binary32 rounding of y is certain when y, known to within 2^-47 |y|,
-// is that far from both midpoints around it.  y != 0 and finite.
-DEV bool rounding_is_certain(double y, float r) {
-  const double a = __builtin_fabs(y);
-  const float ra = __builtin_fabsf(r);
-  const uint32_t rb = fbits(ra);  // >= 1: |y| > 2^-150 here
-  const double up = (double)ffrom(rb + 1u);
-  const double dn = (double)ffrom(rb - 1u);
-  const double m_hi = ((double)ra + up) * 0.5;  // exact
-  const double m_lo = ((double)ra + dn) * 0.5;
-  const double tol = a * 0x1p-47;
-  return (a - m_lo > tol) && (m_hi - a > tol);
+// ---------------------------------------------------------------- fast path
+
+// ln(1 + X) in binary64 for a regular X; inv_t = {inv_i, t_hi} of the row.
+// `row` receives the table row for the accurate path.
+template <typename Table>
+DEV double log1p_fast(double X, const Table& tab, int* row) {
+  const double u = X + 1.0;
+  int k;
+  const double m = reduce(u, &k);
+  *row = table_row(m);
+  const f64x2 it = tab(*row);
+  const double r = __builtin_fma(m, it.x, -1.0);
+  // log1p(r) = r + r^2 (-1/2 + r/3 - r^2/4 + r^3/5 - r^4/6 + r^5/7)
+  double P = 1.0 / 7.0;
+  P = __builtin_fma(P, r, -1.0 / 6.0);
+  P = __builtin_fma(P, r, 1.0 / 5.0);
+  P = __builtin_fma(P, r, -1.0 / 4.0);
+  P = __builtin_fma(P, r, 1.0 / 3.0);
+  P = __builtin_fma(P, r, -0.5);
+  const double L = __builtin_fma(r * r, P, r);
+  const double kd = (double)k;
+  const double A = __builtin_fma(kd, LN2_LO, L);
+  const double B = it.y + A;
+  return __builtin_fma(kd, LN2_HI, B);
+}
+
+// True when y lies within 128 binary64 ulps of a binary32 rounding midpoint
+// (y in the binary32 normal range).
+DEV bool near_midpoint(double y) {
+  const int32_t d = (int32_t)(low_word(y) & 0x1FFFFFFFu) - 0x10000000;
+  return d <= 128 && d >= -128;
 }
 
 // ---------------------------------------------------------------- accurate path
@@ -157,50 +163,35 @@ DEV dd dd_mul(dd x, dd y) {
   return fast_two_sum(p.hi, p.lo);
 }
 
-DEV dd dd_mul_d(dd x, double b) {
-  dd p = two_prod(x.hi, b);
-  p.lo = __builtin_fma(x.lo, b, p.lo);
-  return fast_two_sum(p.hi, p.lo);
+// (-1)^(n+1) / n as a double-double: hi = fl(1/n), lo = fl((1 - hi n) / n),
+// the residual 1 - hi n exact by fma.
+DEV dd series_coef(int n) {
+  const double nd = (double)n;
+  const double hi = 1.0 / nd;
+  const dd c = {hi, __builtin_fma(-hi, nd, 1.0) / nd};
+  return (n & 1) ? c : dd{-c.hi, -c.lo};
 }
 
-DEV dd dd_neg(dd x) { return {-x.hi, -x.lo}; }
-
-// x / y by three quotient digits, each corrected against the remainder.
-DEV dd dd_div(dd x, dd y) {
-  const double q1 = x.hi / y.hi;
-  dd r = dd_add(x, dd_neg(dd_mul_d(y, q1)));
-  const double q2 = r.hi / y.hi;
-  r = dd_add(r, dd_neg(dd_mul_d(y, q2)));
-  const double q3 = r.hi / y.hi;
-  const dd q = fast_two_sum(q1, q2);
-  return dd_add(q, dd{q3, 0.0});
-}
-
-// 1 / n as a double-double: hi = fl(1/n), lo = fl((1 - hi n) / n), where the
-// residual 1 - hi n is exact by fma.
-DEV dd recip(double n) {
-  const double hi = 1.0 / n;
-  return {hi, __builtin_fma(-hi, n, 1.0) / n};
-}
-
-// ln(1 + X) as a double-double, relative error about 2^-100.
+// ln(1 + X) as a double-double for a regular X, about 2^-100 relative.
 DEV dd log1p_accurate(double X) {
   const dd U = two_sum(1.0, X);  // exactly 1 + X
   int k;
   const double mh = reduce(U.hi, &k);
   const double ml = __builtin_amdgcn_ldexp(U.lo, -k);
-  const dd F = two_sum(mh - 1.0, ml);  // m - 1, exact
-  const dd D = dd_add(dd{2.0, 0.0}, F);
-  const dd S = dd_div(F, D);
-  const dd Z = dd_mul(S, S);
-  // P = sum_{n=0}^{19} Z^n / (2n + 1), by Horner
-  dd P = recip(39.0);
-  for (int n = 18; n >= 0; --n) P = dd_add(dd_mul(P, Z), recip(2.0 * n + 1.0));
-  dd L = dd_mul(S, P);
-  L = {L.hi + L.hi, L.lo + L.lo};  // 2 S P: ln m
+  const double* e = log1p_table[table_row(mh)];
+  const double inv = e[0];
+  // R = m * inv - 1: the product exactly, p - 1 exact (p within 2^-8 of 1)
+  dd p = two_prod(mh, inv);
+  p.lo = __builtin_fma(ml, inv, p.lo);
+  const dd R = two_sum(p.hi - 1.0, p.lo);
+  // log1p(R) = R * sum_{n=1}^{13} (-1)^(n+1) R^(n-1) / n, by Horner
+  dd Q = series_coef(13);
+  for (int n = 12; n >= 1; --n) Q = dd_add(dd_mul(Q, R), series_coef(n));
+  const dd L = dd_mul(Q, R);
+  const dd T = {e[1], e[2]};
   const double kd = (double)k;
   const dd K = dd_add(two_sum(kd * LN2_P1, kd * LN2_P2), dd{kd * LN2_P3, 0.0});
-  return dd_add(K, L);
+  return dd_add(K, dd_add(T, L));
 }
 
 // Nearest binary32 (ties to even) of the double-double Y, Y != 0.
@@ -221,33 +212,52 @@ DEV float round_dd_to_f32(dd Y) {
   return neg ? -ra : ra;
 }
 
-// The accurate path, correctly rounded to binary32.  Rare, so it is kept out
-// of line: one copy, called only by the lanes that need it.
-__device__ __noinline__ float log1p_accurate_f32(double X) {
+// The accurate path, correctly rounded to binary32.
+DEV float log1p_accurate_f32(double X) {
   return round_dd_to_f32(log1p_accurate(X));
 }
 
 // ---------------------------------------------------------------- one element
 
-// IEEE special cases of log1p, then the fast path, then, when its rounding is
-// not certain (or `accurate` asks for it), the accurate path.
-DEV float log1p_f32_elem(float x, bool accurate) {
-  const bool is_nan = x != x;
-  const bool special = is_nan || x == 0.0f || x <= -1.0f || x == __builtin_inff();
-  float special_val;
-  if (is_nan)
-    special_val = x + x;  // quiet NaN
-  else if (x == 0.0f || x == __builtin_inff())
-    special_val = x;  // +-0 keep their sign; +Inf
-  else if (x == -1.0f)
-    special_val = -__builtin_inff();
-  else
-    special_val = __builtin_nanf("");  // x < -1, -Inf
-  const double X = special ? 0.5 : (double)x;
-  const double y = log1p_fast(X);
-  float r = (float)y;
-  if (!special && (accurate || !rounding_is_certain(y, r))) r = log1p_accurate_f32(X);
-  return special ? special_val : r;
+// The result of a non-regular x: NaN -> quiet NaN, |x| <= 2^-25 (with +-0)
+// -> x, -1 -> -Inf, x < -1 -> NaN, +Inf -> +Inf.  Selects, no branches.
+DEV float log1p_irregular(float x) {
+  const float below = x == -1.0f ? -__builtin_inff() : __builtin_nanf("");
+  const float v = x < -1.0f || x == -1.0f ? below : x;  // tiny, +Inf
+  return x != x ? x + x : v;
+}
+
+DEV bool is_regular(float x) {
+  return x > -1.0f && x < __builtin_inff() && __builtin_fabsf(x) > 0x1p-25f;  // NaN fails
+}
+
+// log1p of E elements in place.  The fast path of all E runs first, with no
+// branch or call between them so that their instructions interleave; the
+// rare elements whose rounding it cannot settle (or all, when `accurate`)
+// are then recomputed by the accurate path.
+template <int E, typename Table>
+DEV void log1p_f32_vec(float (&v)[E], bool accurate, const Table& tab) {
+  double y[E];
+  bool reg[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    reg[e] = is_regular(v[e]);
+    int row;
+    y[e] = log1p_fast(reg[e] ? (double)v[e] : 0.5, tab, &row);
+  }
+  bool any = false;
+#pragma unroll
+  for (int e = 0; e < E; ++e) any = any || (reg[e] && (accurate || near_midpoint(y[e])));
+  float r[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) r[e] = (float)y[e];
+  if (any) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (reg[e] && (accurate || near_midpoint(y[e]))) r[e] = log1p_accurate_f32((double)v[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = reg[e] ? r[e] : log1p_irregular(v[e]);
 }
 
 // ---------------------------------------------------------------- kernel
@@ -264,13 +274,24 @@ DEV __amdgpu_buffer_rsrc_t tile_rsrc(const float* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
 }
 
+// {inv_i, t_hi} rows of the table, staged in LDS once per workgroup.
+struct LdsTable {
+  const f64x2* rows;
+  DEV f64x2 operator()(int row) const { return rows[row]; }
+};
+
 // E consecutive elements per thread, blockDim.x * E per tile; workgroups loop
 // over tiles.  Full tiles use E-wide nontemporal buffer loads and stores;
 // the last, partial tile goes element by element with a bounds check.
 template <int E>
 __global__ __launch_bounds__(1024) void k_log1p(Log1pParams p) {
+  __shared__ f64x2 rows[LOG1P_TABLE_SIZE];
   const int B = blockDim.x;
   const int t = threadIdx.x;
+  for (int i = t; i < LOG1P_TABLE_SIZE; i += B)
+    rows[i] = f64x2{log1p_table[i][0], log1p_table[i][1]};
+  __syncthreads();
+  const LdsTable tab{rows};
   const bool acc = p.accurate != 0;
   for (int64_t tile = blockIdx.x; tile < p.tiles; tile += gridDim.x) {
     const int64_t base = tile * (int64_t)B * E;
@@ -281,26 +302,30 @@ __global__ __launch_bounds__(1024) void k_log1p(Log1pParams p) {
       const __amdgpu_buffer_rsrc_t ro = tile_rsrc(p.out + base, bytes);
       const int off = t * E * 4;
       if constexpr (E == 1) {
-        const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 2));
-        __builtin_amdgcn_raw_buffer_store_b32(fbits(log1p_f32_elem(v, acc)), ro, off, 0, 2);
+        float v[1] = {__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 2))};
+        log1p_f32_vec(v, acc, tab);
+        __builtin_amdgcn_raw_buffer_store_b32(fbits(v[0]), ro, off, 0, 2);
       } else if constexpr (E == 2) {
-        f32x2 v = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 2));
-        v.x = log1p_f32_elem(v.x, acc);
-        v.y = log1p_f32_elem(v.y, acc);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro, off, 0, 2);
+        const f32x2 q = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 2));
+        float v[2] = {q.x, q.y};
+        log1p_f32_vec(v, acc, tab);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{v[0], v[1]}), ro, off,
+                                              0, 2);
       } else {
-        f32x4 v[E / 4];
-#pragma unroll
-        for (int h = 0; h < E / 4; ++h)
-          v[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16 * h,
-                                                                                   0, 2));
+        float v[E];
 #pragma unroll
         for (int h = 0; h < E / 4; ++h) {
-          f32x4 w;
-          w.x = log1p_f32_elem(v[h].x, acc);
-          w.y = log1p_f32_elem(v[h].y, acc);
-          w.z = log1p_f32_elem(v[h].z, acc);
-          w.w = log1p_f32_elem(v[h].w, acc);
+          const f32x4 q = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16 * h, 0, 2));
+          v[4 * h] = q.x;
+          v[4 * h + 1] = q.y;
+          v[4 * h + 2] = q.z;
+          v[4 * h + 3] = q.w;
+        }
+        log1p_f32_vec(v, acc, tab);
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) {
+          const f32x4 w = {v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, off + 16 * h,
                                                  0, 2);
         }
@@ -308,7 +333,11 @@ __global__ __launch_bounds__(1024) void k_log1p(Log1pParams p) {
     } else {
       for (int e = 0; e < E; ++e) {
         const int64_t i = base + (int64_t)t * E + e;
-        if (i < p.n) p.out[i] = log1p_f32_elem(p.x[i], acc);
+        if (i < p.n) {
+          float v[1] = {p.x[i]};
+          log1p_f32_vec(v, acc, tab);
+          p.out[i] = v[0];
+        }
       }
     }
   }

@@ -158,7 +158,7 @@ def sha256(*arrays: np.ndarray) -> str:
 # The log1p workload of the TE issue's reproducer: N binary32 inputs uniform on
 # [0, 1) (its torch.rand(N)); the benchmark uses a larger N of the same kind.
 LOG1P_N = 225280
-LOG1P_BENCH_N = 1 << 28
+LOG1P_BENCH_N = 1 << 26
 LOG1P_SEED = 7
 
 # The five workloads, named rows x hidden.  Distributions as in workload().
