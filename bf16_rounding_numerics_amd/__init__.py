@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -30,6 +30,7 @@ PATH_AUTO = 0
 PATH_WAVE_ROW = 1
 PATH_WG_ROW = 2
 PATH_LDS_TWO_PASS = 3
+PATH_GENERAL = 4
 
 
 class AddRmsnormError(RuntimeError):
@@ -55,7 +56,8 @@ class LaunchCfg(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_quant_fwd",
+EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_fwd_strided",
+           "rmsnorm_fwd_strided", "add_rmsnorm_quant_fwd",
            "add_rmsnorm_quant_fwd_cfg", "rmsnorm_fwd", "rmsnorm_fwd_cfg", "rmsnorm_quant_fwd",
            "rmsnorm_quant_fwd_cfg", "log1p_f32", "log1p_f32_cfg", "add_rmsnorm_test_cvt_range",
            "add_rmsnorm_test_copy2", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
@@ -83,6 +85,12 @@ def lib() -> ctypes.CDLL:
     L.add_rmsnorm_quant_fwd_cfg.restype = i32
     L.add_rmsnorm_quant_fwd_cfg.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32,
                                             ctypes.POINTER(LaunchCfg), vp]
+    L.add_rmsnorm_fwd_strided.restype = i32
+    L.add_rmsnorm_fwd_strided.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i64, f32,
+                                          ctypes.POINTER(LaunchCfg), vp]
+    L.rmsnorm_fwd_strided.restype = i32
+    L.rmsnorm_fwd_strided.argtypes = [vp, i64, vp, i64, vp, i64, i64, f32,
+                                      ctypes.POINTER(LaunchCfg), vp]
     L.rmsnorm_fwd.restype = i32
     L.rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, vp]
     L.rmsnorm_fwd_cfg.restype = i32
@@ -270,6 +278,60 @@ def add_rmsnorm_quant_fwd_cfg(out_q, out_scale, residual_out, x, residual, weigh
     _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
         residual.data_ptr(), weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg), h)))
+
+
+def _row_view(t, hidden, dev, name):
+    """(pointer, row stride in elements) of a 2-D row-strided bf16 view."""
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.get_device() != dev:
+        raise ValueError("%s must be a GPU tensor on the weight's device" % name)
+    if t.dtype not in _dtypes():
+        raise TypeError("%s must hold bf16 (bfloat16, or raw 16-bit patterns)" % name)
+    if t.dim() != 2 or t.shape[1] != hidden or (t.shape[0] > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be [n_rows, hidden] with unit column stride" % name)
+    return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else hidden)
+
+
+def add_rmsnorm_fwd_strided(out, residual_out, x, residual, weight, eps: float = 1e-6,
+                            path: int = PATH_AUTO, block_threads: int = 0, grid_blocks: int = 0,
+                            stream=None) -> None:
+    """The fused forward on 2-D views whose rows may be strided (e.g. column
+    slices of wider matrices): each tensor [n_rows, hidden] with unit column
+    stride; weight [hidden] contiguous."""
+    if weight.dim() != 1 or not weight.is_cuda or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous 1-D GPU tensor")
+    hidden, dev = weight.shape[0], weight.get_device()
+    po, so = _row_view(out, hidden, dev, "out")
+    pro, sro = _row_view(residual_out, hidden, dev, "residual_out")
+    px, sx = _row_view(x, hidden, dev, "x")
+    pr, sr = _row_view(residual, hidden, dev, "residual")
+    n_rows = x.shape[0]
+    if not (out.shape[0] == residual_out.shape[0] == residual.shape[0] == n_rows):
+        raise ValueError("all views need the same number of rows")
+    L = lib()
+    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_fwd_strided(
+        po, so, pro, sro, px, sx, pr, sr, weight.data_ptr(), n_rows, hidden, eps,
+        ctypes.byref(cfg), h)))
+
+
+def rmsnorm_fwd_strided(out, x, weight, eps: float = 1e-6, path: int = PATH_AUTO,
+                        block_threads: int = 0, grid_blocks: int = 0, stream=None) -> None:
+    """Plain RMSNorm on 2-D views whose rows may be strided."""
+    if weight.dim() != 1 or not weight.is_cuda or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous 1-D GPU tensor")
+    hidden, dev = weight.shape[0], weight.get_device()
+    po, so = _row_view(out, hidden, dev, "out")
+    px, sx = _row_view(x, hidden, dev, "x")
+    if out.shape[0] != x.shape[0]:
+        raise ValueError("out and x need the same number of rows")
+    L = lib()
+    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.rmsnorm_fwd_strided(
+        po, so, px, sx, weight.data_ptr(), x.shape[0], hidden, eps, ctypes.byref(cfg), h)))
 
 
 def rmsnorm_fwd(out, x, weight, eps: float = 1e-6, stream=None) -> None:

@@ -47,6 +47,7 @@ int pow2_at_least(int64_t need) {
 }
 
 // Default workgroup sizes per path.
+constexpr int kGeneralThreads = 256;
 constexpr int kWaveRowThreads = 256;
 constexpr int kWgRowThreads = 512;
 constexpr int kTwoPassThreads = 512;
@@ -94,6 +95,73 @@ bool output_aliases_badly(const void* o, uint64_t t_bytes, const void* x, const 
   return false;
 }
 
+// Scalar arguments and launch configuration of the bf16-out entry points,
+// which take any hidden in [1, ADD_RMSNORM_MAX_HIDDEN] and the general path.
+int check_scalars_any_hidden(int64_t n_rows, int64_t hidden, float eps,
+                             const add_rmsnorm_launch_cfg* cfg, add_rmsnorm_launch_cfg* c) {
+  if (n_rows < 0 || hidden <= 0 || !std::isfinite(eps) || eps < 0.0f) return ADD_RMSNORM_EINVAL;
+  if (hidden > ADD_RMSNORM_MAX_HIDDEN) return ADD_RMSNORM_ERANGE;
+  *c = add_rmsnorm_launch_cfg{ADD_RMSNORM_PATH_AUTO, 0, 0, 0};
+  if (cfg) *c = *cfg;
+  if (c->flags != 0 || c->grid_blocks < -1) return ADD_RMSNORM_EINVAL;
+  if (c->path < ADD_RMSNORM_PATH_AUTO || c->path > ADD_RMSNORM_PATH_GENERAL)
+    return ADD_RMSNORM_EINVAL;
+  if (c->block_threads != 0 && !valid_block(c->block_threads)) return ADD_RMSNORM_EINVAL;
+  return ADD_RMSNORM_OK;
+}
+
+// A row-strided view: n rows of `width` bytes, `stride` bytes apart.
+struct View {
+  const void* p;
+  uint64_t stride;
+};
+
+int64_t floor_div(int64_t a, int64_t b) {  // b > 0
+  int64_t q = a / b;
+  if ((a % b != 0) && (a < 0)) --q;
+  return q;
+}
+
+// Whether two views of n rows of `width` bytes share a byte.  Views with one
+// stride s meet exactly when some row difference q in [-(n-1), n-1] puts the
+// base difference within a row width of q * s; views with different strides
+// are taken to meet whenever their spans do.
+bool views_overlap(View a, View b, int64_t n, uint64_t width) {
+  const uint64_t span_a = (uint64_t)(n - 1) * a.stride + width;
+  const uint64_t span_b = (uint64_t)(n - 1) * b.stride + width;
+  if (!overlap(a.p, span_a, b.p, span_b)) return false;
+  if (a.stride != b.stride) return true;
+  const int64_t d = (int64_t)(reinterpret_cast<uintptr_t>(b.p) - reinterpret_cast<uintptr_t>(a.p));
+  const int64_t s = (int64_t)a.stride;
+  const int64_t q = floor_div(d, s);
+  for (int64_t qq = q; qq <= q + 1; ++qq) {
+    if (qq < -(n - 1) || qq > n - 1) continue;
+    const int64_t r = d - qq * s;
+    if (r > -(int64_t)width && r < (int64_t)width) return true;
+  }
+  return false;
+}
+
+// Whether a view of n rows of `width` bytes shares a byte with the range
+// [q, q + len): some row i in [0, n) with i s < d + len and i s + width > d,
+// d = q - base.
+bool view_meets_range(View v, int64_t n, uint64_t width, const void* q, uint64_t len) {
+  const int64_t d = (int64_t)(reinterpret_cast<uintptr_t>(q) - reinterpret_cast<uintptr_t>(v.p));
+  const int64_t s = (int64_t)v.stride;
+  int64_t i_min = floor_div(d - (int64_t)width, s) + 1;  // first row ending after d
+  int64_t i_max = -floor_div(-(d + (int64_t)len), s) - 1;  // last row starting before d + len
+  if (i_min < 0) i_min = 0;
+  if (i_max > n - 1) i_max = n - 1;
+  return i_min <= i_max;
+}
+
+// An output view against an input view: the very same view (in place), or
+// no shared byte.
+bool output_meets_input(View o, View in, int64_t n, uint64_t width) {
+  if (o.p == in.p && o.stride == in.stride) return false;
+  return views_overlap(o, in, n, width);
+}
+
 // Kernel choice by hidden (or as forced) and launch.
 int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
              struct ihipStream_t* stream) {
@@ -107,7 +175,14 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   const int64_t segs = hidden / 8;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (path == ADD_RMSNORM_PATH_WAVE_ROW) {
+  if (path == ADD_RMSNORM_PATH_GENERAL) {
+    const int b = c.block_threads ? c.block_threads : kGeneralThreads;
+    int max_lds = 0;
+    const int rc = device_max_lds(&max_lds);
+    if (rc != ADD_RMSNORM_OK) return rc;
+    if (addrms::general_lds_bytes((int)hidden) > (size_t)max_lds) return ADD_RMSNORM_ERANGE;
+    e = addrms::launch_general(a, b, c.grid_blocks, s);
+  } else if (path == ADD_RMSNORM_PATH_WAVE_ROW) {
     const int b = c.block_threads ? c.block_threads : kWaveRowThreads;
     const int j = pow2_at_least((segs + 63) / 64);
     if (j == 0 || !addrms::wave_row_supported(b, j)) return ADD_RMSNORM_ERANGE;
@@ -129,36 +204,82 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   return ADD_RMSNORM_OK;
 }
 
+// The bf16-out forward over row-strided views (fused when `fused`, else
+// plain RMSNorm with residual and residual_out unused).  Strides in elements.
+int fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residual_out, int64_t ro_stride,
+                const uint16_t* x, int64_t x_stride, const uint16_t* residual, int64_t r_stride,
+                const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                const add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream, bool fused) {
+  add_rmsnorm_launch_cfg c;
+  int rc = check_scalars_any_hidden(n_rows, hidden, eps, cfg, &c);
+  if (rc != ADD_RMSNORM_OK) return rc;
+  if (n_rows == 0) return ADD_RMSNORM_OK;
+
+  if (!out || !x || !weight) return ADD_RMSNORM_EINVAL;
+  if (fused && (!residual_out || !residual)) return ADD_RMSNORM_EINVAL;
+  if (out_stride < hidden || x_stride < hidden) return ADD_RMSNORM_EINVAL;
+  if (fused && (ro_stride < hidden || r_stride < hidden)) return ADD_RMSNORM_EINVAL;
+  if (!aligned(out, 2) || !aligned(x, 2) || !aligned(weight, 2)) return ADD_RMSNORM_EALIGN;
+  if (fused && (!aligned(residual_out, 2) || !aligned(residual, 2))) return ADD_RMSNORM_EALIGN;
+  // Every view's span, (n_rows - 1) * stride + hidden elements, in bytes.
+  const int64_t strides[4] = {out_stride, x_stride, fused ? ro_stride : hidden,
+                              fused ? r_stride : hidden};
+  for (int64_t st : strides)
+    if ((uint64_t)(n_rows - 1) > ((uint64_t)INT64_MAX / 2 - (uint64_t)hidden) / (uint64_t)st)
+      return ADD_RMSNORM_ERANGE;
+
+  const uint64_t width = (uint64_t)hidden * 2;
+  const View vo = {out, (uint64_t)out_stride * 2}, vx = {x, (uint64_t)x_stride * 2};
+  const View vro = {residual_out, (uint64_t)ro_stride * 2}, vr = {residual, (uint64_t)r_stride * 2};
+  // Outputs: disjoint from the weight and from each other; each either
+  // disjoint from an input or exactly that input's view (in place).
+  if (view_meets_range(vo, n_rows, width, weight, width)) return ADD_RMSNORM_EALIAS;
+  if (output_meets_input(vo, vx, n_rows, width)) return ADD_RMSNORM_EALIAS;
+  if (fused) {
+    if (view_meets_range(vro, n_rows, width, weight, width)) return ADD_RMSNORM_EALIAS;
+    if (views_overlap(vo, vro, n_rows, width)) return ADD_RMSNORM_EALIAS;
+    if (output_meets_input(vo, vr, n_rows, width) || output_meets_input(vro, vx, n_rows, width) ||
+        output_meets_input(vro, vr, n_rows, width))
+      return ADD_RMSNORM_EALIAS;
+  }
+
+  // The fast kernels need hidden, every stride and every pointer on 8
+  // elements (16 bytes); anything else takes the general kernel.
+  bool fast = hidden % 8 == 0 && out_stride % 8 == 0 && x_stride % 8 == 0 && aligned16(out) &&
+              aligned16(x) && aligned16(weight);
+  if (fused)
+    fast = fast && ro_stride % 8 == 0 && r_stride % 8 == 0 && aligned16(residual_out) &&
+           aligned16(residual);
+  if (!fast) {
+    if (c.path == ADD_RMSNORM_PATH_AUTO) c.path = ADD_RMSNORM_PATH_GENERAL;
+    if (c.path != ADD_RMSNORM_PATH_GENERAL) return ADD_RMSNORM_EALIGN;
+  }
+  addrms::FwdArgs a = {out, nullptr, nullptr, fused ? residual_out : nullptr, x,
+                       fused ? residual : nullptr, weight, n_rows, (int32_t)hidden, eps,
+                       x_stride, fused ? r_stride : 0, out_stride, fused ? ro_stride : 0};
+  return dispatch(a, c, stream);
+}
+
 }  // namespace
 
 extern "C" {
+
+int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residual_out,
+                            int64_t residual_out_stride, const uint16_t* x, int64_t x_stride,
+                            const uint16_t* residual, int64_t residual_stride,
+                            const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                            const struct add_rmsnorm_launch_cfg* cfg,
+                            struct ihipStream_t* stream) {
+  return fwd_strided(out, out_stride, residual_out, residual_out_stride, x, x_stride, residual,
+                     residual_stride, weight, n_rows, hidden, eps, cfg, stream, true);
+}
 
 int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
                         const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
                         int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
                         struct ihipStream_t* stream) {
-  add_rmsnorm_launch_cfg c;
-  int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
-  if (rc != ADD_RMSNORM_OK) return rc;
-  if (n_rows == 0) return ADD_RMSNORM_OK;
-
-  if (!out || !residual_out || !x || !residual || !weight) return ADD_RMSNORM_EINVAL;
-  if (!aligned16(out) || !aligned16(residual_out) || !aligned16(x) || !aligned16(residual) ||
-      !aligned16(weight))
-    return ADD_RMSNORM_EALIGN;
-  const uint64_t row_bytes = (uint64_t)hidden * 2;
-  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
-  const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
-  // The outputs are disjoint from each other and from the weight; each is
-  // either disjoint from an input or exactly that input (in place).
-  if (overlap(out, t_bytes, residual_out, t_bytes)) return ADD_RMSNORM_EALIAS;
-  if (output_aliases_badly(out, t_bytes, x, residual, weight, row_bytes) ||
-      output_aliases_badly(residual_out, t_bytes, x, residual, weight, row_bytes))
-    return ADD_RMSNORM_EALIAS;
-
-  const addrms::FwdArgs a = {out, nullptr, nullptr, residual_out, x, residual, weight,
-                             n_rows, (int32_t)hidden, eps};
-  return dispatch(a, c, stream);
+  return fwd_strided(out, hidden, residual_out, hidden, x, hidden, residual, hidden, weight,
+                     n_rows, hidden, eps, cfg, stream, true);
 }
 
 int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
@@ -203,7 +324,7 @@ int add_rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, uint16_t* residua
     return ADD_RMSNORM_EALIAS;
 
   const addrms::FwdArgs a = {nullptr, out_q, out_scale, residual_out, x, residual, weight,
-                             n_rows, (int32_t)hidden, eps};
+                             n_rows, (int32_t)hidden, eps, hidden, hidden, hidden, hidden};
   return dispatch(a, c, stream);
 }
 
@@ -215,25 +336,18 @@ int add_rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, uint16_t* residual_ou
                                    hidden, eps, nullptr, stream);
 }
 
+int rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, const uint16_t* x, int64_t x_stride,
+                        const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                        const struct add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream) {
+  return fwd_strided(out, out_stride, nullptr, 0, x, x_stride, nullptr, 0, weight, n_rows, hidden,
+                     eps, cfg, stream, false);
+}
+
 int rmsnorm_fwd_cfg(uint16_t* out, const uint16_t* x, const uint16_t* weight, int64_t n_rows,
                     int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
                     struct ihipStream_t* stream) {
-  add_rmsnorm_launch_cfg c;
-  int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
-  if (rc != ADD_RMSNORM_OK) return rc;
-  if (n_rows == 0) return ADD_RMSNORM_OK;
-
-  if (!out || !x || !weight) return ADD_RMSNORM_EINVAL;
-  if (!aligned16(out) || !aligned16(x) || !aligned16(weight)) return ADD_RMSNORM_EALIGN;
-  const uint64_t row_bytes = (uint64_t)hidden * 2;
-  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
-  const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
-  // out is disjoint from the weight, and disjoint from x or exactly x.
-  if (output_aliases_badly(out, t_bytes, x, x, weight, row_bytes)) return ADD_RMSNORM_EALIAS;
-
-  const addrms::FwdArgs a = {out, nullptr, nullptr, nullptr, x, nullptr, weight,
-                             n_rows, (int32_t)hidden, eps};
-  return dispatch(a, c, stream);
+  return fwd_strided(out, hidden, nullptr, 0, x, hidden, nullptr, 0, weight, n_rows, hidden, eps,
+                     cfg, stream, false);
 }
 
 int rmsnorm_fwd(uint16_t* out, const uint16_t* x, const uint16_t* weight, int64_t n_rows,
@@ -264,7 +378,7 @@ int rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, const uint16_t* x,
     return ADD_RMSNORM_EALIAS;
 
   const addrms::FwdArgs a = {nullptr, out_q, out_scale, nullptr, x, nullptr, weight,
-                             n_rows, (int32_t)hidden, eps};
+                             n_rows, (int32_t)hidden, eps, hidden, 0, hidden, 0};
   return dispatch(a, c, stream);
 }
 
@@ -337,7 +451,9 @@ const char* add_rmsnorm_strerror(int status) {
     case ADD_RMSNORM_EINVAL:
       return "invalid argument (null pointer, negative rows, hidden <= 0, bad eps or launch "
              "configuration)";
-    case ADD_RMSNORM_EALIGN: return "a pointer is misaligned, or hidden % 8 != 0";
+    case ADD_RMSNORM_EALIGN:
+      return "a pointer is misaligned (2 bytes for bf16 data; 16 bytes with hidden % 8 == 0 "
+             "for the quantised entry points and a forced fast path)";
     case ADD_RMSNORM_EALIAS:
       return "an output partly overlaps an input, or overlaps the weight or another output";
     case ADD_RMSNORM_ERANGE: return "hidden (or the problem size) is above what the path supports";

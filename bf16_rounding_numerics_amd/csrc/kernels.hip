@@ -63,6 +63,9 @@ struct Params {
   const u32x4* residual;
   const u32x4* weight;
   int64_t n_rows;
+  // Row strides, in 16-byte segments (the codes of the quantised variant are
+  // always contiguous: C segments of 8 bytes per row).
+  int64_t x_stride, r_stride, out_stride, ro_stride;
   int32_t segs;  // hidden / 8
   float hidden_f;
   float eps;
@@ -76,12 +79,14 @@ struct Params {
 DEV u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 DEV void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
-// Buffer resource over one row of a tensor: offsets stay 32-bit whatever the
-// tensor size, and the hardware range check (reads past num_records return
-// 0) lets a prefetch run without a branch.  A row outside the tensor gets
-// num_records = 0.  The last word selects 32-bit raw data (gfx9 layout).
-DEV __amdgpu_buffer_rsrc_t row_rsrc(const u32x4* t, int64_t row, int segs, bool valid) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(t) + (valid ? row * segs : 0), 0,
+// Buffer resource over one row of a tensor (row `row`, `stride` segments
+// apart, `segs` segments long): offsets stay 32-bit whatever the tensor size,
+// and the hardware range check (reads past num_records return 0) lets a
+// prefetch run without a branch.  An unused tensor gets num_records = 0.  The
+// last word selects 32-bit raw data (gfx9 layout).
+DEV __amdgpu_buffer_rsrc_t row_rsrc(const u32x4* t, int64_t row, int64_t stride, int segs,
+                                    bool valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(t) + (valid ? row * stride : 0), 0,
                                            valid ? segs * 16 : 0, 0x00020000);
 }
 
@@ -298,10 +303,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 
   const int64_t stride = (int64_t)gridDim.x * WAVES;
   for (int64_t row = (int64_t)blockIdx.x * WAVES + wave; row < p.n_rows; row += stride) {
-    const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, C, true);
-    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, C, R);
-    const __amdgpu_buffer_rsrc_t ro = row_rsrc(p.residual_out, row, C, R);
-    const __amdgpu_buffer_rsrc_t oo = row_rsrc(p.out, row, C, !Q);
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, p.x_stride, C, true);
+    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, p.r_stride, C, R);
+    const __amdgpu_buffer_rsrc_t ro = row_rsrc(p.residual_out, row, p.ro_stride, C, R);
+    const __amdgpu_buffer_rsrc_t oo = row_rsrc(p.out, row, p.out_stride, C, !Q);
     u32x4 xq[J], rq[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -378,14 +383,16 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
 
   int parity = 0;
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x, parity ^= 1) {
-    const size_t base = (size_t)row * (size_t)C;
+    const size_t base = (size_t)row * (size_t)C;  // the codes
+    const u32x4* xr = p.x + row * p.x_stride;
+    const u32x4* rr = p.residual + (R ? row * p.r_stride : 0);
     u32x4 xq[J], rq[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int s = t + B * j;
       if (s < C) {
-        xq[j] = load_stream(p.x + base + s);
-        rq[j] = R ? load_stream(p.residual + base + s) : u32x4{0, 0, 0, 0};
+        xq[j] = load_stream(xr + s);
+        rq[j] = R ? load_stream(rr + s) : u32x4{0, 0, 0, 0};
       } else {
         xq[j] = u32x4{0, 0, 0, 0};
         rq[j] = u32x4{0, 0, 0, 0};
@@ -397,7 +404,7 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
     for (int j = 0; j < J; ++j) {
       const int s = t + B * j;
       bs[j] = add_segment<R>(xq[j], rq[j], acc[j]);
-      if (R && s < C) store_stream(p.residual_out + base + s, pack8_rne(acc[j]));
+      if (R && s < C) store_stream(p.residual_out + row * p.ro_stride + s, pack8_rne(acc[j]));
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) bs[j] = wave_block_sum(bs[j]);
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int s = t + B * j;
-        if (s < C) store_stream(p.out + base + s, normalise8(acc[j], rinv, wq[j]));
+        if (s < C) store_stream(p.out + row * p.out_stride + s, normalise8(acc[j], rinv, wq[j]));
       }
     } else {
       float m = 0.0f;
@@ -469,9 +476,9 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
   float4* hi = stage + C;
 
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
-    const size_t base = (size_t)row * (size_t)C;
-    const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, C, true);
-    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, C, R);
+    const size_t base = (size_t)row * (size_t)C;  // the codes
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, p.x_stride, C, true);
+    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, p.r_stride, C, R);
     // Blocks past the row's last chunk are +0.
     for (int i = chunks * W + t; i < NB; i += B) blk[i] = 0.0f;
     for (int c0 = 0; c0 < chunks; c0 += U) {
@@ -489,7 +496,7 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
         float acc[8];
         float bs = add_segment<R>(xq[u], rq[u], acc);
         if (s < C) {
-          if constexpr (R) store_stream(p.residual_out + base + s, pack8_rne(acc));
+          if constexpr (R) store_stream(p.residual_out + row * p.ro_stride + s, pack8_rne(acc));
           lo[s] = make_float4(acc[0], acc[1], acc[2], acc[3]);
           hi[s] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
         if (s < C) {
           const float4 l = lo[s], h = hi[s];
           const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
-          store_stream(p.out + base + s, normalise8(acc, rinv, p.weight[s]));
+          store_stream(p.out + row * p.out_stride + s, normalise8(acc, rinv, p.weight[s]));
         }
       }
     } else {
@@ -543,6 +550,99 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
       }
     }
     __syncthreads();  // blk (and mx) are rewritten by the next row
+  }
+}
+
+// ---------------------------------------------------------------- general shapes
+
+// Any hidden in [1, 32768] and any row strides, 2-byte aligned.  Elements are
+// loaded and stored one by one (16-bit), and the row is cut into the same
+// 8-element segments as everywhere else: the last segment's missing elements
+// are +0, which leaves its fma chain unchanged (fma(0, 0, t) = t for t >= 0),
+// and segments past the row are +0 leaves of the tree.  So the sum of squares,
+// and every result, is the same as the fast kernels give where both apply.
+// Structure of the LDS two-pass kernel: one workgroup of B threads per row;
+// pass 1 stages the fp32 sums in LDS and forms one block sum per wave per
+// chunk of B segments; pass 2 normalises from LDS.
+struct GenParams {
+  uint16_t* out;
+  uint16_t* residual_out;
+  const uint16_t* x;
+  const uint16_t* residual;
+  const uint16_t* weight;
+  int64_t n_rows;
+  int64_t x_stride, r_stride, out_stride, ro_stride;  // elements
+  int32_t hidden;
+  float hidden_f;
+  float eps;
+};
+
+DEV float bf16_at(const uint16_t* p, int j) { return __builtin_bit_cast(float, (uint32_t)p[j] << 16); }
+
+// bf16 of one fp32 value by the same packed conversion as the fast kernels.
+DEV uint16_t bf16_rne1(float v) { return (uint16_t)(pack2_rne(v, v) & 0xFFFFu); }
+
+template <int B, int NB, bool R>
+__global__ __launch_bounds__(B) void k_general(GenParams p) {
+  constexpr int W = B / 64;
+  __shared__ float blk[NB];
+  extern __shared__ float4 stage[];  // [2][C]: elements 0-3, then 4-7, of each segment
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int H = p.hidden;
+  const int C = (H + 7) / 8;
+  const int chunks = (C + B - 1) / B;
+  float4* lo = stage;
+  float4* hi = stage + C;
+
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
+    const uint16_t* xr = p.x + row * p.x_stride;
+    const uint16_t* rr = R ? p.residual + row * p.r_stride : nullptr;
+    uint16_t* ror = R ? p.residual_out + row * p.ro_stride : nullptr;
+    uint16_t* orow = p.out + row * p.out_stride;
+    for (int i = chunks * W + t; i < NB; i += B) blk[i] = 0.0f;
+    for (int c = 0; c < chunks; ++c) {
+      const int s = c * B + t;
+      float acc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = 8 * s + k;
+        float a = 0.0f;
+        if (j < H) {
+          a = bf16_at(xr, j);
+          if constexpr (R) a = a + bf16_at(rr, j);
+        }
+        acc[k] = a;
+      }
+      if (s < C) {
+        if constexpr (R) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (8 * s + k < H) ror[8 * s + k] = bf16_rne1(acc[k]);
+        }
+        lo[s] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        hi[s] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      }
+      const float bs = wave_block_sum(seg_sumsq(acc));
+      if (lane == 0) blk[c * W + wave] = bs;
+    }
+    __syncthreads();
+    const float sumsq = pairwise_tree_lds<NB>(blk);
+    const float rinv = 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
+    for (int c = 0; c < chunks; ++c) {
+      const int s = c * B + t;
+      if (s < C) {
+        const float4 l = lo[s], h = hi[s];
+        const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = 8 * s + k;
+          if (j < H) orow[j] = bf16_rne1((acc[k] * rinv) * bf16_at(p.weight, j));
+        }
+      }
+    }
+    __syncthreads();  // blk and the staged sums are rewritten by the next row
   }
 }
 
@@ -588,6 +688,10 @@ Params make_params(const FwdArgs& a) {
   p.weight = reinterpret_cast<const u32x4*>(a.weight);
   p.n_rows = a.n_rows;
   p.segs = a.hidden / 8;
+  p.x_stride = a.x_stride / 8;
+  p.r_stride = a.r_stride / 8;
+  p.out_stride = a.out_stride / 8;
+  p.ro_stride = a.ro_stride / 8;
   p.hidden_f = (float)a.hidden;
   p.eps = a.eps;
   return p;
@@ -722,6 +826,33 @@ hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, h
 
 // ---------------------------------------------------------------- internal API
 
+template <bool R, int B>
+hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t s) {
+  const size_t lds = (size_t)((hidden + 7) / 8) * 32;
+  if (two_pass_nb(hidden) == 32) {
+    auto k = k_general<B, 32, R>;
+    if (grid == -1) grid = resident(k, B, lds);
+    hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
+  } else {
+    auto k = k_general<B, 64, R>;
+    if (grid == -1) grid = resident(k, B, lds);
+    hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <bool R>
+hipError_t general_by_block(const GenParams& p, int b, int hidden, int64_t grid, hipStream_t s) {
+  switch (b) {
+    case 64: return go_general<R, 64>(p, hidden, grid, s);
+    case 128: return go_general<R, 128>(p, hidden, grid, s);
+    case 256: return go_general<R, 256>(p, hidden, grid, s);
+    case 512: return go_general<R, 512>(p, hidden, grid, s);
+    case 1024: return go_general<R, 1024>(p, hidden, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 // The variant is chosen by which outputs and inputs are set: quantised when
 // codes are requested, plain when there is no residual.
 hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
@@ -767,6 +898,30 @@ bool wg_row_supported(int block_threads, int segs_per_thread) {
 
 size_t lds_two_pass_lds_bytes(int hidden) {
   return (size_t)(hidden / 8) * 32 + (size_t)two_pass_nb(hidden) * sizeof(float) + 64;
+}
+
+hipError_t launch_general(const FwdArgs& a, int block_threads, int64_t grid_blocks,
+                          hipStream_t s) {
+  GenParams p;
+  p.out = a.out;
+  p.residual_out = a.residual_out;
+  p.x = a.x;
+  p.residual = a.residual;
+  p.weight = a.weight;
+  p.n_rows = a.n_rows;
+  p.x_stride = a.x_stride;
+  p.r_stride = a.r_stride;
+  p.out_stride = a.out_stride;
+  p.ro_stride = a.ro_stride;
+  p.hidden = a.hidden;
+  p.hidden_f = (float)a.hidden;
+  p.eps = a.eps;
+  return a.residual ? general_by_block<true>(p, block_threads, a.hidden, grid_blocks, s)
+                    : general_by_block<false>(p, block_threads, a.hidden, grid_blocks, s);
+}
+
+size_t general_lds_bytes(int hidden) {
+  return (size_t)((hidden + 7) / 8) * 32 + (size_t)two_pass_nb(hidden) * 4 + 64;
 }
 
 hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,

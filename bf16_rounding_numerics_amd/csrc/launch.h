@@ -16,8 +16,12 @@ struct FwdArgs {
   const uint16_t* residual;  // null for plain RMSNorm (acc = x, no residual_out)
   const uint16_t* weight;
   int64_t n_rows;
-  int32_t hidden;  // multiple of 8
+  int32_t hidden;
   float eps;
+  // Row strides in elements (>= hidden).  The three fast kernels need hidden,
+  // the strides and every pointer aligned to 8 elements (16 bytes); the
+  // general kernel takes any hidden and any 2-byte aligned layout.
+  int64_t x_stride, r_stride, out_stride, ro_stride;
 };
 
 // Largest number of 8-element segments any row can have.
@@ -43,6 +47,13 @@ hipError_t launch_wg_row(const FwdArgs& a, int block_threads, int segs_per_threa
 hipError_t launch_lds_two_pass(const FwdArgs& a, int block_threads, int64_t grid_blocks,
                                hipStream_t stream);
 size_t lds_two_pass_lds_bytes(int hidden);
+
+// Any hidden in [1, 32768], any row strides, 2-byte aligned pointers
+// (bf16 out only): element-wise loads and stores, the same reduction tree.
+// general_lds_bytes() gives its LDS size.
+hipError_t launch_general(const FwdArgs& a, int block_threads, int64_t grid_blocks,
+                          hipStream_t stream);
+size_t general_lds_bytes(int hidden);
 
 // Which (workgroup size, segments per thread) pairs are built: those whose
 // per-thread row share fits the register file without spilling.

@@ -24,10 +24,11 @@
  * real value.
  *
  * Conventions shared by every entry point below:
- *   - Tensors are raw bf16 bit patterns (uint16_t), row-major and contiguous:
- *     x, residual, out, residual_out are [n_rows, hidden], weight is [hidden].
+ *   - Tensors are raw bf16 bit patterns (uint16_t), row-major: x, residual,
+ *     out, residual_out are [n_rows, hidden] (contiguous, or with row strides
+ *     for the *_strided entry points), weight is [hidden].
  *   - All tensor pointers are DEVICE pointers (HIP device memory, or memory
- *     the device can address), 16-byte aligned.  The caller owns them; the
+ *     the device can address).  The caller owns them; the
  *     library never allocates, frees or synchronises, keeps no state between
  *     calls, and is safe to call from several host threads.
  *   - Work is enqueued on `stream` (NULL = the null stream) and the call
@@ -48,7 +49,7 @@ extern "C" {
 /* hipStream_t is a pointer to this opaque struct. */
 struct ihipStream_t;
 
-#define ADD_RMSNORM_ABI_VERSION 3
+#define ADD_RMSNORM_ABI_VERSION 4
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768
@@ -56,7 +57,7 @@ struct ihipStream_t;
 /* Status codes. */
 #define ADD_RMSNORM_OK 0
 #define ADD_RMSNORM_EINVAL (-1) /* null pointer, n_rows < 0, hidden <= 0, eps < 0 or not finite, bad cfg */
-#define ADD_RMSNORM_EALIGN (-2) /* a pointer misaligned (16 bytes; 4 for scales), or hidden % 8 != 0 */
+#define ADD_RMSNORM_EALIGN (-2) /* a pointer misaligned (see each entry point), or a forced fast path on a shape it cannot take */
 #define ADD_RMSNORM_EALIAS (-3) /* an output partly overlaps an input, or overlaps the weight or another output */
 #define ADD_RMSNORM_ERANGE (-4) /* hidden above the maximum (of the library, the chosen path or the device) */
 #define ADD_RMSNORM_EHIP (-5)   /* the HIP launch failed; add_rmsnorm_last_hip_error() has the detail */
@@ -68,13 +69,17 @@ struct ihipStream_t;
  *   x, residual   [n_rows, hidden] bf16, read.
  *   weight        [hidden] bf16, read.
  *   n_rows >= 0 (0 enqueues nothing and returns OK; pointers are not checked),
- *   8 <= hidden <= ADD_RMSNORM_MAX_HIDDEN with hidden % 8 == 0,
+ *   1 <= hidden <= ADD_RMSNORM_MAX_HIDDEN,
  *   eps finite and >= 0, added to the mean of squares inside the square root.
+ * Pointers need only 2-byte alignment.  When hidden % 8 == 0 and every
+ * pointer is 16-byte aligned one of the three fast kernels below runs;
+ * otherwise the general kernel (element-wise loads and stores, the same
+ * reduction tree, so the same results).
  * In place: an output may be the very same buffer as x or residual (e.g.
  * out == x and residual_out == residual, the usual residual-stream update);
  * any other overlap of an output with an input, the weight or the other
  * output is rejected with ADD_RMSNORM_EALIAS.
- * The kernel is chosen by hidden: one wavefront per row up to 2048, one
+ * The fast kernel is chosen by hidden: one wavefront per row up to 2048, one
  * workgroup per row with the row held in registers up to 8192, and above
  * that one workgroup per row that stages the row's fp32 sums in LDS and
  * normalises in a second pass over LDS.
@@ -84,11 +89,32 @@ int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
                     const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
                     int64_t hidden, float eps, struct ihipStream_t* stream);
 
+/*
+ * The fused forward over row-strided views, for rows that are slices of wider
+ * matrices.  Row i of each tensor starts `*_stride` elements after row i - 1
+ * (strides >= hidden, in elements; the weight stays contiguous).  Results are
+ * those of add_rmsnorm_fwd on the same rows.  The fast kernels run when
+ * hidden, every stride and every pointer are multiples of 8 elements (16
+ * bytes), the general kernel otherwise.  An output may be exactly an input's
+ * view (same pointer and stride: in place); any other shared element between
+ * an output and an input, the other output or the weight is
+ * ADD_RMSNORM_EALIAS.  Views with equal strides are tested element by element
+ * (so interleaved column blocks of one matrix are fine); views with unequal
+ * strides must not share any byte of their spans.  cfg may be NULL.
+ */
+int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residual_out,
+                            int64_t residual_out_stride, const uint16_t* x, int64_t x_stride,
+                            const uint16_t* residual, int64_t residual_stride,
+                            const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                            const struct add_rmsnorm_launch_cfg* cfg,
+                            struct ihipStream_t* stream);
+
 /* Kernel paths for add_rmsnorm_fwd_cfg. */
 #define ADD_RMSNORM_PATH_AUTO 0
 #define ADD_RMSNORM_PATH_WAVE_ROW 1     /* hidden <= 4096 (2048 with 1024 threads) when forced */
 #define ADD_RMSNORM_PATH_WG_ROW 2       /* hidden <= min(64 * block_threads, 16384) when forced */
 #define ADD_RMSNORM_PATH_LDS_TWO_PASS 3 /* any supported hidden */
+#define ADD_RMSNORM_PATH_GENERAL 4      /* any hidden, strides and 2-byte alignment (bf16 out only) */
 
 /*
  * Launch configuration, for tests and benchmarks that must show that results
@@ -113,8 +139,10 @@ struct add_rmsnorm_launch_cfg {
  * add_rmsnorm_fwd with an explicit launch configuration (cfg may be NULL,
  * meaning all defaults).  Same arguments, results and errors as
  * add_rmsnorm_fwd; a configuration the chosen path cannot run returns
- * ADD_RMSNORM_EINVAL (bad field) or ADD_RMSNORM_ERANGE (hidden too large for
- * that path).  The numerical result is the same for every configuration.
+ * ADD_RMSNORM_EINVAL (bad field), ADD_RMSNORM_ERANGE (hidden too large for
+ * that path) or ADD_RMSNORM_EALIGN (a fast path forced on a shape or
+ * alignment only the general path takes).  The numerical result is the same
+ * for every configuration, the general path included.
  */
 int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
                         const uint16_t* residual, const uint16_t* weight, int64_t n_rows,
@@ -140,7 +168,9 @@ int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x
  *   out_q      [n_rows, hidden] int8, written, 16-byte aligned.
  *   out_scale  [n_rows] fp32, written, 4-byte aligned.
  * Codes and scales must not overlap any other buffer (ADD_RMSNORM_EALIAS).
- * Everything else (sizes, alignment, errors, stream) as add_rmsnorm_fwd.
+ * Unlike add_rmsnorm_fwd, the quantised entry points need hidden % 8 == 0
+ * and 16-byte aligned rows (ADD_RMSNORM_EALIGN otherwise) and take no general
+ * path; everything else (sizes, errors, stream) as add_rmsnorm_fwd.
  */
 int add_rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, uint16_t* residual_out,
                           const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
@@ -174,11 +204,18 @@ int rmsnorm_fwd_cfg(uint16_t* out, const uint16_t* x, const uint16_t* weight, in
                     int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
                     struct ihipStream_t* stream);
 
+/* rmsnorm_fwd over row-strided views, as add_rmsnorm_fwd_strided (out may
+ * be exactly x's view). */
+int rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, const uint16_t* x, int64_t x_stride,
+                        const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                        const struct add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream);
+
 /*
  * Plain RMSNorm with int8 out: rmsnorm_fwd's row computation followed by the
  * per-row quantisation of add_rmsnorm_quant_fwd (same scale, inverse scale,
  * rounding and zero-code rule).  Codes and scales must not overlap x, the
- * weight or each other (ADD_RMSNORM_EALIAS).
+ * weight or each other (ADD_RMSNORM_EALIAS).  Like add_rmsnorm_quant_fwd it
+ * needs hidden % 8 == 0 and 16-byte aligned x and weight.
  *   out_q      [n_rows, hidden] int8, written, 16-byte aligned.
  *   out_scale  [n_rows] fp32, written, 4-byte aligned.
  */

@@ -6,7 +6,9 @@
  * the library documents for its kernels, so that a GPU result can be checked
  * bit for bit rather than to within one bf16 ULP:
  *   acc_j      = fl32(x_j + r_j)
- *   segment s  = elements 8s .. 8s+7:  t = acc0*acc0, then t = fmaf(acck, acck, t)
+ *   segment s  = elements 8s .. 8s+7:  t = acc0*acc0, then t = fmaf(acck, acck, t);
+ *                the last segment of a row whose hidden is not a multiple of 8
+ *                is padded with +0 (which leaves the chain unchanged)
  *   S          = balanced pairwise sum of the segment sums in index order,
  *                padded with +0 to a power of two
  *   rinv       = 1 / sqrtf(S / hidden + eps)     (correctly rounded / and sqrt)
@@ -48,7 +50,7 @@ static uint16_t round_bf16(float f) {
  */
 static float row_rinv(float* acc, float* seg, int64_t padded, uint16_t* ro, const uint16_t* xr,
                       const uint16_t* rr, int64_t hidden, float eps, float* sumsq) {
-  const int64_t segs = hidden / 8;
+  const int64_t segs = (hidden + 7) / 8;
   for (int64_t j = 0; j < hidden; ++j) {
     acc[j] = f32_of((uint32_t)xr[j] << 16);
     if (rr) acc[j] = acc[j] + f32_of((uint32_t)rr[j] << 16);
@@ -59,7 +61,8 @@ static float row_rinv(float* acc, float* seg, int64_t padded, uint16_t* ro, cons
       seg[s] = 0.0f;
       continue;
     }
-    const float* a = acc + 8 * s;
+    float a[8];
+    for (int k = 0; k < 8; ++k) a[k] = 8 * s + k < hidden ? acc[8 * s + k] : 0.0f;
     float t = a[0] * a[0];
     for (int k = 1; k < 8; ++k) t = fmaf(a[k], a[k], t);
     seg[s] = t;
@@ -73,13 +76,13 @@ static float row_rinv(float* acc, float* seg, int64_t padded, uint16_t* ro, cons
   return 1.0f / sqrtf(v);
 }
 
-/* Returns 0, or -1 on bad arguments (hidden not a positive multiple of 8). */
+/* Returns 0, or -1 on bad arguments. */
 int model_add_rmsnorm(uint16_t* out, uint16_t* residual_out, float* sumsq_out,
                       const uint16_t* x, const uint16_t* r, const uint16_t* w, int64_t n_rows,
                       int64_t hidden, float eps) {
-  if (hidden <= 0 || hidden % 8 || !r != !residual_out) return -1;
+  if (hidden <= 0 || !r != !residual_out) return -1;
   int64_t padded = 1;
-  while (padded < hidden / 8) padded *= 2;
+  while (padded < (hidden + 7) / 8) padded *= 2;
   float* seg = (float*)malloc(sizeof(float) * (size_t)padded);
   float* acc = (float*)malloc(sizeof(float) * (size_t)hidden);
   if (!seg || !acc) {
@@ -118,9 +121,9 @@ static float max_nan(float m, float v) {
 int model_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, const uint16_t* x,
                             const uint16_t* r, const uint16_t* w, int64_t n_rows, int64_t hidden,
                             float eps) {
-  if (hidden <= 0 || hidden % 8 || !r != !residual_out) return -1;
+  if (hidden <= 0 || !r != !residual_out) return -1;
   int64_t padded = 1;
-  while (padded < hidden / 8) padded *= 2;
+  while (padded < (hidden + 7) / 8) padded *= 2;
   float* seg = (float*)malloc(sizeof(float) * (size_t)padded);
   float* acc = (float*)malloc(sizeof(float) * (size_t)hidden);
   if (!seg || !acc) {

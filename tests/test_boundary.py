@@ -98,16 +98,17 @@ def call(out=A, res=A + MB, x=A + 2 * MB, r=A + 3 * MB, w=A + 4 * MB, n=4, h=64,
     (dict(eps=-1.0), arn.EINVAL),
     (dict(eps=math.nan), arn.EINVAL),
     (dict(eps=math.inf), arn.EINVAL),
-    (dict(h=12), arn.EALIGN),
-    (dict(h=4), arn.EALIGN),
+    (dict(h=12, cfg=(arn.PATH_WG_ROW, 0, 0, 0)), arn.EALIGN),   # a fast path forced on
+    (dict(h=4, cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)), arn.EALIGN),  # what only the general takes
     (dict(h=32776), arn.ERANGE),
     (dict(out=0), arn.EINVAL),
     (dict(res=0), arn.EINVAL),
     (dict(x=0), arn.EINVAL),
     (dict(r=0), arn.EINVAL),
     (dict(w=0), arn.EINVAL),
-    (dict(x=A + 2 * MB + 8), arn.EALIGN),
-    (dict(w=A + 4 * MB + 2), arn.EALIGN),
+    (dict(x=A + 2 * MB + 1), arn.EALIGN),               # odd address
+    (dict(w=A + 4 * MB + 1), arn.EALIGN),
+    (dict(x=A + 2 * MB + 8, cfg=(arn.PATH_LDS_TWO_PASS, 0, 0, 0)), arn.EALIGN),
     (dict(out=A + 2 * MB + 16), arn.EALIAS),            # out partly overlaps x
     (dict(res=A + 3 * MB - 16), arn.EALIAS),            # residual_out partly overlaps residual
     (dict(res=A + 4 * 64 * 2 - 16), arn.EALIAS),        # residual_out overlaps out's tail
@@ -156,6 +157,7 @@ def test_exact_in_place_aliases_pass_validation(kw):
 @pytest.mark.parametrize("cfg,status", [
     ((0, 0, 0, 1), arn.EINVAL),                 # flags must be 0
     ((9, 0, 0, 0), arn.EINVAL),                 # unknown path
+    ((5, 0, 0, 0), arn.EINVAL),
     ((-1, 0, 0, 0), arn.EINVAL),
     ((0, 100, 0, 0), arn.EINVAL),               # not a supported workgroup size
     ((0, 2048, 0, 0), arn.EINVAL),
@@ -247,12 +249,13 @@ def pqcall(q=A + 5 * MB, sc=A + 6 * MB, x=A + 2 * MB, w=A + 4 * MB, n=4, h=64, e
     (dict(n=-1), arn.EINVAL),
     (dict(h=0), arn.EINVAL),
     (dict(eps=-1.0), arn.EINVAL),
-    (dict(h=12), arn.EALIGN),
+    (dict(h=12, cfg=(arn.PATH_WG_ROW, 0, 0, 0)), arn.EALIGN),
     (dict(h=32776), arn.ERANGE),
     (dict(out=0), arn.EINVAL),
     (dict(x=0), arn.EINVAL),
     (dict(w=0), arn.EINVAL),
-    (dict(out=A + 8), arn.EALIGN),
+    (dict(out=A + 1), arn.EALIGN),
+    (dict(out=A + 8, cfg=(arn.PATH_WG_ROW, 0, 0, 0)), arn.EALIGN),
     (dict(out=A + 2 * MB + 16), arn.EALIAS),            # out partly overlaps x
     (dict(out=A + 4 * MB - 16), arn.EALIAS),            # out's tail on the weight
     (dict(n=1 << 62, h=8), arn.ERANGE),
@@ -369,3 +372,83 @@ def test_log1p_binding_refuses_cpu_tensors():
     x = torch.zeros(16, dtype=torch.float32)
     with pytest.raises(ValueError):
         arn.log1p_f32(torch.empty_like(x), x)
+
+
+# ---------------------------------------------------------------- strided views
+
+def scall(out=A, so=None, res=A + MB, sro=None, x=A + 2 * MB, sx=None, r=A + 3 * MB, sr=None,
+          w=A + 4 * MB, n=4, h=4104, eps=1e-6, cfg=(1, 0, 0, 0)):
+    """add_rmsnorm_fwd_strided with fake addresses.  The default forced path
+    (one wavefront per row) cannot take hidden 4104: a call that passes every
+    argument and alias check returns ERANGE, or EALIGN when only the general
+    kernel could take the layout; nothing is launched."""
+    L = arn.lib()
+    st = [v if v is not None else h for v in (so, sro, sx, sr)]
+    c = arn.LaunchCfg(*cfg)
+    return L.add_rmsnorm_fwd_strided(out, st[0], res, st[1], x, st[2], r, st[3], w, n, h, eps,
+                                     ctypes.byref(c), None)
+
+
+PASSED = (arn.ERANGE, arn.EALIGN)
+
+
+@fake_addresses
+def test_strided_argument_errors():
+    assert scall(so=4103) == arn.EINVAL                 # stride below hidden
+    assert scall(sx=100) == arn.EINVAL
+    assert scall(out=A + 1) == arn.EALIGN
+    assert scall(n=1 << 40, sx=1 << 30) == arn.ERANGE   # span overflows
+    assert scall(out=0) == arn.EINVAL
+    assert scall(n=0, out=0, res=0, x=0, r=0, w=0, cfg=(0, 0, 0, 0)) == arn.OK
+    L = arn.lib()
+    c = arn.LaunchCfg(1, 0, 0, 0)
+    assert L.rmsnorm_fwd_strided(A, 4100, A + MB, 4104, A + 4 * MB, 4, 4104, 1e-6,
+                                 ctypes.byref(c), None) == arn.EINVAL
+
+
+@fake_addresses
+def test_strided_column_blocks_of_one_matrix():
+    h, ld = 4104, 3 * 4104
+    # x, residual, out as three interleaved column blocks of one [4, 3h] matrix
+    base = A
+    assert scall(x=base, sx=ld, r=base + 2 * h, sr=ld, out=base + 4 * h, so=ld) in PASSED
+    # out shifted half a row width into x's columns: shares elements
+    assert scall(x=base, sx=ld, r=base + 4 * h, sr=ld, out=base + h, so=ld) == arn.EALIAS
+    # in place on a strided view
+    assert scall(x=base, sx=ld, out=base, so=ld, r=base + 2 * h, sr=ld) in PASSED
+    # same base, other stride: not the same view
+    assert scall(x=base, sx=ld, out=base, so=ld + 8, r=base + 2 * h, sr=ld) == arn.EALIAS
+    # the weight inside the gap between out's rows, then on one of them
+    assert scall(out=base, so=ld, w=base + 2 * h + 64) in PASSED
+    assert scall(out=base, so=ld, w=base + 2 * ld + 64) == arn.EALIAS
+
+
+def _bytes_of(base, stride, n, h):
+    return {base + 2 * (i * stride) + k for i in range(n) for k in range(2 * h)}
+
+
+@fake_addresses
+def test_strided_alias_check_against_brute_force():
+    import random
+
+    rnd = random.Random(5)
+    h = 4104
+    for _ in range(200):
+        n = rnd.choice([1, 2, 3, 5])
+        s_out = h + rnd.choice([0, 8, 1000, 4104, 5000])
+        s_x = s_out if rnd.random() < 0.7 else h + rnd.choice([0, 16, 3000])
+        out = A + 2 * rnd.randrange(0, 4 * h)
+        x = A + 2 * rnd.randrange(0, 4 * h)
+        got = scall(out=out, so=s_out, x=x, sx=s_x, res=A + 6 * MB, r=A + 8 * MB, n=n)
+        shared = bool(_bytes_of(out, s_out, n, h) & _bytes_of(x, s_x, n, h))
+        if out == x and s_out == s_x:
+            expect_alias = False                              # in place
+        elif s_out == s_x:
+            expect_alias = shared                             # exact, element by element
+        else:
+            lo_o, hi_o = out, out + 2 * ((n - 1) * s_out + h)
+            lo_x, hi_x = x, x + 2 * ((n - 1) * s_x + h)
+            expect_alias = lo_o < hi_x and lo_x < hi_o        # spans
+        assert (got == arn.EALIAS) == expect_alias, (n, s_out, s_x, out - A, x - A, got)
+        if not expect_alias:
+            assert got in PASSED

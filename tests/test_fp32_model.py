@@ -142,3 +142,24 @@ def test_plain_model_agrees_with_the_oracle(n, h):
     assert np.allclose(ms, os_, rtol=2e-6, atol=0)
     dq = np.abs(mq.astype(np.int32) - oq.astype(np.int32))
     assert dq.max() <= 1 and (dq > 0).mean() < 1e-3
+
+
+@pytest.mark.parametrize("h", [1, 3, 7, 9, 15, 100, 1001, 4095, 8193])
+def test_model_with_a_partial_last_segment_agrees_with_the_oracle(h):
+    x, r, w = synth.workload(900 + h, 6, h)
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
+    o_out, o_res = oracle.add_rmsnorm(x, r, w, 1e-6)
+    assert np.array_equal(m_res, o_res)
+    assert ulp_distance(m_out, o_out).max() <= 1
+    p_out, _ = fp32_model.add_rmsnorm(x, None, w, 1e-6)
+    assert ulp_distance(p_out, oracle.rmsnorm(x, w, 1e-6)).max() <= 1
+
+
+def test_partial_segment_is_zero_padding():
+    # hidden 13 equals hidden 16 with three zero columns (weights irrelevant there)
+    x, r, w = synth.workload(950, 5, 16)
+    x[:, 13:] = 0
+    r[:, 13:] = 0
+    full, _, s16 = fp32_model.add_rmsnorm(x, r, w, 1e-6, want_sumsq=True)
+    part, _, s13 = fp32_model.add_rmsnorm(x[:, :13], r[:, :13], w[:13], 1e-6, want_sumsq=True)
+    assert np.array_equal(s16.view(np.uint32), s13.view(np.uint32))

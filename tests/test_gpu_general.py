@@ -1,0 +1,194 @@
+"""General shapes on the GPU: any hidden, unaligned pointers, row-strided views.
+
+Bars, as for the contiguous fast kernels:
+  * bit-exact against the fp32 model (which pads a partial last segment with
+    zeros, the canonical tree's own padding), within one bf16 ULP of the
+    oracle with residual_out bit-exact;
+  * the general kernel gives the fast kernels' bits where both apply, for
+    every workgroup size and grid;
+  * strided views give the contiguous results on the same rows and write
+    nothing outside their rows.
+"""
+import numpy as np
+import pytest
+
+import bf16_rounding_numerics_amd as arn
+import fp32_model
+import synth
+from gpu_helpers import (POISON, announce, check_parity, from_dev, gpu_fwd, is_nan16,
+                         poisoned_like, require_gpu, to_dev, ulp_distance)
+from test_gpu_parity import _special_rows
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS = (64, 128, 256, 512, 1024)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def same16(a, b):
+    return np.array_equal(a, b) or not ((a != b) & ~(is_nan16(a) & is_nan16(b))).any()
+
+
+def check_model(x, r, w, eps, out, res, label):
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, eps)
+    assert same16(out, m_out), "%s: out differs from the fp32 model in %d" % (
+        label, int(((out != m_out) & ~(is_nan16(out) & is_nan16(m_out))).sum()))
+    if r is not None:
+        assert same16(res, m_res), "%s: residual_out differs from the fp32 model" % label
+
+
+def gpu_plain(x, w, eps=1e-6, path=0, block=0, grid=0):
+    import torch
+
+    xd, wd = to_dev(x), to_dev(w)
+    out = poisoned_like(xd)
+    arn.rmsnorm_fwd_cfg(out, xd, wd, eps, path=path, block_threads=block, grid_blocks=grid)
+    torch.cuda.synchronize()
+    return from_dev(out)
+
+
+HIDDEN = [1, 3, 7, 9, 15, 100, 1001, 2049, 4095, 4097, 8191, 12289, 16385, 24577, 32767]
+
+
+@pytest.mark.parametrize("h", HIDDEN)
+def test_any_hidden(h):
+    n = 37 if h < 8192 else 9
+    announce("general hidden %d, %d rows" % (h, n))
+    x, r, w = synth.workload(5200 + h, n, h)
+    out, res = gpu_fwd(x, r, w, 1e-6)
+    check_model(x, r, w, 1e-6, out, res, "h=%d" % h)
+    check_parity(x, r, w, 1e-6, out, res, label="h=%d" % h)
+    p = gpu_plain(x, w)
+    check_model(x, None, w, 1e-6, p, None, "plain h=%d" % h)
+
+
+@pytest.mark.parametrize("h", [9, 1001, 16385])
+def test_any_hidden_special_values(h):
+    announce("general special values hidden %d" % h)
+    x, r = _special_rows(h)
+    w = synth.bf16_normal(5300 + h, 2, (h,), 1.0, 0.5)
+    out, res = gpu_fwd(x, r, w, 1e-6)
+    check_model(x, r, w, 1e-6, out, res, "special h=%d" % h)
+    p = gpu_plain(x, w)
+    check_model(x, None, w, 1e-6, p, None, "plain special h=%d" % h)
+
+
+@pytest.mark.parametrize("h", [64, 1000, 2048, 4096, 8192, 16384, 32768])
+def test_general_path_gives_the_fast_kernels_bits(h):
+    import torch
+
+    n = 19
+    x, r, w = synth.workload(5400 + h, n, h)
+    announce("general vs fast, hidden %d" % h)
+    ref_out, ref_res = gpu_fwd(x, r, w, 1e-6)
+    ref_plain = gpu_plain(x, w)
+    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    for b in BLOCKS:
+        for grid in (0, 7, -1):
+            out, res = gpu_fwd(x, r, w, 1e-6, path=arn.PATH_GENERAL, block=b, grid=grid,
+                               xd=xd, rd=rd, wd=wd)
+            assert np.array_equal(out, ref_out) and np.array_equal(res, ref_res), (b, grid)
+            o = poisoned_like(xd)
+            arn.rmsnorm_fwd_cfg(o, xd, wd, 1e-6, path=arn.PATH_GENERAL, block_threads=b,
+                                grid_blocks=grid)
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(o), ref_plain), (b, grid)
+
+
+def test_unaligned_pointers_take_the_general_kernel():
+    import torch
+
+    n, h = 24, 4096
+    x, r, w = synth.workload(5500, n, h)
+    announce("general: pointers offset by one element")
+    ref_out, ref_res = gpu_fwd(x, r, w, 1e-6)
+    # each tensor one element past a 16-byte boundary
+    def shifted(a):
+        buf = torch.empty(a.size + 8, dtype=torch.int16, device="cuda:0")
+        view = buf[1:1 + a.size]
+        view.copy_(to_dev(a.reshape(-1)))
+        return view.view(a.shape) if a.ndim > 1 else view
+
+    xd, rd, wd = shifted(x), shifted(r), shifted(w)
+    ob = torch.full((n * h + 8,), np.int16(np.uint16(POISON).view(np.int16)), dtype=torch.int16,
+                    device="cuda:0")
+    rb = ob.clone()
+    out, res = ob[1:1 + n * h].view(n, h), rb[1:1 + n * h].view(n, h)
+    arn.add_rmsnorm_fwd(out, res, xd, rd, wd, 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), ref_out) and np.array_equal(from_dev(res), ref_res)
+    assert from_dev(ob)[0] == POISON and (from_dev(ob)[1 + n * h:] == POISON).all()
+
+
+def _matrix(rows, cols, fill=POISON):
+    import torch
+
+    return torch.full((rows, cols), np.int16(np.uint16(fill).view(np.int16)), dtype=torch.int16,
+                      device="cuda:0")
+
+
+@pytest.mark.parametrize("h,ld,offs", [
+    (4096, 3 * 4096, (0, 4096, 8192)),        # column blocks, fast-kernel aligned
+    (1024, 1024 + 8, (0, 0, 0)),              # padded rows, aligned
+    (2048, 5001, (8, 16, 24)),                # a stride not a multiple of 8: general
+    (1000, 3001, (1, 1001, 2001)),            # odd strides and offsets: general
+    (16384, 16384 * 2, (0, 16384, 0)),        # two-pass kernel on strided rows
+])
+def test_strided_views(h, ld, offs):
+    import torch
+
+    n = 17
+    announce("strided views: hidden %d, row stride %d, column offsets %s" % (h, ld, offs))
+    x, r, w = synth.workload(5600 + h, n, h)
+    ref_out, ref_res = gpu_fwd(x, r, w, 1e-6)
+    ox, orr, oo = offs
+    X = _matrix(n, ld)                       # x lives in X, residual in R
+    R = _matrix(n, ld)
+    X[:, ox:ox + h] = to_dev(x)
+    R[:, orr:orr + h] = to_dev(r)
+    O = _matrix(n, ld)                       # out and residual_out, poisoned around
+    RO = _matrix(n, ld + 16)
+    wd = to_dev(w)
+    out, res = O[:, oo:oo + h], RO[:, 16:16 + h]
+    arn.add_rmsnorm_fwd_strided(out, res, X[:, ox:ox + h], R[:, orr:orr + h], wd, 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), ref_out)
+    assert np.array_equal(from_dev(res), ref_res)
+    Oh, ROh = from_dev(O), from_dev(RO)
+    mask = np.ones_like(Oh, bool)
+    mask[:, oo:oo + h] = False
+    assert (Oh[mask] == POISON).all(), "out wrote outside its rows"
+    mask = np.ones_like(ROh, bool)
+    mask[:, 16:16 + h] = False
+    assert (ROh[mask] == POISON).all(), "residual_out wrote outside its rows"
+    # plain RMSNorm on the same strided x
+    ref_plain = gpu_plain(x, w)
+    P = _matrix(n, ld)
+    arn.rmsnorm_fwd_strided(P[:, oo:oo + h], X[:, ox:ox + h], wd, 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(P[:, oo:oo + h]), ref_plain)
+
+
+@pytest.mark.parametrize("h,ld", [(4096, 8192), (1001, 2003)])
+def test_strided_in_place(h, ld):
+    """out = x and residual_out = residual on strided views (residual stream
+    update inside wider buffers)."""
+    import torch
+
+    n = 11
+    announce("strided in place: hidden %d, row stride %d" % (h, ld))
+    x, r, w = synth.workload(5700 + h, n, h)
+    ref_out, ref_res = gpu_fwd(x, r, w, 1e-6)
+    B = _matrix(n, ld)
+    B[:, :h] = to_dev(x)
+    B[:, ld - h:] = to_dev(r)
+    xv, rv = B[:, :h], B[:, ld - h:]
+    arn.add_rmsnorm_fwd_strided(xv, rv, xv, rv, to_dev(w), 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(xv), ref_out) and np.array_equal(from_dev(rv), ref_res)
+    if ld - h > h:
+        assert (from_dev(B)[:, h:ld - h] == POISON).all()
