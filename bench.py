@@ -37,9 +37,10 @@ PEAK_HBM_GBPS = 8000.0
 CACHE_DEFEAT_BYTES = 1 << 30  # rotate buffer sets until the footprint is >= 1 GiB
 
 
-OPS = ("bf16", "quant", "plain", "plain_quant", "log1p")
+OPS = ("bf16", "quant", "plain", "plain_quant", "general", "log1p")
 ENTRY = {"bf16": "add_rmsnorm_fwd", "quant": "add_rmsnorm_quant_fwd", "plain": "rmsnorm_fwd",
-         "plain_quant": "rmsnorm_quant_fwd", "log1p": "log1p_f32"}
+         "plain_quant": "rmsnorm_quant_fwd", "general": "add_rmsnorm_fwd (general kernel)",
+         "log1p": "log1p_f32"}
 
 
 def algorithmic_bytes(n_rows: int, hidden: int, op: str = "bf16") -> int:
@@ -48,7 +49,7 @@ def algorithmic_bytes(n_rows: int, hidden: int, op: str = "bf16") -> int:
     for the quantised variants 1 byte of code per element and a 4-byte scale
     per row); the weight read once.  Plain RMSNorm has no residual and no
     residual_out."""
-    per_elem = {"bf16": 8, "quant": 7, "plain": 4, "plain_quant": 3}[op]
+    per_elem = {"bf16": 8, "general": 8, "quant": 7, "plain": 4, "plain_quant": 3}[op]
     per_row = 4 if op in ("quant", "plain_quant") else 0
     return per_elem * n_rows * hidden + per_row * n_rows + 2 * hidden
 
@@ -62,6 +63,8 @@ def parse_args(argv=None):
     p.add_argument("--op", choices=OPS, default="bf16",
                    help="bf16: the fused op (the benchmark); quant: its int8-quantised "
                         "variant; plain, plain_quant: RMSNorm without the residual add; "
+                        "general: the fused op on the general kernel (the workload's hidden "
+                        "minus one, so rows leave 16-byte alignment); "
                         "log1p: the correctly rounded binary32 log1p")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -271,6 +274,8 @@ def main(argv=None):
 
     n_rows, hidden = (int(v) for v in args.workload.split("x"))
     cfg = synth.CONFIGS.get(args.workload, dict(seed=3, n_rows=n_rows, hidden=hidden))
+    if args.op == "general":
+        hidden -= 1   # hidden % 8 != 0: every row off 16-byte alignment
     eps = 1e-6
     x, r, w = synth.workload(cfg["seed"], n_rows, hidden)
     tensor_bytes = n_rows * hidden * 2
@@ -299,6 +304,8 @@ def main(argv=None):
             arn.add_rmsnorm_quant_fwd(q, sc, ro, xd, rd, wd, eps)
         elif args.op == "plain":
             arn.rmsnorm_fwd(o, xd, wd, eps)
+        elif args.op == "general":
+            arn.add_rmsnorm_fwd_cfg(o, ro, xd, rd, wd, eps, path=arn.PATH_GENERAL)
         elif args.op == "plain_quant":
             q, sc = qbufs[i % sets]
             arn.rmsnorm_quant_fwd(q, sc, xd, wd, eps)
@@ -328,8 +335,10 @@ def main(argv=None):
     copy_gbps = copy_ceiling(torch, arn, bufs, min(args.steps, 500), n_rows, hidden, plain)
 
     path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"
+    if args.op == "general":
+        path = "general"
     digest = hip_build.source_digest()
-    tag = path if args.op == "bf16" else path + "_" + args.op
+    tag = path if args.op in ("bf16", "general") else path + "_" + args.op
     traffic = traffic_from_profiles(tag, args.workload, digest)
     roofline = {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
@@ -340,7 +349,9 @@ def main(argv=None):
                    "quant": "fused add+RMSNorm, int8-quantised out, HBM GB/s and % of peak",
                    "plain": "RMSNorm (no residual add), HBM GB/s and % of peak",
                    "plain_quant": "RMSNorm (no residual add), int8-quantised out, HBM GB/s "
-                                  "and % of peak"}[args.op],
+                                  "and % of peak",
+                   "general": "fused add+RMSNorm on the general kernel (hidden % 8 != 0), "
+                              "HBM GB/s and % of peak"}[args.op],
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -361,7 +372,7 @@ def main(argv=None):
         "roofline": roofline,
         "copy_ceiling": {"gbps": round(copy_gbps, 2),
                          "kernel_frac_of_copy": round(gbps / copy_gbps, 4)
-                         if args.op in ("bf16", "plain") else None,
+                         if args.op in ("bf16", "plain", "general") else None,
                          "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
                          "what": "add_rmsnorm_test_copy2 over the same bytes: two 16-byte "
                                  "nontemporal streaming copies, no arithmetic, same buffer rotation"},

@@ -47,7 +47,6 @@ int pow2_at_least(int64_t need) {
 }
 
 // Default workgroup sizes per path.
-constexpr int kGeneralThreads = 256;
 constexpr int kWaveRowThreads = 256;
 constexpr int kWgRowThreads = 512;
 constexpr int kTwoPassThreads = 512;
@@ -176,7 +175,12 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (path == ADD_RMSNORM_PATH_GENERAL) {
-    const int b = c.block_threads ? c.block_threads : kGeneralThreads;
+    // One workgroup per row: wider rows want more threads in flight.
+    const int b = c.block_threads ? c.block_threads
+                  : hidden <= 1024  ? 64
+                  : hidden <= 4096  ? 256
+                  : hidden <= 8192  ? 512
+                                    : 1024;
     int max_lds = 0;
     const int rc = device_max_lds(&max_lds);
     if (rc != ADD_RMSNORM_OK) return rc;

@@ -561,9 +561,11 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
 // are +0, which leaves its fma chain unchanged (fma(0, 0, t) = t for t >= 0),
 // and segments past the row are +0 leaves of the tree.  So the sum of squares,
 // and every result, is the same as the fast kernels give where both apply.
-// Structure of the LDS two-pass kernel: one workgroup of B threads per row;
-// pass 1 stages the fp32 sums in LDS and forms one block sum per wave per
-// chunk of B segments; pass 2 normalises from LDS.
+// One workgroup of B threads per row.  Loads and stores go one element per
+// lane, consecutive lanes on consecutive elements (128 bytes per wavefront
+// instruction); the fp32 sums are staged in LDS by element, and thread t then
+// reads its segments t + B c from there for the tree, as the fast kernels
+// hold them.  Normalisation reads LDS again and stores element by element.
 struct GenParams {
   uint16_t* out;
   uint16_t* residual_out;
@@ -577,6 +579,9 @@ struct GenParams {
   float eps;
 };
 
+// Elements per thread loaded together by the general kernel.
+constexpr int GU = 8;
+
 DEV float bf16_at(const uint16_t* p, int j) { return __builtin_bit_cast(float, (uint32_t)p[j] << 16); }
 
 // bf16 of one fp32 value by the same packed conversion as the fast kernels.
@@ -586,43 +591,57 @@ template <int B, int NB, bool R>
 __global__ __launch_bounds__(B) void k_general(GenParams p) {
   constexpr int W = B / 64;
   __shared__ float blk[NB];
-  extern __shared__ float4 stage[];  // [2][C]: elements 0-3, then 4-7, of each segment
+  extern __shared__ float4 stage4[];  // acc of element j at stage[j], padded to 8 * C
+  float* stage = reinterpret_cast<float*>(stage4);
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const int H = p.hidden;
   const int C = (H + 7) / 8;
   const int chunks = (C + B - 1) / B;
-  float4* lo = stage;
-  float4* hi = stage + C;
 
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
     const uint16_t* xr = p.x + row * p.x_stride;
     const uint16_t* rr = R ? p.residual + row * p.r_stride : nullptr;
     uint16_t* ror = R ? p.residual_out + row * p.ro_stride : nullptr;
     uint16_t* orow = p.out + row * p.out_stride;
+    // acc, one element per lane (consecutive lanes, consecutive elements),
+    // residual_out stored the same way; the padding of the last segment is
+    // +0.  GU elements per thread are loaded before any is used, so that
+    // many loads are in flight.
+    for (int j0 = t; j0 < 8 * C; j0 += GU * B) {
+      float xv[GU], rv[GU];
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int j = j0 + u * B;
+        xv[u] = j < H ? bf16_at(xr, j) : 0.0f;
+        if constexpr (R) rv[u] = j < H ? bf16_at(rr, j) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int j = j0 + u * B;
+        float a = xv[u];
+        if constexpr (R) {
+          a = a + rv[u];
+          if (j < H) ror[j] = bf16_rne1(a);
+        }
+        if (j < 8 * C) stage[j] = j < H ? a : 0.0f;
+      }
+    }
     for (int i = chunks * W + t; i < NB; i += B) blk[i] = 0.0f;
+    __syncthreads();
+    // the segments' sums, thread t holding segments t + B c as everywhere
     for (int c = 0; c < chunks; ++c) {
       const int s = c * B + t;
       float acc[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = 8 * s + k;
-        float a = 0.0f;
-        if (j < H) {
-          a = bf16_at(xr, j);
-          if constexpr (R) a = a + bf16_at(rr, j);
-        }
-        acc[k] = a;
-      }
       if (s < C) {
-        if constexpr (R) {
+        const float4 l = stage4[2 * s];
+        const float4 h = stage4[2 * s + 1];
+        acc[0] = l.x; acc[1] = l.y; acc[2] = l.z; acc[3] = l.w;
+        acc[4] = h.x; acc[5] = h.y; acc[6] = h.z; acc[7] = h.w;
+      } else {
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (8 * s + k < H) ror[8 * s + k] = bf16_rne1(acc[k]);
-        }
-        lo[s] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        hi[s] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
       }
       const float bs = wave_block_sum(seg_sumsq(acc));
       if (lane == 0) blk[c * W + wave] = bs;
@@ -630,16 +649,14 @@ __global__ __launch_bounds__(B) void k_general(GenParams p) {
     __syncthreads();
     const float sumsq = pairwise_tree_lds<NB>(blk);
     const float rinv = 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
-    for (int c = 0; c < chunks; ++c) {
-      const int s = c * B + t;
-      if (s < C) {
-        const float4 l = lo[s], h = hi[s];
-        const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
+    for (int j0 = t; j0 < H; j0 += GU * B) {
+      float wv[GU];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int j = 8 * s + k;
-          if (j < H) orow[j] = bf16_rne1((acc[k] * rinv) * bf16_at(p.weight, j));
-        }
+      for (int u = 0; u < GU; ++u) wv[u] = j0 + u * B < H ? bf16_at(p.weight, j0 + u * B) : 0.0f;
+#pragma unroll
+      for (int u = 0; u < GU; ++u) {
+        const int j = j0 + u * B;
+        if (j < H) orow[j] = bf16_rne1((stage[j] * rinv) * wv[u]);
       }
     }
     __syncthreads();  // blk and the staged sums are rewritten by the next row
