@@ -334,9 +334,12 @@ def main(argv=None):
 
     copy_gbps = copy_ceiling(torch, arn, bufs, min(args.steps, 500), n_rows, hidden, plain)
 
-    path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"
     if args.op == "general":
         path = "general"
+    elif args.op == "bf16":
+        path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"
+    else:  # the quantised and plain variants keep rows in registers up to 16384
+        path = "wave_row" if hidden <= 1024 else "wg_row" if hidden <= 16384 else "lds_two_pass"
     digest = hip_build.source_digest()
     tag = path if args.op in ("bf16", "general") else path + "_" + args.op
     traffic = traffic_from_profiles(tag, args.workload, digest)
