@@ -194,12 +194,15 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (path == ADD_RMSNORM_PATH_GENERAL) {
-    // One workgroup per row: wider rows want more threads in flight.
-    const int b = c.block_threads ? c.block_threads
-                  : hidden <= 1024  ? 64
-                  : hidden <= 4096  ? 256
-                  : hidden <= 8192  ? 512
-                                    : 1024;
+    // One workgroup per row.  By default one segment per thread (the fewest
+    // registers, so the most rows in flight): the smallest workgroup that
+    // covers the row, 64 to 1024 threads; two segments per thread at 1024
+    // threads up to 16384, and the LDS kernel above.
+    int b = c.block_threads;
+    if (b == 0) {
+      b = 64;
+      while (b < 1024 && b * 8 < hidden) b *= 2;
+    }
     int max_lds = 0;
     const int rc = device_max_lds(&max_lds);
     if (rc != ADD_RMSNORM_OK) return rc;

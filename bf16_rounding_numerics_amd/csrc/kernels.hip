@@ -663,6 +663,103 @@ __global__ __launch_bounds__(B) void k_general(GenParams p) {
   }
 }
 
+// Register-resident general kernel: one workgroup of B threads per row,
+// thread t holding segments t + B j (j < J) in registers, as k_wg_row does,
+// with the same block sums and tree.  Loads and stores are 16-bit and
+// coalesced: wavefront w reads the 512 elements of its segment block
+// w + W j one element per lane (eight loads), then regroups them into one
+// segment per lane through its own 1 KiB of LDS, and sends residual_out and
+// out back out the same way.  A wavefront's LDS accesses execute in order,
+// so the regrouping needs no workgroup barrier; a wavefront-scope fence keeps
+// the compiler from moving them across one another.  The weight is staged in
+// LDS once per workgroup, in segment order, zero padded.
+DEV void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
+template <int B, int J, bool R>
+__global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
+  constexpr int W = B / 64;
+  constexpr int NB = W * J;
+  __shared__ float blk[2][NB];  // alternates by row so one barrier per row suffices
+  __shared__ u32x4 slot[W][64];
+  extern __shared__ u32x4 wseg[];  // B * J segments of weight
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int H = p.hidden;
+  uint16_t* wl = reinterpret_cast<uint16_t*>(wseg);
+  for (int i = t; i < 8 * B * J; i += B) wl[i] = i < H ? p.weight[i] : (uint16_t)0;
+  __syncthreads();
+  uint16_t* sl = reinterpret_cast<uint16_t*>(slot[wave]);
+
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x, parity ^= 1) {
+    const uint16_t* xr = p.x + row * p.x_stride;
+    const uint16_t* rr = R ? p.residual + row * p.r_stride : nullptr;
+    uint16_t* ror = R ? p.residual_out + row * p.ro_stride : nullptr;
+    uint16_t* orow = p.out + row * p.out_stride;
+    uint16_t xv[J][8], rv[J][8];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = 512 * (wave + W * j) + 64 * k + lane;
+        xv[j][k] = e < H ? xr[e] : (uint16_t)0;
+        if constexpr (R) rv[j][k] = e < H ? rr[e] : (uint16_t)0;
+      }
+    }
+    float acc[J][8];
+    float bs[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sl[64 * k + lane] = xv[j][k];
+      wave_fence();
+      const u32x4 xq = slot[wave][lane];
+      u32x4 rq = {0, 0, 0, 0};
+      if constexpr (R) {
+        wave_fence();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sl[64 * k + lane] = rv[j][k];
+        wave_fence();
+        rq = slot[wave][lane];
+      }
+      bs[j] = add_segment<R>(xq, rq, acc[j]);
+      if constexpr (R) {
+        wave_fence();
+        slot[wave][lane] = pack8_rne(acc[j]);
+        wave_fence();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int e = 512 * (wave + W * j) + 64 * k + lane;
+          if (e < H) ror[e] = sl[64 * k + lane];
+        }
+      }
+      wave_fence();
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) bs[j] = wave_block_sum(bs[j]);
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) blk[parity][wave + W * j] = bs[j];
+    }
+    __syncthreads();
+    const float sumsq = pairwise_tree_lds<NB>(blk[parity]);
+    const float rinv = 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const u32x4 wq = wseg[64 * (wave + W * j) + lane];
+      slot[wave][lane] = normalise8(acc[j], rinv, wq);
+      wave_fence();
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = 512 * (wave + W * j) + 64 * k + lane;
+        if (e < H) orow[e] = sl[64 * k + lane];
+      }
+      wave_fence();
+    }
+  }
+}
+
 // ---------------------------------------------------------------- epilogue test
 
 __global__ __launch_bounds__(256) void k_cvt_range(u32x4* out, uint32_t start, int64_t groups) {
@@ -858,6 +955,46 @@ hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t 
   return hipGetLastError();
 }
 
+template <bool R, int B>
+hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s) {
+  const size_t lds = (size_t)B * j * 16;
+  switch (j) {
+    case 1: {
+      auto k = k_general_reg<B, 1, R>;
+      if (grid == -1) grid = resident(k, B, lds);
+      hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
+      return hipGetLastError();
+    }
+    case 2: {
+      auto k = k_general_reg<B, 2, R>;
+      if (grid == -1) grid = resident(k, B, lds);
+      hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
+      return hipGetLastError();
+    }
+    case 4:
+      if constexpr (B * 4 <= 2048) {
+        auto k = k_general_reg<B, 4, R>;
+        if (grid == -1) grid = resident(k, B, lds);
+        hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
+        return hipGetLastError();
+      }
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool R>
+hipError_t general_reg_by_block(const GenParams& p, int b, int j, int64_t grid, hipStream_t s) {
+  switch (b) {
+    case 64: return go_general_reg<R, 64>(p, j, grid, s);
+    case 128: return go_general_reg<R, 128>(p, j, grid, s);
+    case 256: return go_general_reg<R, 256>(p, j, grid, s);
+    case 512: return go_general_reg<R, 512>(p, j, grid, s);
+    case 1024: return go_general_reg<R, 1024>(p, j, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <bool R>
 hipError_t general_by_block(const GenParams& p, int b, int hidden, int64_t grid, hipStream_t s) {
   switch (b) {
@@ -933,6 +1070,14 @@ hipError_t launch_general(const FwdArgs& a, int block_threads, int64_t grid_bloc
   p.hidden = a.hidden;
   p.hidden_f = (float)a.hidden;
   p.eps = a.eps;
+  // Rows that fit in registers (at most 4 segments per thread and 2048 per
+  // workgroup) take the register-resident kernel, others the LDS one.
+  const int segs = (a.hidden + 7) / 8;
+  int j = 1;
+  while (j * block_threads < segs) j *= 2;
+  if (j <= 4 && j * block_threads <= 2048)
+    return a.residual ? general_reg_by_block<true>(p, block_threads, j, grid_blocks, s)
+                      : general_reg_by_block<false>(p, block_threads, j, grid_blocks, s);
   return a.residual ? general_by_block<true>(p, block_threads, a.hidden, grid_blocks, s)
                     : general_by_block<false>(p, block_threads, a.hidden, grid_blocks, s);
 }
