@@ -200,12 +200,15 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (path == ADD_RMSNORM_PATH_GENERAL) {
-    // One workgroup per row.  By default one segment per thread (the fewest
-    // registers, so the most rows in flight): the smallest workgroup that
-    // covers the row, 64 to 1024 threads; two segments per thread at 1024
-    // threads up to 16384, and the LDS kernel above.
+    // Rows up to 1024 take one wavefront each, four rows per workgroup.
+    // Longer rows take one workgroup each, by default with one segment per
+    // thread (the fewest registers, so the most rows in flight): the smallest
+    // workgroup that covers the row, 64 to 1024 threads; two segments per
+    // thread at 1024 threads up to 16384, and the LDS kernel above.
     int b = c.block_threads;
-    if (b == 0) {
+    if (b == 0 && hidden <= 1024) {
+      b = 256;
+    } else if (b == 0) {
       b = 64;
       while (b < 1024 && b * 8 < hidden) b *= 2;
     }

@@ -760,6 +760,87 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
   }
 }
 
+// Wavefront-per-row general kernel for short rows (at most 64 J segments):
+// WAVES rows per workgroup, each wavefront one row, its J segment blocks
+// regrouped through its own LDS slot as in k_general_reg; the J block sums
+// finish the tree in registers, so no barrier is needed after the weight is
+// staged.
+template <int WAVES, int J, bool R>
+__global__ __launch_bounds__(WAVES * 64) void k_general_wave(GenParams p) {
+  __shared__ u32x4 slot[WAVES][64];
+  __shared__ u32x4 wseg[64 * J];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int H = p.hidden;
+  uint16_t* wl = reinterpret_cast<uint16_t*>(wseg);
+  for (int i = t; i < 512 * J; i += WAVES * 64) wl[i] = i < H ? p.weight[i] : (uint16_t)0;
+  __syncthreads();
+  uint16_t* sl = reinterpret_cast<uint16_t*>(slot[wave]);
+
+  const int64_t stride = (int64_t)gridDim.x * WAVES;
+  for (int64_t row = (int64_t)blockIdx.x * WAVES + wave; row < p.n_rows; row += stride) {
+    const uint16_t* xr = p.x + row * p.x_stride;
+    const uint16_t* rr = R ? p.residual + row * p.r_stride : nullptr;
+    uint16_t* ror = R ? p.residual_out + row * p.ro_stride : nullptr;
+    uint16_t* orow = p.out + row * p.out_stride;
+    uint16_t xv[J][8], rv[J][8];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = 512 * j + 64 * k + lane;
+        xv[j][k] = e < H ? xr[e] : (uint16_t)0;
+        if constexpr (R) rv[j][k] = e < H ? rr[e] : (uint16_t)0;
+      }
+    }
+    float acc[J][8];
+    float bs[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sl[64 * k + lane] = xv[j][k];
+      wave_fence();
+      const u32x4 xq = slot[wave][lane];
+      u32x4 rq = {0, 0, 0, 0};
+      if constexpr (R) {
+        wave_fence();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sl[64 * k + lane] = rv[j][k];
+        wave_fence();
+        rq = slot[wave][lane];
+      }
+      bs[j] = add_segment<R>(xq, rq, acc[j]);
+      if constexpr (R) {
+        wave_fence();
+        slot[wave][lane] = pack8_rne(acc[j]);
+        wave_fence();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int e = 512 * j + 64 * k + lane;
+          if (e < H) ror[e] = sl[64 * k + lane];
+        }
+      }
+      wave_fence();
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) bs[j] = wave_block_sum(bs[j]);
+    const float sumsq = pairwise_tree<J>(bs);
+    const float rinv = 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      slot[wave][lane] = normalise8(acc[j], rinv, wseg[64 * j + lane]);
+      wave_fence();
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = 512 * j + 64 * k + lane;
+        if (e < H) orow[e] = sl[64 * k + lane];
+      }
+      wave_fence();
+    }
+  }
+}
+
 // ---------------------------------------------------------------- epilogue test
 
 __global__ __launch_bounds__(256) void k_cvt_range(u32x4* out, uint32_t start, int64_t groups) {
@@ -983,6 +1064,33 @@ hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s
   return hipErrorInvalidValue;
 }
 
+template <bool R, int WAVES>
+hipError_t go_general_wave(const GenParams& p, int j, int64_t grid, hipStream_t s) {
+  const int64_t groups = (p.n_rows + WAVES - 1) / WAVES;
+  if (j == 1) {
+    auto k = k_general_wave<WAVES, 1, R>;
+    if (grid == -1) grid = resident(k, WAVES * 64, 0);
+    hipLaunchKernelGGL(k, dim3(grid_for(grid, groups)), dim3(WAVES * 64), 0, s, p);
+  } else {
+    auto k = k_general_wave<WAVES, 2, R>;
+    if (grid == -1) grid = resident(k, WAVES * 64, 0);
+    hipLaunchKernelGGL(k, dim3(grid_for(grid, groups)), dim3(WAVES * 64), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <bool R>
+hipError_t general_wave_by_block(const GenParams& p, int b, int j, int64_t grid, hipStream_t s) {
+  switch (b) {
+    case 64: return go_general_wave<R, 1>(p, j, grid, s);
+    case 128: return go_general_wave<R, 2>(p, j, grid, s);
+    case 256: return go_general_wave<R, 4>(p, j, grid, s);
+    case 512: return go_general_wave<R, 8>(p, j, grid, s);
+    case 1024: return go_general_wave<R, 16>(p, j, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <bool R>
 hipError_t general_reg_by_block(const GenParams& p, int b, int j, int64_t grid, hipStream_t s) {
   switch (b) {
@@ -1070,9 +1178,15 @@ hipError_t launch_general(const FwdArgs& a, int block_threads, int64_t grid_bloc
   p.hidden = a.hidden;
   p.hidden_f = (float)a.hidden;
   p.eps = a.eps;
-  // Rows that fit in registers (at most 4 segments per thread and 2048 per
-  // workgroup) take the register-resident kernel, others the LDS one.
+  // Rows of at most 128 segments take one wavefront each; other rows that fit
+  // in registers (at most 4 segments per thread and 2048 per workgroup) the
+  // register-resident kernel, the rest the LDS one.
   const int segs = (a.hidden + 7) / 8;
+  if (segs <= 128) {
+    const int jw = segs <= 64 ? 1 : 2;
+    return a.residual ? general_wave_by_block<true>(p, block_threads, jw, grid_blocks, s)
+                      : general_wave_by_block<false>(p, block_threads, jw, grid_blocks, s);
+  }
   int j = 1;
   while (j * block_threads < segs) j *= 2;
   if (j <= 4 && j * block_threads <= 2048)
