@@ -63,7 +63,7 @@ bool wg_row_supported(int block_threads, int segs_per_thread);
 // Correctly rounded binary32 log1p of n elements (log1p.hip): E =
 // elems_per_thread (1, 2, 4 or 8) consecutive elements per thread,
 // block_threads * E per tile; grid_blocks as above (0: one workgroup per
-// tile).  accurate_only sends every element through the double-double path.
+// tile, at most 8192).  accurate_only sends every element through the double-double path.
 hipError_t launch_log1p(float* out, const float* x, int64_t n, int block_threads,
                         int elems_per_thread, int64_t grid_blocks, bool accurate_only,
                         hipStream_t stream);

@@ -48,8 +48,10 @@ int log1p_f32(float* out, const float* x, int64_t n, struct ihipStream_t* stream
  *   block_threads     64, 128, 256, 512 or 1024.
  *   elems_per_thread  1, 2, 4 or 8 consecutive elements per thread.
  *   grid_blocks       0: one workgroup per tile of block_threads *
- *                     elems_per_thread elements; > 0: that many workgroups,
- *                     looping over tiles; -1: as many as fit on the device.
+ *                     elems_per_thread elements, at most 8192 workgroups
+ *                     (which then loop over tiles); > 0: that many
+ *                     workgroups, looping over tiles; -1: as many as fit on
+ *                     the device.
  *   flags             0 or LOG1P_FLAG_ACCURATE_ONLY.
  */
 struct log1p_launch_cfg {
