@@ -216,7 +216,9 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
     const int rc = device_max_lds(&max_lds);
     if (rc != ADD_RMSNORM_OK) return rc;
     if (addrms::general_lds_bytes((int)hidden) > (size_t)max_lds) return ADD_RMSNORM_ERANGE;
-    e = addrms::launch_general(a, b, c.grid_blocks, s);
+    // By default as many workgroups as fit, looping over rows: the weight is
+    // staged in LDS once per workgroup (measured +15-50% over one per row).
+    e = addrms::launch_general(a, b, c.grid_blocks == 0 ? -1 : c.grid_blocks, s);
   } else if (path == ADD_RMSNORM_PATH_WAVE_ROW) {
     const int b = block ? block : kWaveRowThreads;
     const int j = pow2_at_least((segs + 63) / 64);
