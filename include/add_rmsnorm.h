@@ -122,9 +122,10 @@ int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residua
  *   path           one of ADD_RMSNORM_PATH_*.
  *   block_threads  workgroup size: 64, 128, 256, 512 or 1024 (the wave path
  *                  runs block_threads / 64 rows per workgroup).
- *   grid_blocks    0: one workgroup per row (per row group on the wave path)
- *                  for the fast kernels, as many as fit on the device for the
- *                  general ones; > 0: exactly that many workgroups, each
+ *   grid_blocks    0: the library's choice: one workgroup per row (per row
+ *                  group on the wave path) for the fused fast kernels, as
+ *                  many as fit on the device for plain RMSNorm and the
+ *                  general kernels; > 0: exactly that many workgroups, each
  *                  looping over rows (a persistent grid); -1: as many as fit
  *                  on the device at once.
  *   flags          must be 0.
