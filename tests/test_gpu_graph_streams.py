@@ -91,3 +91,74 @@ def test_two_streams_at_once():
     for o1, ro1, o2, ro2 in outs:
         assert torch.equal(o1, ref[0][0]) and torch.equal(ro1, ref[0][1])
         assert torch.equal(o2, ref[1][0]) and torch.equal(ro2, ref[1][1])
+
+
+@pytest.mark.parametrize("kind", ["plain", "plain_quant", "strided_general", "log1p"])
+def test_graph_replays_of_the_other_entry_points(kind):
+    """Plain RMSNorm (resident grid by default), a strided view on the
+    general kernels, and log1p (capped persistent grid), each captured once
+    and replayed on fresh inputs, checked against eager calls."""
+    require_gpu()
+    import torch
+
+    announce("graph replay: %s" % kind)
+    n, h = 64, 4096
+    dev = "cuda:0"
+    if kind == "log1p":
+        xs = torch.empty(1 << 20, dtype=torch.float32, device=dev)
+        out = torch.empty_like(xs)
+
+        def call(o, x):
+            arn.log1p_f32(o, x)
+    elif kind == "strided_general":
+        h = 1001
+        X = torch.zeros(n, 2 * h + 3, dtype=torch.int16, device=dev)
+        O = torch.zeros_like(X)
+        RO = torch.zeros_like(X)
+        xs, out = X[:, 1:1 + h], O[:, 2:2 + h]
+        res = RO[:, 3:3 + h]
+        rs = torch.empty(n, h, dtype=torch.int16, device=dev)
+        w = to_dev(synth.bf16_normal(4400, 2, (h,), 1.0, 0.1))
+
+        def call(o, x):
+            arn.add_rmsnorm_fwd_strided(o, res if o is out else torch.empty_like(rs), x, rs, w,
+                                        1e-6)
+    else:
+        xs = torch.empty(n, h, dtype=torch.int16, device=dev)
+        w = to_dev(synth.bf16_normal(4400, 2, (h,), 1.0, 0.1))
+        if kind == "plain":
+            out = torch.empty_like(xs)
+
+            def call(o, x):
+                arn.rmsnorm_fwd(o, x, w, 1e-6)
+        else:
+            out = torch.empty(n, h, dtype=torch.int8, device=dev)
+            sc = torch.empty(n, dtype=torch.float32, device=dev)
+
+            def call(o, x):
+                arn.rmsnorm_quant_fwd(o, sc if o is out else torch.empty_like(sc), x, w, 1e-6)
+
+    def fresh(rep):
+        if kind == "log1p":
+            return torch.from_numpy(synth.uniform_f32(4500 + rep, 0, xs.numel())).to(dev)
+        x, r, _ = synth.workload(4500 + rep, n, h)
+        if kind == "strided_general":
+            rs.copy_(to_dev(r))
+        return to_dev(x)
+
+    xs.copy_(fresh(0))
+    call(out, xs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, xs)
+    torch.cuda.synchronize()
+    for rep in range(1, 4):
+        x = fresh(rep)
+        xs.copy_(x)
+        g.replay()
+        eager_out = torch.empty_like(out)
+        call(eager_out, x.contiguous() if kind != "strided_general" else xs.contiguous())
+        _ = (xs.float() * 2).sum()
+        torch.cuda.synchronize()
+        assert torch.equal(out.contiguous(), eager_out.contiguous()), (kind, rep)
