@@ -71,6 +71,9 @@ def parse_args(argv=None):
                    help="time budget of the CPU oracle baseline")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain device copy of known size (counter calibration)")
+    p.add_argument("--ceilings", action="store_true",
+                   help="measure the device's read-only, write-only and 50/50 copy streaming "
+                        "rates at the workload's bytes, beside the fused kernel")
     return p.parse_args(argv)
 
 
@@ -245,6 +248,63 @@ def bench_log1p(args, torch, arn, hip_build, synth):
     return 0
 
 
+def ceilings(args, torch, arn, synth):
+    """Streaming rates of the device with the fused kernels' access pattern,
+    at the bytes of one fused call on the workload (x and residual read, out
+    and residual_out written), each over rotated buffers and one launch per
+    step: read-only, write-only, the 2-in/2-out copy, and the fused kernel."""
+    import numpy as np
+
+    n_rows, hidden = (int(v) for v in args.workload.split("x"))
+    dev = torch.device("cuda:0")
+    count = n_rows * hidden              # elements per tensor
+    sets = max(1, -(-CACHE_DEFEAT_BYTES // (8 * count)))
+    x, r, w = synth.workload(3, n_rows, hidden)
+    bufs = []
+    for _ in range(sets):
+        xd = torch.from_numpy(x.view(np.int16)).to(dev)
+        rd = torch.from_numpy(r.view(np.int16)).to(dev)
+        bufs.append((torch.empty_like(xd), torch.empty_like(xd), xd, rd))
+    wd = torch.from_numpy(w.view(np.int16)).to(dev)
+    # one contiguous buffer of four tensors' bytes per set, for the
+    # one-directional streams
+    big = [torch.empty(4 * count, dtype=torch.int16, device=dev) for _ in range(sets)]
+    sink = torch.empty_like(big[0])
+    stream = torch.cuda.current_stream(dev)
+    steps = min(args.steps, 1000)
+    moved = 8 * count                    # bytes per step in every case
+
+    def rate(fn):
+        ms, _ = time_steps(torch, fn, steps, 20, stream)
+        return round(moved / (ms * 1e-3) / 1e9, 1)
+
+    def read(i):
+        arn.add_rmsnorm_test_stream(sink, big[i % sets], 0)
+
+    def write(i):
+        b = big[i % sets]
+        arn.add_rmsnorm_test_stream(b, b, 1)
+
+    def copy(i):
+        o, ro, xd, rd = bufs[i % sets]
+        arn.add_rmsnorm_test_copy2(ro, o, xd, rd)
+
+    def fused(i):
+        o, ro, xd, rd = bufs[i % sets]
+        arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, 1e-6)
+
+    res = {"read_only": rate(read), "write_only": rate(write), "copy_2in_2out": rate(copy),
+           "add_rmsnorm_fwd": rate(fused)}
+    print(json.dumps({"ceilings_GBps": res, "peak_GBps": PEAK_HBM_GBPS,
+                      "frac_of_peak": {k: round(v / PEAK_HBM_GBPS, 4) for k, v in res.items()},
+                      "workload": args.workload, "bytes_per_step": moved, "buffer_sets": sets,
+                      "what": "8 * rows * hidden bytes per step, one launch each: read-only and "
+                              "write-only stream one buffer of four tensors' size, the copy reads "
+                              "two tensors and writes two, the fused call reads x and residual "
+                              "and writes out and residual_out"}))
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -269,6 +329,8 @@ def main(argv=None):
     if args.calibrate_copy:
         run_copy_calibration(torch)
         return 0
+    if args.ceilings:
+        return ceilings(args, torch, arn, synth)
     if args.op == "log1p":
         return bench_log1p(args, torch, arn, hip_build, synth)
 

@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -57,10 +57,10 @@ class LaunchCfg(ctypes.Structure):
 _lib = None
 
 EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_fwd_strided",
-           "rmsnorm_fwd_strided", "add_rmsnorm_quant_fwd",
-           "add_rmsnorm_quant_fwd_cfg", "rmsnorm_fwd", "rmsnorm_fwd_cfg", "rmsnorm_quant_fwd",
-           "rmsnorm_quant_fwd_cfg", "log1p_f32", "log1p_f32_cfg", "add_rmsnorm_test_cvt_range",
-           "add_rmsnorm_test_copy2", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
+           "rmsnorm_fwd_strided", "add_rmsnorm_quant_fwd", "add_rmsnorm_quant_fwd_cfg",
+           "rmsnorm_fwd", "rmsnorm_fwd_cfg", "rmsnorm_quant_fwd", "rmsnorm_quant_fwd_cfg",
+           "log1p_f32", "log1p_f32_cfg", "add_rmsnorm_test_cvt_range", "add_rmsnorm_test_copy2",
+           "add_rmsnorm_test_stream", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
            "add_rmsnorm_abi_version", "add_rmsnorm_build_info")
 
 
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
     L.add_rmsnorm_test_cvt_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
     L.add_rmsnorm_test_copy2.restype = i32
     L.add_rmsnorm_test_copy2.argtypes = [vp, vp, vp, vp, i64, vp]
+    L.add_rmsnorm_test_stream.restype = i32
+    L.add_rmsnorm_test_stream.argtypes = [vp, vp, i64, i32, vp]
     L.add_rmsnorm_strerror.restype = ctypes.c_char_p
     L.add_rmsnorm_strerror.argtypes = [i32]
     L.add_rmsnorm_last_hip_error.restype = ctypes.c_char_p
@@ -437,3 +439,16 @@ def add_rmsnorm_test_copy2(dst0, dst1, src0, src1, stream=None) -> None:
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_test_copy2(
         dst0.data_ptr(), dst1.data_ptr(), src0.data_ptr(), src1.data_ptr(), n, h)))
+
+
+def add_rmsnorm_test_stream(dst, src, mode: int, stream=None) -> None:
+    """Measurement hook: mode 0 reads src (dst, of src's size, receives almost
+    nothing), mode 1 writes dst.  Contiguous 16-bit GPU tensors."""
+    for t in (dst,) + ((src,) if mode == 0 else ()):
+        if not t.is_cuda or t.element_size() != 2 or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous 16-bit GPU tensors")
+    dev = dst.get_device()
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_test_stream(
+        dst.data_ptr(), src.data_ptr() if mode == 0 else None, dst.numel(), mode, h)))

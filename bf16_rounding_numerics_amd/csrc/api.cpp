@@ -488,6 +488,20 @@ int add_rmsnorm_test_copy2(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
   return ADD_RMSNORM_OK;
 }
 
+int add_rmsnorm_test_stream(uint16_t* dst, const uint16_t* src, int64_t count, int mode,
+                            struct ihipStream_t* stream) {
+  if (count < 0 || (mode != 0 && mode != 1)) return ADD_RMSNORM_EINVAL;
+  if (count % 8 != 0) return ADD_RMSNORM_EALIGN;
+  if (count == 0) return ADD_RMSNORM_OK;
+  if (!dst || (mode == 0 && !src)) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(dst) || (mode == 0 && !aligned16(src))) return ADD_RMSNORM_EALIGN;
+  const uint64_t n = (uint64_t)count * 2;
+  if (mode == 0 && overlap(dst, n, src, n)) return ADD_RMSNORM_EALIAS;
+  hipError_t e = addrms::launch_stream(dst, src, count, mode, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_failure(e);
+  return ADD_RMSNORM_OK;
+}
+
 const char* add_rmsnorm_strerror(int status) {
   switch (status) {
     case ADD_RMSNORM_OK: return "success";

@@ -68,6 +68,12 @@ hipError_t launch_log1p(float* out, const float* x, int64_t n, int block_threads
                         int elems_per_thread, int64_t grid_blocks, bool accurate_only,
                         hipStream_t stream);
 
+// Reference streams: mode 0 reads count 16-bit elements of src (dst must hold
+// count elements; at most one 16-byte word per thread is ever written),
+// mode 1 writes count elements to dst.
+hipError_t launch_stream(uint16_t* dst, const uint16_t* src, int64_t count, int mode,
+                         hipStream_t stream);
+
 // Reference copy: d0 <- s0 and d1 <- s1, count 16-bit elements each.
 hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,
                         int64_t count, hipStream_t stream);

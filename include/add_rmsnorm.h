@@ -49,7 +49,7 @@ extern "C" {
 /* hipStream_t is a pointer to this opaque struct. */
 struct ihipStream_t;
 
-#define ADD_RMSNORM_ABI_VERSION 4
+#define ADD_RMSNORM_ABI_VERSION 5
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768
@@ -250,7 +250,20 @@ int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,
 int add_rmsnorm_test_copy2(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
                            const uint16_t* src1, int64_t count, struct ihipStream_t* stream);
 
-/* Human-readable text of a status code (static storage). */
+/*
+ * Measurement hook: one-directional streams with the same access pattern as
+ * add_rmsnorm_test_copy2.  mode 0 reads count 16-bit elements of src and
+ * writes (almost) nothing; dst must hold count elements and not overlap src.
+ * mode 1 writes count elements of dst (bf16 1.0) and reads nothing; src is
+ * unused.  With the copy they give the device's read-only, write-only and
+ * 50/50 streaming rates, the bounds of the fused kernels' traffic mix.
+ * Device pointers, 16-byte aligned, count a multiple of 8.  Enqueued on
+ * stream.
+ */
+int add_rmsnorm_test_stream(uint16_t* dst, const uint16_t* src, int64_t count, int mode,
+                            struct ihipStream_t* stream);
+
+/* Human-readable text of a status code (static storage). *//* Human-readable text of a status code (static storage). */
 const char* add_rmsnorm_strerror(int status);
 
 /* Text of the HIP error behind the last ADD_RMSNORM_EHIP on this thread. */

@@ -307,6 +307,18 @@ def test_copy2_errors():
     assert L.add_rmsnorm_test_copy2(0, 0, 0, 0, 0, None) == arn.OK
 
 
+@fake_addresses
+def test_stream_hook_errors():
+    L = arn.lib()
+    assert L.add_rmsnorm_test_stream(A, A + MB, -8, 0, None) == arn.EINVAL
+    assert L.add_rmsnorm_test_stream(A, A + MB, 16, 2, None) == arn.EINVAL   # unknown mode
+    assert L.add_rmsnorm_test_stream(A, A + MB, 12, 0, None) == arn.EALIGN
+    assert L.add_rmsnorm_test_stream(A + 2, A + MB, 16, 0, None) == arn.EALIGN
+    assert L.add_rmsnorm_test_stream(A, 0, 16, 0, None) == arn.EINVAL        # read needs src
+    assert L.add_rmsnorm_test_stream(A, A + 16, 16, 0, None) == arn.EALIAS
+    assert L.add_rmsnorm_test_stream(0, 0, 0, 1, None) == arn.OK
+
+
 # ---------------------------------------------------------------- binding
 
 def test_binding_refuses_cpu_tensors():

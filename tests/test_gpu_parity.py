@@ -8,10 +8,11 @@ so an element the kernel fails to write cannot pass.
 import numpy as np
 import pytest
 
+import bf16_rounding_numerics_amd as arn
 import oracle
 import synth
-from gpu_helpers import (BIAS_GATE, announce, check_parity, from_dev, gpu_fwd, is_nan16,
-                         poisoned_like, require_gpu, to_dev)
+from gpu_helpers import (BIAS_GATE, POISON, announce, check_parity, from_dev, gpu_fwd,
+                         is_nan16, poisoned_like, require_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -181,8 +182,6 @@ def test_copy_reference_copies_bit_exactly():
     reference rate) must really move every byte."""
     import torch
 
-    import bf16_rounding_numerics_amd as arn
-
     announce("copy2 reference")
     x, r, _ = synth.workload(91, 333, 1024)
     xd, rd = to_dev(x), to_dev(r)
@@ -190,3 +189,21 @@ def test_copy_reference_copies_bit_exactly():
     arn.add_rmsnorm_test_copy2(d0, d1, xd, rd)
     torch.cuda.synchronize()
     assert np.array_equal(from_dev(d0), x) and np.array_equal(from_dev(d1), r)
+
+
+def test_stream_hooks():
+    """The read-only and write-only measurement streams: writing fills every
+    element with bf16 1.0; reading leaves the sink untouched (its fold of
+    these inputs is not the trigger pattern)."""
+    import torch
+
+    announce("stream hooks")
+    n = (1 << 20) + 8
+    src = to_dev(synth.bf16_normal(91, 0, (n,), 0.0, 1.0))
+    sink = poisoned_like(src)
+    arn.add_rmsnorm_test_stream(sink, src, 0)
+    dst = poisoned_like(src)
+    arn.add_rmsnorm_test_stream(dst, dst, 1)
+    torch.cuda.synchronize()
+    assert (from_dev(sink) == POISON).all()
+    assert (from_dev(dst) == 0x3F80).all()
