@@ -173,3 +173,32 @@ def test_all_binary32_inputs():
         if c % 8 == 7:
             announce("  all inputs: %d of 64 chunks agree" % (c + 1))
     announce("  all 2^32 inputs agree; %d decided by the oracle in binary128" % total_esc)
+
+
+def test_more_than_two_to_the_31_elements():
+    """2^31 + 1000 inputs (8 GiB each way): every bit-pattern class appears,
+    and sampled outputs, the last partial tile among them, match the
+    oracle."""
+    import torch
+
+    n = (1 << 31) + 1000
+    announce("log1p n = 2^31 + 1000")
+    x = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    xi = x.view(torch.int32)
+    chunk = 1 << 28
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        i = torch.arange(lo, hi, dtype=torch.int64, device="cuda:0")
+        xi[lo:hi] = ((i * 2654435761) & 0xFFFFFFFF).to(torch.int64).sub_(
+            ((i * 2654435761) & 0x80000000) * 2).to(torch.int32)
+        del i
+    out = torch.empty_like(x)
+    arn.log1p_f32(out, x)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(74)
+    idx = np.concatenate([rng.integers(0, n, 200000), np.arange(n - 3000, n)])
+    it = torch.from_numpy(idx).to("cuda:0")
+    xs, got = x[it].cpu().numpy(), out[it].cpu().numpy()
+    assert_same(got, oracle.log1p_f32(xs), "sampled")
+    del x, out
+    torch.cuda.empty_cache()

@@ -207,3 +207,25 @@ def test_stream_hooks():
     torch.cuda.synchronize()
     assert (from_dev(sink) == POISON).all()
     assert (from_dev(dst) == 0x3F80).all()
+
+
+def test_empty_inputs_through_every_entry_point():
+    """Zero rows (and zero log1p elements): every entry point returns at once
+    and touches nothing."""
+    import torch
+
+    announce("empty inputs")
+    dev = "cuda:0"
+    e = torch.empty(0, 1024, dtype=torch.int16, device=dev)
+    w = torch.ones(1024, dtype=torch.int16, device=dev)
+    arn.add_rmsnorm_fwd(e, e.clone(), e, e.clone(), w, 1e-6)
+    arn.rmsnorm_fwd(e, e.clone(), w, 1e-6)
+    arn.add_rmsnorm_quant_fwd(torch.empty(0, 1024, dtype=torch.int8, device=dev),
+                              torch.empty(0, dtype=torch.float32, device=dev), e, e.clone(),
+                              e.clone(), w, 1e-6)
+    arn.rmsnorm_quant_fwd(torch.empty(0, 1024, dtype=torch.int8, device=dev),
+                          torch.empty(0, dtype=torch.float32, device=dev), e, w, 1e-6)
+    arn.add_rmsnorm_fwd_strided(e, e.clone(), e.clone(), e.clone(), w, 1e-6)
+    f = torch.empty(0, dtype=torch.float32, device=dev)
+    arn.log1p_f32(f, f.clone())
+    torch.cuda.synchronize()
