@@ -89,6 +89,11 @@ class Oracle:
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_float]
+        L.orc_e4m3_rne.restype = ctypes.c_int
+        L.orc_e4m3_rne.argtypes = [ctypes.c_float]
+        L.orc_add_rmsnorm_quant_fp8.restype = ctypes.c_int
+        L.orc_add_rmsnorm_quant_fp8.argtypes = [ctypes.c_void_p] * 7 + [
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_float]
         self.path = path
         self.lib = L
 
@@ -222,6 +227,41 @@ class Oracle:
         return (q, sc, y) if want_exact else (q, sc)
 
 
+    # ------------------------------------------------------------ fp8 e4m3 out
+
+    def e4m3_rne(self, v: float) -> int:
+        """e4m3fn code (0..255) of a finite binary32 value, nearest-even,
+        saturating at +-448."""
+        return int(self.lib.orc_e4m3_rne(float(np.float32(v))))
+
+    def add_rmsnorm_quant_fp8(self, x, residual, weight, eps: float = 1e-6,
+                              want_exact: bool = False):
+        """FP8 E4M3 variant: (codes uint8 [n, hidden], scale fp32 [n],
+        residual_out uint16 [n, hidden] or None) plus the binary64 y when
+        asked.  residual None is plain RMSNorm."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        weight = np.ascontiguousarray(weight, dtype=np.uint16)
+        if residual is not None:
+            residual = np.ascontiguousarray(residual, dtype=np.uint16)
+            if residual.shape != x.shape:
+                raise ValueError("shape mismatch")
+        if x.ndim != 2 or weight.shape != (x.shape[1],):
+            raise ValueError("shape mismatch")
+        n, h = x.shape
+        q = np.empty(x.shape, dtype=np.uint8)
+        sc = np.empty(n, dtype=np.float32)
+        res_out = np.empty_like(x) if residual is not None else None
+        y = np.empty(x.shape, dtype=np.float64) if want_exact else None
+        rc = self.lib.orc_add_rmsnorm_quant_fp8(
+            _ptr(q), _ptr(sc), _ptr(res_out) if res_out is not None else None,
+            _ptr(y) if y is not None else None, _ptr(x),
+            _ptr(residual) if residual is not None else None, _ptr(weight), n, h,
+            ctypes.c_float(eps))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+        return (q, sc, res_out, y) if want_exact else (q, sc, res_out)
+
+
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
@@ -271,6 +311,23 @@ def add_rmsnorm(x, residual, weight, eps: float = 1e-6, rounding: int = RNE,
 
 def add_rmsnorm_quant(x, residual, weight, eps: float = 1e-6, want_exact: bool = False):
     return default().add_rmsnorm_quant(x, residual, weight, eps, want_exact)
+
+
+def add_rmsnorm_quant_fp8(x, residual, weight, eps: float = 1e-6, want_exact: bool = False):
+    return default().add_rmsnorm_quant_fp8(x, residual, weight, eps, want_exact)
+
+
+def e4m3_rne(v: float) -> int:
+    return default().e4m3_rne(v)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact values of e4m3fn codes (NaN for the NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
 
 
 def rmsnorm(x, weight, eps: float = 1e-6, rounding: int = RNE, want_exact: bool = False):

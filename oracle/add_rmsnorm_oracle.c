@@ -264,3 +264,95 @@ int orc_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, doubl
   }
   return 0;
 }
+
+/*
+ * OCP FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 holds the subnormals m/8 * 2^-6, fields 1..15 hold
+ * (1 + m/8) * 2^(E-7), except E = 15, m = 7, which is NaN.  The largest
+ * finite value is 448; there are no infinities.
+ */
+static double e4m3_value(int code) { /* code 0..126, non-negative */
+  const int e = code >> 3, m = code & 7;
+  if (e == 0) return ldexp((double)m, -9);
+  return ldexp(1.0 + m / 8.0, e - 7);
+}
+
+/*
+ * The e4m3 code nearest to the binary32 value v, ties to the even code
+ * (mantissa bit 0 clear), magnitudes beyond 448 saturating to 448.  The sign
+ * of v is kept (-0 and tiny negatives give 0x80).  v is finite.  Found by
+ * walking the 127 non-negative finite values in order.
+ */
+int orc_e4m3_rne(float v) {
+  const double a = fabs((double)v);
+  const int sign = signbit(v) ? 0x80 : 0;
+  if (a >= 448.0) return sign | 0x7E;
+  int lo = 0;
+  while (lo < 126 && e4m3_value(lo + 1) <= a) ++lo;
+  int code = lo;
+  if (e4m3_value(lo) != a) {
+    const double dlo = a - e4m3_value(lo), dhi = e4m3_value(lo + 1) - a;
+    if (dhi < dlo || (dhi == dlo && (lo & 1))) code = lo + 1;
+  }
+  return sign | code;
+}
+
+/*
+ * Quantised out in FP8 E4M3, the other scaled cast of the aiter issue's
+ * quantised configurations besides int8 ("Cost of fixing").  The pages do
+ * not give the cast; the reading taken mirrors the int8 one with the E4M3
+ * range:
+ *   y_j   = (acc_j * rinv) * w_j            (binary64, as in orc_add_rmsnorm)
+ *   amax  = max_j |y_j|
+ *   scale = amax / 448
+ *   q_j   = e4m3_rne(y_j * (448 / amax))    (saturating at +-448)
+ * A row is quantised only when 448 / amax is a finite binary32 number, taken
+ * as 2^-118 <= amax <= FLT_MAX; other rows (amax 0, tiny, Inf or NaN) get
+ * all-zero codes, and their scale is still amax / 448.  As for int8, the
+ * decisions are taken in binary32 from y rounded once.  q holds the codes as
+ * bytes.  Plain RMSNorm: residual and residual_out NULL.
+ */
+int orc_add_rmsnorm_quant_fp8(uint8_t* q, float* scale, uint16_t* residual_out, double* y_exact,
+                              const uint16_t* x, const uint16_t* residual, const uint16_t* weight,
+                              int64_t n_rows, int64_t hidden, float eps) {
+  if (n_rows < 0 || hidden <= 0) return -1;
+  if (n_rows == 0) return 0;
+  if (!q || !scale || !x || !weight || !residual != !residual_out) return -1;
+
+  const double f32_overflow = ldexp(2.0 - ldexp(1.0, -24), 127);
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const uint16_t* xr = x + i * hidden;
+    const uint16_t* rr = residual ? residual + i * hidden : NULL;
+    double s = 0.0;
+    for (int64_t j = 0; j < hidden; ++j) {
+      float acc = row_acc(xr, rr, j);
+      if (residual_out) residual_out[i * hidden + j] = orc_rne16(f32_bits(acc));
+      double a = (double)acc;
+      s += a * a;
+    }
+    if (s >= f32_overflow) s = INFINITY;
+    double rinv = 1.0 / sqrt(s / (double)hidden + (double)eps);
+
+    float amax = 0.0f;
+    for (int64_t j = 0; j < hidden; ++j) {
+      double a = (double)row_acc(xr, rr, j);
+      double y = (a * rinv) * (double)bf16_to_f32(weight[j]);
+      if (y_exact) y_exact[i * hidden + j] = y;
+      amax = max_nan(amax, fabsf((float)y));
+    }
+    const float sc = amax / 448.0f;
+    const float inv = 448.0f / amax;
+    scale[i] = sc;
+    const int ok = isfinite(amax) && amax >= ldexpf(1.0f, -118);
+    for (int64_t j = 0; j < hidden; ++j) {
+      uint8_t code = 0;
+      if (ok) {
+        double a = (double)row_acc(xr, rr, j);
+        float y32 = (float)((a * rinv) * (double)bf16_to_f32(weight[j]));
+        code = (uint8_t)orc_e4m3_rne(y32 * inv);
+      }
+      q[i * hidden + j] = code;
+    }
+  }
+  return 0;
+}
