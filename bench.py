@@ -17,7 +17,7 @@ the weight once), the HBM roofline fraction against 8 TB/s, and the CPU
 oracle timed on the host as a baseline.
 
   python bench.py [--steps K] [--warmup W] [--workload 4096x8192]
-                  [--op bf16|quant|plain|plain_quant]
+                  [--op bf16|quant|quant_fp8|plain|plain_quant|plain_quant_fp8|general|log1p]
                   [--no-cpu-baseline] [--calibrate-copy]
 """
 from __future__ import annotations
@@ -37,10 +37,14 @@ PEAK_HBM_GBPS = 8000.0
 CACHE_DEFEAT_BYTES = 1 << 30  # rotate buffer sets until the footprint is >= 1 GiB
 
 
-OPS = ("bf16", "quant", "plain", "plain_quant", "general", "log1p")
-ENTRY = {"bf16": "add_rmsnorm_fwd", "quant": "add_rmsnorm_quant_fwd", "plain": "rmsnorm_fwd",
-         "plain_quant": "rmsnorm_quant_fwd", "general": "add_rmsnorm_fwd (general kernel)",
-         "log1p": "log1p_f32"}
+OPS = ("bf16", "quant", "quant_fp8", "plain", "plain_quant", "plain_quant_fp8", "general",
+       "log1p")
+ENTRY = {"bf16": "add_rmsnorm_fwd", "quant": "add_rmsnorm_quant_fwd",
+         "quant_fp8": "add_rmsnorm_quant_fp8_fwd", "plain": "rmsnorm_fwd",
+         "plain_quant": "rmsnorm_quant_fwd", "plain_quant_fp8": "rmsnorm_quant_fp8_fwd",
+         "general": "add_rmsnorm_fwd (general kernel)", "log1p": "log1p_f32"}
+QUANT_OPS = ("quant", "quant_fp8", "plain_quant", "plain_quant_fp8")
+PLAIN_OPS = ("plain", "plain_quant", "plain_quant_fp8")
 
 
 def algorithmic_bytes(n_rows: int, hidden: int, op: str = "bf16") -> int:
@@ -49,8 +53,9 @@ def algorithmic_bytes(n_rows: int, hidden: int, op: str = "bf16") -> int:
     for the quantised variants 1 byte of code per element and a 4-byte scale
     per row); the weight read once.  Plain RMSNorm has no residual and no
     residual_out."""
-    per_elem = {"bf16": 8, "general": 8, "quant": 7, "plain": 4, "plain_quant": 3}[op]
-    per_row = 4 if op in ("quant", "plain_quant") else 0
+    per_elem = {"bf16": 8, "general": 8, "quant": 7, "quant_fp8": 7, "plain": 4,
+                "plain_quant": 3, "plain_quant_fp8": 3}[op]
+    per_row = 4 if op in QUANT_OPS else 0
     return per_elem * n_rows * hidden + per_row * n_rows + 2 * hidden
 
 
@@ -61,8 +66,9 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="4096x8192")
     p.add_argument("--op", choices=OPS, default="bf16",
-                   help="bf16: the fused op (the benchmark); quant: its int8-quantised "
-                        "variant; plain, plain_quant: RMSNorm without the residual add; "
+                   help="bf16: the fused op (the benchmark); quant, quant_fp8: its int8- "
+                        "and FP8 E4M3-quantised variants; plain, plain_quant, "
+                        "plain_quant_fp8: RMSNorm without the residual add; "
                         "general: the fused op on the general kernel (the workload's hidden "
                         "minus one, so rows leave 16-byte alignment); "
                         "log1p: the correctly rounded binary32 log1p")
@@ -153,6 +159,10 @@ def cpu_baseline(x, r, w, eps, n_rows, hidden, budget_s, op="bf16"):
             oracle.rmsnorm(x, w, eps)
         elif op == "plain_quant":
             oracle.rmsnorm_quant(x, w, eps)
+        elif op == "quant_fp8":
+            oracle.add_rmsnorm_quant_fp8(x, r, w, eps)
+        elif op == "plain_quant_fp8":
+            oracle.add_rmsnorm_quant_fp8(x, None, w, eps)
         else:
             oracle.add_rmsnorm(x, r, w, eps)
         passes += 1
@@ -341,7 +351,7 @@ def main(argv=None):
     eps = 1e-6
     x, r, w = synth.workload(cfg["seed"], n_rows, hidden)
     tensor_bytes = n_rows * hidden * 2
-    plain = args.op in ("plain", "plain_quant")
+    plain = args.op in PLAIN_OPS
     touched = (2 if plain else 4) * tensor_bytes   # bf16 tensors one step reads or writes
     sets = max(1, -(-CACHE_DEFEAT_BYTES // touched))
     xd0 = torch.from_numpy(x.view(np.int16)).to(dev)
@@ -353,9 +363,10 @@ def main(argv=None):
         rd = rd0 if i == 0 else rd0.clone()
         bufs.append((torch.empty_like(xd), torch.empty_like(xd), xd, rd))
     qbufs = []
-    if args.op in ("quant", "plain_quant"):
+    if args.op in QUANT_OPS:
+        code_dtype = torch.uint8 if args.op.endswith("fp8") else torch.int8
         for i in range(sets):
-            qbufs.append((torch.empty(n_rows, hidden, dtype=torch.int8, device=dev),
+            qbufs.append((torch.empty(n_rows, hidden, dtype=code_dtype, device=dev),
                           torch.empty(n_rows, dtype=torch.float32, device=dev)))
     torch.cuda.synchronize()
 
@@ -371,6 +382,12 @@ def main(argv=None):
         elif args.op == "plain_quant":
             q, sc = qbufs[i % sets]
             arn.rmsnorm_quant_fwd(q, sc, xd, wd, eps)
+        elif args.op == "quant_fp8":
+            q, sc = qbufs[i % sets]
+            arn.add_rmsnorm_quant_fp8_fwd(q, sc, ro, xd, rd, wd, eps)
+        elif args.op == "plain_quant_fp8":
+            q, sc = qbufs[i % sets]
+            arn.rmsnorm_quant_fp8_fwd(q, sc, xd, wd, eps)
         else:
             arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, eps)
 
@@ -412,6 +429,10 @@ def main(argv=None):
     line = {
         "metric": {"bf16": "fused add+RMSNorm HBM GB/s and % of peak, n=4096 x hidden=8192 bf16",
                    "quant": "fused add+RMSNorm, int8-quantised out, HBM GB/s and % of peak",
+                   "quant_fp8": "fused add+RMSNorm, FP8 E4M3-quantised out, HBM GB/s and % "
+                                "of peak",
+                   "plain_quant_fp8": "RMSNorm (no residual add), FP8 E4M3-quantised out, HBM "
+                                      "GB/s and % of peak",
                    "plain": "RMSNorm (no residual add), HBM GB/s and % of peak",
                    "plain_quant": "RMSNorm (no residual add), int8-quantised out, HBM GB/s "
                                   "and % of peak",

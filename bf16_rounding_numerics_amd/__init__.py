@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -59,7 +59,10 @@ _lib = None
 EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_fwd_strided",
            "rmsnorm_fwd_strided", "add_rmsnorm_quant_fwd", "add_rmsnorm_quant_fwd_cfg",
            "rmsnorm_fwd", "rmsnorm_fwd_cfg", "rmsnorm_quant_fwd", "rmsnorm_quant_fwd_cfg",
-           "log1p_f32", "log1p_f32_cfg", "add_rmsnorm_test_cvt_range", "add_rmsnorm_test_copy2",
+           "add_rmsnorm_quant_fp8_fwd", "add_rmsnorm_quant_fp8_fwd_cfg", "rmsnorm_quant_fp8_fwd",
+           "rmsnorm_quant_fp8_fwd_cfg", "log1p_f32", "log1p_f32_cfg",
+           "add_rmsnorm_test_cvt_range", "add_rmsnorm_test_cvt_e4m3_range",
+           "add_rmsnorm_test_copy2",
            "add_rmsnorm_test_stream", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
            "add_rmsnorm_abi_version", "add_rmsnorm_build_info")
 
@@ -101,6 +104,18 @@ def lib() -> ctypes.CDLL:
     L.rmsnorm_quant_fwd_cfg.argtypes = [vp, vp, vp, vp, i64, i64, f32,
                                         ctypes.POINTER(LaunchCfg), vp]
     L.log1p_f32.restype = i32
+    for name in ("add_rmsnorm_quant_fp8_fwd", "add_rmsnorm_quant_fp8_fwd_cfg"):
+        getattr(L, name).restype = i32
+    L.add_rmsnorm_quant_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, vp]
+    L.add_rmsnorm_quant_fp8_fwd_cfg.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32,
+                                                ctypes.POINTER(LaunchCfg), vp]
+    L.rmsnorm_quant_fp8_fwd.restype = i32
+    L.rmsnorm_quant_fp8_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, vp]
+    L.rmsnorm_quant_fp8_fwd_cfg.restype = i32
+    L.rmsnorm_quant_fp8_fwd_cfg.argtypes = [vp, vp, vp, vp, i64, i64, f32,
+                                            ctypes.POINTER(LaunchCfg), vp]
+    L.add_rmsnorm_test_cvt_e4m3_range.restype = i32
+    L.add_rmsnorm_test_cvt_e4m3_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
     L.log1p_f32.argtypes = [vp, vp, i64, vp]
     L.log1p_f32_cfg.restype = i32
     L.log1p_f32_cfg.argtypes = [vp, vp, i64, ctypes.POINTER(Log1pCfg), vp]
@@ -242,13 +257,22 @@ def add_rmsnorm_fwd_cfg(out, residual_out, x, residual, weight, eps: float = 1e-
         weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg), h)))
 
 
-def _marshal_quant(out_q, out_scale, residual_out, x, residual, weight):
+def _code_dtypes(fp8: bool):
+    import torch
+
+    if not fp8:
+        return (torch.int8,)
+    return tuple(t for t in (torch.uint8, getattr(torch, "float8_e4m3fn", None)) if t is not None)
+
+
+def _marshal_quant(out_q, out_scale, residual_out, x, residual, weight, fp8=False):
     import torch
 
     n_rows, hidden, dev = _marshal(residual_out, residual_out, x, residual, weight)
-    if not isinstance(out_q, torch.Tensor) or out_q.dtype != torch.int8 or \
+    if not isinstance(out_q, torch.Tensor) or out_q.dtype not in _code_dtypes(fp8) or \
             out_q.shape != x.shape or not out_q.is_contiguous() or out_q.get_device() != dev:
-        raise ValueError("out_q must be a contiguous int8 tensor of x's shape on x's GPU")
+        raise ValueError("out_q must be a contiguous %s tensor of x's shape on x's GPU"
+                         % ("uint8 or float8_e4m3fn" if fp8 else "int8"))
     if not isinstance(out_scale, torch.Tensor) or out_scale.dtype != torch.float32 or \
             out_scale.numel() != n_rows or not out_scale.is_contiguous() or \
             out_scale.get_device() != dev:
@@ -278,6 +302,32 @@ def add_rmsnorm_quant_fwd_cfg(out_q, out_scale, residual_out, x, residual, weigh
     cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fwd_cfg(
+        out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+        residual.data_ptr(), weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg), h)))
+
+
+def add_rmsnorm_quant_fp8_fwd(out_q, out_scale, residual_out, x, residual, weight,
+                              eps: float = 1e-6, stream=None) -> None:
+    """add_rmsnorm_quant_fwd with OCP FP8 E4M3 codes (scale = amax / 448).
+    out_q: uint8 or torch.float8_e4m3fn of x's shape."""
+    n_rows, hidden, dev = _marshal_quant(out_q, out_scale, residual_out, x, residual, weight, True)
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fp8_fwd(
+        out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
+        residual.data_ptr(), weight.data_ptr(), n_rows, hidden, eps, h)))
+
+
+def add_rmsnorm_quant_fp8_fwd_cfg(out_q, out_scale, residual_out, x, residual, weight,
+                                  eps: float = 1e-6, path: int = PATH_AUTO,
+                                  block_threads: int = 0, grid_blocks: int = 0,
+                                  stream=None) -> None:
+    """add_rmsnorm_quant_fp8_fwd with an explicit launch configuration."""
+    n_rows, hidden, dev = _marshal_quant(out_q, out_scale, residual_out, x, residual, weight, True)
+    L = lib()
+    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fp8_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
         residual.data_ptr(), weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg), h)))
 
@@ -381,6 +431,29 @@ def rmsnorm_quant_fwd_cfg(out_q, out_scale, x, weight, eps: float = 1e-6, path: 
         eps, ctypes.byref(cfg), h)))
 
 
+def rmsnorm_quant_fp8_fwd(out_q, out_scale, x, weight, eps: float = 1e-6, stream=None) -> None:
+    """rmsnorm_quant_fwd with OCP FP8 E4M3 codes (out_q uint8 or float8_e4m3fn)."""
+    n_rows, hidden, dev = _marshal_quant(out_q, out_scale, x, x, x, weight, True)
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.rmsnorm_quant_fp8_fwd(
+        out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
+        eps, h)))
+
+
+def rmsnorm_quant_fp8_fwd_cfg(out_q, out_scale, x, weight, eps: float = 1e-6,
+                              path: int = PATH_AUTO, block_threads: int = 0,
+                              grid_blocks: int = 0, stream=None) -> None:
+    """rmsnorm_quant_fp8_fwd with an explicit launch configuration."""
+    n_rows, hidden, dev = _marshal_quant(out_q, out_scale, x, x, x, weight, True)
+    L = lib()
+    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.rmsnorm_quant_fp8_fwd_cfg(
+        out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
+        eps, ctypes.byref(cfg), h)))
+
+
 def _marshal_log1p(out, x):
     import torch
 
@@ -422,6 +495,18 @@ def add_rmsnorm_test_cvt_range(out, start: int, stream=None) -> None:
     L = lib()
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_test_cvt_range(
+        out.data_ptr(), start & 0xFFFFFFFF, out.numel(), h)))
+
+
+def add_rmsnorm_test_cvt_e4m3_range(out, start: int, stream=None) -> None:
+    """out[i] <- E4M3 code (by the fp8 variant's code routine, inv = 1) of the
+    fp32 bit pattern (start + i) mod 2^32.  out: contiguous 8-bit GPU tensor."""
+    if not out.is_cuda or out.element_size() != 1 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous 8-bit GPU tensor")
+    dev = out.get_device()
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_test_cvt_e4m3_range(
         out.data_ptr(), start & 0xFFFFFFFF, out.numel(), h)))
 
 

@@ -332,20 +332,26 @@ int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
                              nullptr, stream);
 }
 
-int add_rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, uint16_t* residual_out,
-                              const uint16_t* x, const uint16_t* residual,
-                              const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
-                              const struct add_rmsnorm_launch_cfg* cfg,
-                              struct ihipStream_t* stream) {
+}  // extern "C"
+
+namespace {
+
+// The quantised entry points, fused (residual set) or plain (residual and
+// residual_out null), with codes in format fmt (1 int8, 2 E4M3).
+int quant_fwd(void* out_q, float* out_scale, uint16_t* residual_out, const uint16_t* x,
+              const uint16_t* residual, const uint16_t* weight, int64_t n_rows, int64_t hidden,
+              float eps, const add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream,
+              int fmt) {
   add_rmsnorm_launch_cfg c;
   int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
   if (rc != ADD_RMSNORM_OK) return rc;
   if (n_rows == 0) return ADD_RMSNORM_OK;
 
-  if (!out_q || !out_scale || !residual_out || !x || !residual || !weight)
+  const bool fused = residual != nullptr || residual_out != nullptr;
+  if (!out_q || !out_scale || !x || !weight || (fused && (!residual || !residual_out)))
     return ADD_RMSNORM_EINVAL;
-  if (!aligned16(out_q) || !aligned(out_scale, 4) || !aligned16(residual_out) || !aligned16(x) ||
-      !aligned16(residual) || !aligned16(weight))
+  if (!aligned16(out_q) || !aligned(out_scale, 4) || !aligned16(x) || !aligned16(weight) ||
+      (fused && (!aligned16(residual_out) || !aligned16(residual))))
     return ADD_RMSNORM_EALIGN;
   const uint64_t row_bytes = (uint64_t)hidden * 2;
   if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
@@ -353,22 +359,46 @@ int add_rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, uint16_t* residua
   const uint64_t q_bytes = (uint64_t)n_rows * (uint64_t)hidden;
   const uint64_t s_bytes = (uint64_t)n_rows * 4;
   // Codes and scales overlap nothing; residual_out as in the bf16 variant.
-  const void* ins[3] = {x, residual, weight};
-  const uint64_t in_bytes[3] = {t_bytes, t_bytes, row_bytes};
-  if (overlap(out_q, q_bytes, out_scale, s_bytes) ||
-      overlap(out_q, q_bytes, residual_out, t_bytes) ||
-      overlap(out_scale, s_bytes, residual_out, t_bytes))
+  const void* ins[3] = {x, weight, residual};
+  const uint64_t in_bytes[3] = {t_bytes, row_bytes, t_bytes};
+  const int n_ins = fused ? 3 : 2;
+  if (overlap(out_q, q_bytes, out_scale, s_bytes)) return ADD_RMSNORM_EALIAS;
+  if (fused && (overlap(out_q, q_bytes, residual_out, t_bytes) ||
+                overlap(out_scale, s_bytes, residual_out, t_bytes)))
     return ADD_RMSNORM_EALIAS;
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < n_ins; ++i)
     if (overlap(out_q, q_bytes, ins[i], in_bytes[i]) ||
         overlap(out_scale, s_bytes, ins[i], in_bytes[i]))
       return ADD_RMSNORM_EALIAS;
-  if (output_aliases_badly(residual_out, t_bytes, x, residual, weight, row_bytes))
+  if (fused && output_aliases_badly(residual_out, t_bytes, x, residual, weight, row_bytes))
     return ADD_RMSNORM_EALIAS;
 
-  const addrms::FwdArgs a = {nullptr, out_q, out_scale, residual_out, x, residual, weight,
-                             n_rows, (int32_t)hidden, eps, hidden, hidden, hidden, hidden};
+  const addrms::FwdArgs a = {nullptr,  out_q,  out_scale, residual_out,
+                             x,        residual, weight,  n_rows,
+                             (int32_t)hidden, eps, hidden, fused ? hidden : 0,
+                             hidden,   fused ? hidden : 0, fmt};
   return dispatch(a, c, stream);
+}
+
+constexpr int kFmtInt8 = 1;
+constexpr int kFmtFp8 = 2;
+
+}  // namespace
+
+extern "C" {
+
+int add_rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, uint16_t* residual_out,
+                              const uint16_t* x, const uint16_t* residual,
+                              const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                              const struct add_rmsnorm_launch_cfg* cfg,
+                              struct ihipStream_t* stream) {
+  if (!residual || !residual_out) {
+    add_rmsnorm_launch_cfg c;
+    const int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
+    return rc != ADD_RMSNORM_OK ? rc : n_rows == 0 ? ADD_RMSNORM_OK : ADD_RMSNORM_EINVAL;
+  }
+  return quant_fwd(out_q, out_scale, residual_out, x, residual, weight, n_rows, hidden, eps, cfg,
+                   stream, kFmtInt8);
 }
 
 int add_rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, uint16_t* residual_out,
@@ -377,6 +407,28 @@ int add_rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, uint16_t* residual_ou
                           struct ihipStream_t* stream) {
   return add_rmsnorm_quant_fwd_cfg(out_q, out_scale, residual_out, x, residual, weight, n_rows,
                                    hidden, eps, nullptr, stream);
+}
+
+int add_rmsnorm_quant_fp8_fwd_cfg(uint8_t* out_q, float* out_scale, uint16_t* residual_out,
+                                  const uint16_t* x, const uint16_t* residual,
+                                  const uint16_t* weight, int64_t n_rows, int64_t hidden,
+                                  float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                                  struct ihipStream_t* stream) {
+  if (!residual || !residual_out) {
+    add_rmsnorm_launch_cfg c;
+    const int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
+    return rc != ADD_RMSNORM_OK ? rc : n_rows == 0 ? ADD_RMSNORM_OK : ADD_RMSNORM_EINVAL;
+  }
+  return quant_fwd(out_q, out_scale, residual_out, x, residual, weight, n_rows, hidden, eps, cfg,
+                   stream, kFmtFp8);
+}
+
+int add_rmsnorm_quant_fp8_fwd(uint8_t* out_q, float* out_scale, uint16_t* residual_out,
+                              const uint16_t* x, const uint16_t* residual,
+                              const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                              struct ihipStream_t* stream) {
+  return add_rmsnorm_quant_fp8_fwd_cfg(out_q, out_scale, residual_out, x, residual, weight,
+                                       n_rows, hidden, eps, nullptr, stream);
 }
 
 int rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, const uint16_t* x, int64_t x_stride,
@@ -401,34 +453,29 @@ int rmsnorm_fwd(uint16_t* out, const uint16_t* x, const uint16_t* weight, int64_
 int rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, const uint16_t* x,
                           const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
                           const struct add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream) {
-  add_rmsnorm_launch_cfg c;
-  int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
-  if (rc != ADD_RMSNORM_OK) return rc;
-  if (n_rows == 0) return ADD_RMSNORM_OK;
-
-  if (!out_q || !out_scale || !x || !weight) return ADD_RMSNORM_EINVAL;
-  if (!aligned16(out_q) || !aligned(out_scale, 4) || !aligned16(x) || !aligned16(weight))
-    return ADD_RMSNORM_EALIGN;
-  const uint64_t row_bytes = (uint64_t)hidden * 2;
-  if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
-  const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
-  const uint64_t q_bytes = (uint64_t)n_rows * (uint64_t)hidden;
-  const uint64_t s_bytes = (uint64_t)n_rows * 4;
-  // Codes and scales overlap nothing.
-  if (overlap(out_q, q_bytes, out_scale, s_bytes) || overlap(out_q, q_bytes, x, t_bytes) ||
-      overlap(out_q, q_bytes, weight, row_bytes) || overlap(out_scale, s_bytes, x, t_bytes) ||
-      overlap(out_scale, s_bytes, weight, row_bytes))
-    return ADD_RMSNORM_EALIAS;
-
-  const addrms::FwdArgs a = {nullptr, out_q, out_scale, nullptr, x, nullptr, weight,
-                             n_rows, (int32_t)hidden, eps, hidden, 0, hidden, 0};
-  return dispatch(a, c, stream);
+  return quant_fwd(out_q, out_scale, nullptr, x, nullptr, weight, n_rows, hidden, eps, cfg,
+                   stream, kFmtInt8);
 }
 
 int rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, const uint16_t* x, const uint16_t* weight,
                       int64_t n_rows, int64_t hidden, float eps, struct ihipStream_t* stream) {
   return rmsnorm_quant_fwd_cfg(out_q, out_scale, x, weight, n_rows, hidden, eps, nullptr,
                                stream);
+}
+
+int rmsnorm_quant_fp8_fwd_cfg(uint8_t* out_q, float* out_scale, const uint16_t* x,
+                              const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                              const struct add_rmsnorm_launch_cfg* cfg,
+                              struct ihipStream_t* stream) {
+  return quant_fwd(out_q, out_scale, nullptr, x, nullptr, weight, n_rows, hidden, eps, cfg,
+                   stream, kFmtFp8);
+}
+
+int rmsnorm_quant_fp8_fwd(uint8_t* out_q, float* out_scale, const uint16_t* x,
+                          const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                          struct ihipStream_t* stream) {
+  return rmsnorm_quant_fp8_fwd_cfg(out_q, out_scale, x, weight, n_rows, hidden, eps, nullptr,
+                                   stream);
 }
 
 int log1p_f32_cfg(float* out, const float* x, int64_t n, const struct log1p_launch_cfg* cfg,
@@ -466,6 +513,19 @@ int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,
   if (!out) return ADD_RMSNORM_EINVAL;
   if (!aligned16(out)) return ADD_RMSNORM_EALIGN;
   hipError_t e = addrms::launch_cvt_range(out, start, count, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_failure(e);
+  return ADD_RMSNORM_OK;
+}
+
+int add_rmsnorm_test_cvt_e4m3_range(uint8_t* out, uint32_t start, int64_t count,
+                                    struct ihipStream_t* stream) {
+  if (count < 0) return ADD_RMSNORM_EINVAL;
+  if (count % 8 != 0) return ADD_RMSNORM_EALIGN;
+  if (count == 0) return ADD_RMSNORM_OK;
+  if (!out) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(out)) return ADD_RMSNORM_EALIGN;
+  hipError_t e =
+      addrms::launch_cvt_e4m3_range(out, start, count, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_failure(e);
   return ADD_RMSNORM_OK;
 }

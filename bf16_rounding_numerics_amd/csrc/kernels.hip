@@ -36,6 +36,12 @@
 //     [-127, 127].  The inverse must be finite, so a row is quantised only
 //     when 2^-120 <= amax <= FLT_MAX; other rows (amax 0, tiny, Inf or NaN)
 //     get all-zero codes, and their scale is still amax / 127.
+//     The same with OCP FP8 E4M3 codes (Q = 2): 448 (E4M3's largest finite
+//     value) in place of 127, threshold 2^-118, and the code of y * inv is
+//     its nearest E4M3 value, ties to even, from gfx950's packed fp32 -> fp8
+//     conversion (v_cvt_pk_fp8_f32, OCP formats on this architecture).
+//     |y * inv| <= 448 (1 + 2^-23) always rounds to at most 448, so no code
+//     is NaN.
 //   * Plain variant (template flag R false): RMSNorm without the residual
 //     add.  acc = x exactly (no add at all: adding a zero would turn -0 into
 //     +0), and there is no residual_out; everything after acc is the same.
@@ -56,7 +62,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct Params {
   u32x4* out;           // bf16 out (plain variant)
-  u32x2* qout;          // int8 codes, 8 per segment (quantised variant)
+  u32x2* qout;          // 1-byte codes, 8 per segment (quantised variants)
   float* qscale;        // per-row scale (quantised variant)
   u32x4* residual_out;
   const u32x4* x;
@@ -227,23 +233,50 @@ DEV float max_abs8(float m, const float (&y)[8]) {
   return m;
 }
 
-// Whether a row's codes are taken from y * inv: 127 / amax must be finite,
-// so 2^-120 <= amax <= FLT_MAX (false for NaN).
-DEV bool quantisable(float amax) { return amax >= 0x1p-120f && amax <= 3.40282347e38f; }
+// Code formats of the quantised variants (template parameter Q): 1 int8,
+// 2 OCP FP8 E4M3; 0 is the bf16-out variant.  Codes are bytes either way.
+constexpr int kQInt8 = 1;
+constexpr int kQFp8 = 2;
 
-// int8 codes of one segment: nearest-even integer of y * inv, kept within
-// [-127, 127].
+// The largest code magnitude: scale = amax / qmax, inv = qmax / amax.
+template <int Q>
+constexpr float qmax() {
+  return Q == kQInt8 ? 127.0f : 448.0f;
+}
+
+// Whether a row's codes are taken from y * inv: qmax / amax must be finite,
+// so 2^-120 (int8) or 2^-118 (E4M3) <= amax <= FLT_MAX (false for NaN).
+template <int Q>
+DEV bool quantisable(float amax) {
+  return amax >= (Q == kQInt8 ? 0x1p-120f : 0x1p-118f) && amax <= 3.40282347e38f;
+}
+
+// Codes of one segment.  int8: nearest-even integer of y * inv, kept within
+// [-127, 127].  E4M3: the packed conversion of y * inv, two values per
+// instruction.
+template <int Q>
 DEV u32x2 quant8(const float (&y)[8], float inv) {
-  uint32_t w0 = 0, w1 = 0;
+  if constexpr (Q == kQInt8) {
+    uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float t = __builtin_rintf(y[k] * inv);
-    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
-    const uint32_t c = (uint32_t)(int)t & 0xFFu;
-    if (k < 4) w0 |= c << (8 * k);
-    else w1 |= c << (8 * (k - 4));
+    for (int k = 0; k < 8; ++k) {
+      float t = __builtin_rintf(y[k] * inv);
+      t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+      const uint32_t c = (uint32_t)(int)t & 0xFFu;
+      if (k < 4) w0 |= c << (8 * k);
+      else w1 |= c << (8 * (k - 4));
+    }
+    return u32x2{w0, w1};
+  } else {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = y[k] * inv;
+    uint32_t w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], (int)w0, true);
+    uint32_t w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], (int)w1, true);
+    return u32x2{w0, w1};
   }
-  return u32x2{w0, w1};
 }
 
 // acc = x + r for one segment (acc = x in the plain variant), without the
@@ -289,7 +322,7 @@ DEV float add_segment(u32x4 xq, u32x4 rq, float (&acc)[8]) {
 // per-lane register footprint small enough for more rows in flight per CU.
 // Rows are read and written through per-row buffer resources: segments past
 // the row read as zero and their stores are dropped, so nothing branches.
-template <int WAVES, int J, bool Q, bool R>
+template <int WAVES, int J, int Q, bool R>
 __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
   __shared__ u32x4 wl[64 * J];
   const int lane = threadIdx.x & 63;
@@ -342,9 +375,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
         if (lane + 64 * j < C) m = max_abs8(m, y);
       }
       const float amax = wave_max(m);
-      const float scale = amax / 127.0f;
-      const float inv = 127.0f / amax;
-      const bool ok = quantisable(amax);
+      const float scale = amax / qmax<Q>();
+      const float inv = qmax<Q>() / amax;
+      const bool ok = quantisable<Q>(amax);
       if (lane == 0) p.qscale[row] = scale;
       const __amdgpu_buffer_rsrc_t qo = code_row_rsrc(p.qout, row, C);
 #pragma unroll
@@ -352,7 +385,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
         float acc[8], y[8];
         add8<R>(opaque(xq[j]), opaque(rq[j]), acc);
         scale8(acc, rinv, wl[opaque(lane + 64 * j)], y);
-        store_codes(qo, lane + 64 * j, ok ? quant8(y, inv) : u32x2{0, 0});
+        store_codes(qo, lane + 64 * j, ok ? quant8<Q>(y, inv) : u32x2{0, 0});
       }
     }
   }
@@ -363,7 +396,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 // B threads per row; thread t holds segments t, t + B, ..., t + B (J - 1).
 // For each j, wave w's butterfly yields the sum of block w + j * (B / 64);
 // the B / 64 * J block sums meet in LDS and every thread finishes the tree.
-template <int B, int J, bool Q, bool R>
+template <int B, int J, int Q, bool R>
 __global__ __launch_bounds__(B) void k_wg_row(Params p) {
   constexpr int W = B / 64;
   constexpr int NB = W * J;
@@ -436,14 +469,14 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
       float amax = mx[parity][0];
 #pragma unroll
       for (int i = 1; i < W; ++i) amax = max_nan(amax, mx[parity][i]);
-      const float scale = amax / 127.0f;
-      const float inv = 127.0f / amax;
-      const bool ok = quantisable(amax);
+      const float scale = amax / qmax<Q>();
+      const float inv = qmax<Q>() / amax;
+      const bool ok = quantisable<Q>(amax);
       if (t == 0) p.qscale[row] = scale;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int s = t + B * j;
-        if (s < C) store_codes_stream(p.qout + base + s, ok ? quant8(acc[j], inv) : u32x2{0, 0});
+        if (s < C) store_codes_stream(p.qout + base + s, ok ? quant8<Q>(acc[j], inv) : u32x2{0, 0});
       }
     }
   }
@@ -461,7 +494,7 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
 // each wavefront keeps U chunks of x and residual in flight.  Loads go
 // through a per-row buffer resource: segments past the row read as zero,
 // without a branch.
-template <int B, int NB, int U, bool Q, bool R>
+template <int B, int NB, int U, int Q, bool R>
 __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
   constexpr int W = B / 64;
   __shared__ float blk[NB];
@@ -534,9 +567,9 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
       float amax = mx[0];
 #pragma unroll
       for (int i = 1; i < W; ++i) amax = max_nan(amax, mx[i]);
-      const float scale = amax / 127.0f;
-      const float inv = 127.0f / amax;
-      const bool ok = quantisable(amax);
+      const float scale = amax / qmax<Q>();
+      const float inv = qmax<Q>() / amax;
+      const bool ok = quantisable<Q>(amax);
       if (t == 0) p.qscale[row] = scale;
       for (int c = 0; c < chunks; ++c) {
         const int s = c * B + t;
@@ -545,7 +578,7 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
           const float acc[8] = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
           float y[8];
           scale8(acc, rinv, p.weight[s], y);
-          store_codes_stream(p.qout + base + s, ok ? quant8(y, inv) : u32x2{0, 0});
+          store_codes_stream(p.qout + base + s, ok ? quant8<Q>(y, inv) : u32x2{0, 0});
         }
       }
     }
@@ -854,6 +887,20 @@ __global__ __launch_bounds__(256) void k_cvt_range(u32x4* out, uint32_t start, i
   }
 }
 
+// out[i] = E4M3 code of the fp32 with bit pattern start + i, through the
+// quantised variant's code routine with inv = 1 (y * 1 = y exactly).
+__global__ __launch_bounds__(256) void k_cvt_e4m3_range(u32x2* out, uint32_t start,
+                                                        int64_t groups) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
+    const uint32_t u0 = start + (uint32_t)(g * 8);
+    float a[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = __builtin_bit_cast(float, u0 + (uint32_t)k);
+    out[g] = quant8<kQFp8>(a, 1.0f);
+  }
+}
+
 // ---------------------------------------------------------------- copy reference
 
 // Two streaming copies with the fused kernels' access pattern (16-byte
@@ -962,7 +1009,7 @@ hipError_t launch(K kernel, int block_threads, size_t lds, int64_t grid_blocks,
 // Combinations that would not fit the register file (segments held per thread
 // times threads per workgroup) are not built; wave_row_supported() and
 // wg_row_supported() say which exist.
-template <bool Q, bool R, int WAVES>
+template <int Q, bool R, int WAVES>
 hipError_t go_wave(const Params& p, int j, int64_t grid, hipStream_t s) {
   const int64_t groups = (p.n_rows + WAVES - 1) / WAVES;
   switch (j) {
@@ -977,7 +1024,7 @@ hipError_t go_wave(const Params& p, int j, int64_t grid, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <bool Q, bool R, int B>
+template <int Q, bool R, int B>
 hipError_t go_wg(const Params& p, int j, int64_t grid, hipStream_t s) {
   switch (j) {
     case 1: return launch(k_wg_row<B, 1, Q, R>, B, 0, grid, p.n_rows, p, s);
@@ -994,7 +1041,7 @@ hipError_t go_wg(const Params& p, int j, int64_t grid, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <bool Q, bool R, int B>
+template <int Q, bool R, int B>
 hipError_t go_two_pass(const Params& p, int hidden, int64_t grid, hipStream_t s) {
   const size_t lds = (size_t)p.segs * 32;
   if (two_pass_nb(hidden) == 32)
@@ -1003,7 +1050,7 @@ hipError_t go_two_pass(const Params& p, int hidden, int64_t grid, hipStream_t s)
   return launch(k_lds_two_pass<B, 64, two_pass_batch<B>(), Q, R>, B, lds, grid, p.n_rows, p, s);
 }
 
-template <bool Q, bool R>
+template <int Q, bool R>
 hipError_t wave_by_block(const Params& p, int b, int j, int64_t grid, hipStream_t s) {
   switch (b) {
     case 64: return go_wave<Q, R, 1>(p, j, grid, s);
@@ -1015,7 +1062,7 @@ hipError_t wave_by_block(const Params& p, int b, int j, int64_t grid, hipStream_
   return hipErrorInvalidValue;
 }
 
-template <bool Q, bool R>
+template <int Q, bool R>
 hipError_t wg_by_block(const Params& p, int b, int j, int64_t grid, hipStream_t s) {
   switch (b) {
     case 64: return go_wg<Q, R, 64>(p, j, grid, s);
@@ -1027,7 +1074,7 @@ hipError_t wg_by_block(const Params& p, int b, int j, int64_t grid, hipStream_t 
   return hipErrorInvalidValue;
 }
 
-template <bool Q, bool R>
+template <int Q, bool R>
 hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, hipStream_t s) {
   switch (b) {
     case 64: return go_two_pass<Q, R, 64>(p, hidden, grid, s);
@@ -1137,39 +1184,51 @@ hipError_t general_by_block(const GenParams& p, int b, int hidden, int64_t grid,
   return hipErrorInvalidValue;
 }
 
-// The variant is chosen by which outputs and inputs are set: quantised when
-// codes are requested, plain when there is no residual.
+// The variant is chosen by the arguments: quantised, in the format qfmt,
+// when codes are requested, plain when there is no residual.
 hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
                            int64_t grid_blocks, hipStream_t s) {
   const Params p = make_params(a);
   const int b = block_threads, j = segs_per_lane;
-  if (a.qout)
-    return a.residual ? wave_by_block<true, true>(p, b, j, grid_blocks, s)
-                      : wave_by_block<true, false>(p, b, j, grid_blocks, s);
-  return a.residual ? wave_by_block<false, true>(p, b, j, grid_blocks, s)
-                    : wave_by_block<false, false>(p, b, j, grid_blocks, s);
+  if (a.qout && a.qfmt == kQInt8)
+    return a.residual ? wave_by_block<kQInt8, true>(p, b, j, grid_blocks, s)
+                      : wave_by_block<kQInt8, false>(p, b, j, grid_blocks, s);
+  if (a.qout && a.qfmt == kQFp8)
+    return a.residual ? wave_by_block<kQFp8, true>(p, b, j, grid_blocks, s)
+                      : wave_by_block<kQFp8, false>(p, b, j, grid_blocks, s);
+  if (a.qout) return hipErrorInvalidValue;
+  return a.residual ? wave_by_block<0, true>(p, b, j, grid_blocks, s)
+                    : wave_by_block<0, false>(p, b, j, grid_blocks, s);
 }
 
 hipError_t launch_wg_row(const FwdArgs& a, int block_threads, int segs_per_thread,
                          int64_t grid_blocks, hipStream_t s) {
   const Params p = make_params(a);
   const int b = block_threads, j = segs_per_thread;
-  if (a.qout)
-    return a.residual ? wg_by_block<true, true>(p, b, j, grid_blocks, s)
-                      : wg_by_block<true, false>(p, b, j, grid_blocks, s);
-  return a.residual ? wg_by_block<false, true>(p, b, j, grid_blocks, s)
-                    : wg_by_block<false, false>(p, b, j, grid_blocks, s);
+  if (a.qout && a.qfmt == kQInt8)
+    return a.residual ? wg_by_block<kQInt8, true>(p, b, j, grid_blocks, s)
+                      : wg_by_block<kQInt8, false>(p, b, j, grid_blocks, s);
+  if (a.qout && a.qfmt == kQFp8)
+    return a.residual ? wg_by_block<kQFp8, true>(p, b, j, grid_blocks, s)
+                      : wg_by_block<kQFp8, false>(p, b, j, grid_blocks, s);
+  if (a.qout) return hipErrorInvalidValue;
+  return a.residual ? wg_by_block<0, true>(p, b, j, grid_blocks, s)
+                    : wg_by_block<0, false>(p, b, j, grid_blocks, s);
 }
 
 hipError_t launch_lds_two_pass(const FwdArgs& a, int block_threads, int64_t grid_blocks,
                                hipStream_t s) {
   const Params p = make_params(a);
   const int b = block_threads, h = a.hidden;
-  if (a.qout)
-    return a.residual ? two_pass_by_block<true, true>(p, b, h, grid_blocks, s)
-                      : two_pass_by_block<true, false>(p, b, h, grid_blocks, s);
-  return a.residual ? two_pass_by_block<false, true>(p, b, h, grid_blocks, s)
-                    : two_pass_by_block<false, false>(p, b, h, grid_blocks, s);
+  if (a.qout && a.qfmt == kQInt8)
+    return a.residual ? two_pass_by_block<kQInt8, true>(p, b, h, grid_blocks, s)
+                      : two_pass_by_block<kQInt8, false>(p, b, h, grid_blocks, s);
+  if (a.qout && a.qfmt == kQFp8)
+    return a.residual ? two_pass_by_block<kQFp8, true>(p, b, h, grid_blocks, s)
+                      : two_pass_by_block<kQFp8, false>(p, b, h, grid_blocks, s);
+  if (a.qout) return hipErrorInvalidValue;
+  return a.residual ? two_pass_by_block<0, true>(p, b, h, grid_blocks, s)
+                    : two_pass_by_block<0, false>(p, b, h, grid_blocks, s);
 }
 
 bool wave_row_supported(int block_threads, int segs_per_lane) {
@@ -1261,6 +1320,16 @@ hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const ui
   hipLaunchKernelGGL(k_copy2, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<u32x4*>(d0),
                      reinterpret_cast<u32x4*>(d1), reinterpret_cast<const u32x4*>(s0),
                      reinterpret_cast<const u32x4*>(s1), segs);
+  return hipGetLastError();
+}
+
+hipError_t launch_cvt_e4m3_range(uint8_t* out, uint32_t start, int64_t count, hipStream_t s) {
+  const int64_t groups = count / 8;
+  int64_t blocks = (groups + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_cvt_e4m3_range, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<u32x2*>(out), start, groups);
   return hipGetLastError();
 }
 

@@ -9,8 +9,8 @@ namespace addrms {
 
 struct FwdArgs {
   uint16_t* out;           // bf16 out, or null for the quantised variant
-  int8_t* qout;            // int8 codes (quantised variant), else null
-  float* qscale;           // per-row scale (quantised variant), else null
+  void* qout;              // 1-byte codes (quantised variants), else null
+  float* qscale;           // per-row scale (quantised variants), else null
   uint16_t* residual_out;  // null for plain RMSNorm
   const uint16_t* x;
   const uint16_t* residual;  // null for plain RMSNorm (acc = x, no residual_out)
@@ -22,6 +22,7 @@ struct FwdArgs {
   // the strides and every pointer aligned to 8 elements (16 bytes); the
   // general kernel takes any hidden and any 2-byte aligned layout.
   int64_t x_stride, r_stride, out_stride, ro_stride;
+  int32_t qfmt;  // code format when qout is set: 1 int8, 2 OCP FP8 E4M3
 };
 
 // Largest number of 8-element segments any row can have.
@@ -31,7 +32,7 @@ constexpr int kMaxSegments = 32768 / 8;
 // segments are spread over the 64 lanes, segs_per_lane (1, 2, 4 or 8) each.
 // grid_blocks > 0 launches that many workgroups, which loop over the rows;
 // -1 launches as many as fit on the device at once; 0 one per row group.
-// The quantised variant runs when FwdArgs::qout is set, plain RMSNorm when
+// The quantised variants run when FwdArgs::qout is set, plain RMSNorm when
 // FwdArgs::residual is null.
 hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lane,
                            int64_t grid_blocks, hipStream_t stream);
@@ -80,5 +81,10 @@ hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const ui
 
 // Test hook: the store epilogue applied to consecutive fp32 bit patterns.
 hipError_t launch_cvt_range(uint16_t* out, uint32_t start, int64_t count, hipStream_t stream);
+
+// E4M3 codes of count consecutive fp32 bit patterns (the quantised variant's
+// code routine with inv = 1); count a multiple of 8.
+hipError_t launch_cvt_e4m3_range(uint8_t* out, uint32_t start, int64_t count,
+                                 hipStream_t stream);
 
 }  // namespace addrms

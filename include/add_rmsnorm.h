@@ -49,7 +49,7 @@ extern "C" {
 /* hipStream_t is a pointer to this opaque struct. */
 struct ihipStream_t;
 
-#define ADD_RMSNORM_ABI_VERSION 5
+#define ADD_RMSNORM_ABI_VERSION 6
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768
@@ -186,6 +186,34 @@ int add_rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, uint16_t* residua
                               struct ihipStream_t* stream);
 
 /*
+ * FP8 quantised variant: add_rmsnorm_quant_fwd with OCP FP8 E4M3 codes
+ * ("e4m3fn": 1 sign, 4 exponent (bias 7) and 3 mantissa bits, largest finite
+ * value 448, no infinities), the fp8 scaled cast among the aiter issue's
+ * quantised configurations ("Cost of fixing"; the cast itself is not given
+ * there, this is the per-row reading with E4M3's range).  Per row:
+ *   out_scale[i]  = amax / 448                        (fp32, correctly rounded)
+ *   inv           = 448 / amax                        (fp32, correctly rounded)
+ *   out_q[i, j]   = the E4M3 value nearest to y_j * inv (fp32), ties to the
+ *                   even code; |y_j * inv| never rounds past 448, so no code
+ *                   is NaN
+ * A row is quantised only when 2^-118 <= amax <= FLT_MAX (448 / amax
+ * finite); other rows get all-zero codes and the scale amax / 448.  Codes
+ * are bytes (0x80 is -0).  Arguments, alignment, aliasing and errors exactly
+ * as add_rmsnorm_quant_fwd.
+ */
+int add_rmsnorm_quant_fp8_fwd(uint8_t* out_q, float* out_scale, uint16_t* residual_out,
+                              const uint16_t* x, const uint16_t* residual,
+                              const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                              struct ihipStream_t* stream);
+
+/* add_rmsnorm_quant_fp8_fwd with an explicit launch configuration (same results). */
+int add_rmsnorm_quant_fp8_fwd_cfg(uint8_t* out_q, float* out_scale, uint16_t* residual_out,
+                                  const uint16_t* x, const uint16_t* residual,
+                                  const uint16_t* weight, int64_t n_rows, int64_t hidden,
+                                  float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                                  struct ihipStream_t* stream);
+
+/*
  * Plain RMSNorm: the row computation above without the residual add, for the
  * other norms with bf16 stores that the aiter issue's "Notes" list beside the
  * fused kernel (the q/k norms, the norm kernel used above hidden 8192).  Per
@@ -230,6 +258,21 @@ int rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, const uint16_t* x,
                           const struct add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream);
 
 /*
+ * Plain RMSNorm with FP8 E4M3 out: rmsnorm_quant_fwd with the codes, scale
+ * and zero-code rule of add_rmsnorm_quant_fp8_fwd.  Arguments as
+ * rmsnorm_quant_fwd.
+ */
+int rmsnorm_quant_fp8_fwd(uint8_t* out_q, float* out_scale, const uint16_t* x,
+                          const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                          struct ihipStream_t* stream);
+
+/* rmsnorm_quant_fp8_fwd with an explicit launch configuration (same results). */
+int rmsnorm_quant_fp8_fwd_cfg(uint8_t* out_q, float* out_scale, const uint16_t* x,
+                              const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
+                              const struct add_rmsnorm_launch_cfg* cfg,
+                              struct ihipStream_t* stream);
+
+/*
  * Test hook for the store epilogue: out[i] = bf16_rne of the fp32 whose bit
  * pattern is (start + i) mod 2^32, for 0 <= i < count, converted by the same
  * device routine that rounds both stores of the fused kernels.  out is a
@@ -238,6 +281,17 @@ int rmsnorm_quant_fwd_cfg(int8_t* out_q, float* out_scale, const uint16_t* x,
  */
 int add_rmsnorm_test_cvt_range(uint16_t* out, uint32_t start, int64_t count,
                                struct ihipStream_t* stream);
+
+/*
+ * Test hook for the FP8 code routine: out[i] = the E4M3 code (as stored by
+ * the fp8 quantised entry points, with inv = 1) of the fp32 whose bit
+ * pattern is (start + i) mod 2^32.  Meaningful for |value| < 464 (beyond,
+ * the conversion's out-of-range result, which the quantised entry points
+ * never reach).  out: device pointer to count bytes, 16-byte aligned; count
+ * >= 0 and a multiple of 8.  Enqueued on stream.
+ */
+int add_rmsnorm_test_cvt_e4m3_range(uint8_t* out, uint32_t start, int64_t count,
+                                    struct ihipStream_t* stream);
 
 /*
  * Measurement hook: dst0 <- src0 and dst1 <- src1, count 16-bit elements
@@ -263,7 +317,7 @@ int add_rmsnorm_test_copy2(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
 int add_rmsnorm_test_stream(uint16_t* dst, const uint16_t* src, int64_t count, int mode,
                             struct ihipStream_t* stream);
 
-/* Human-readable text of a status code (static storage). *//* Human-readable text of a status code (static storage). */
+/* Human-readable text of a status code (static storage). */
 const char* add_rmsnorm_strerror(int status);
 
 /* Text of the HIP error behind the last ADD_RMSNORM_EHIP on this thread. */

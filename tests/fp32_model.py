@@ -43,6 +43,11 @@ def lib():
         L.model_add_rmsnorm_quant.restype = ctypes.c_int
         L.model_add_rmsnorm_quant.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64,
                                               ctypes.c_int64, ctypes.c_float]
+        L.model_add_rmsnorm_quant_fp8.restype = ctypes.c_int
+        L.model_add_rmsnorm_quant_fp8.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_float]
+        L.model_e4m3_codes.restype = ctypes.c_int
+        L.model_e4m3_codes.argtypes = [vp, vp, ctypes.c_int64]
         _lib = L
     return _lib
 
@@ -86,3 +91,30 @@ def add_rmsnorm_quant(x, residual, weight, eps=1e-6):
     if rc != 0:
         raise ValueError("fp32 model rejected its arguments")
     return q, sc, res
+
+
+def add_rmsnorm_quant_fp8(x, residual, weight, eps=1e-6):
+    """(E4M3 codes uint8, scale fp32 per row, residual_out) of the fp32 model.
+    residual None is plain RMSNorm; residual_out is then None."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    if residual is not None:
+        residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    weight = np.ascontiguousarray(weight, dtype=np.uint16)
+    n, h = x.shape
+    q = np.empty(x.shape, dtype=np.uint8)
+    sc = np.empty(n, dtype=np.float32)
+    res = np.empty_like(x) if residual is not None else None
+    rc = lib().model_add_rmsnorm_quant_fp8(q.ctypes.data, sc.ctypes.data, _ptr(res),
+                                           x.ctypes.data, _ptr(residual), weight.ctypes.data, n,
+                                           h, ctypes.c_float(eps))
+    if rc != 0:
+        raise ValueError("fp32 model rejected its arguments")
+    return q, sc, res
+
+
+def e4m3_codes(v):
+    """The model's E4M3 code of each binary32 value (|v| < 464)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().model_e4m3_codes(out.ctypes.data, v.ctypes.data, v.size)
+    return out

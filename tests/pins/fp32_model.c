@@ -158,3 +158,67 @@ int model_add_rmsnorm_quant(int8_t* q, float* scale, uint16_t* residual_out, con
   free(acc);
   return 0;
 }
+
+/*
+ * OCP FP8 E4M3 code of a finite binary32 v with |v| < 464, nearest value with
+ * ties to the even code, by bit arithmetic: below 2^-6 the values are
+ * multiples of 2^-9 (nearbyintf of v * 2^9, exact scaling); from 2^-6 up the
+ * binary32 exponent minus 120 and the top 3 mantissa bits, rounded at the
+ * 20 dropped bits.  |v| >= 464 saturates to 448 (never reached below).
+ */
+static uint8_t e4m3_code(float v) {
+  const uint32_t sign = (bits_of(v) >> 24) & 0x80;
+  const float a = fabsf(v);
+  uint32_t mag;
+  if (!(a < 464.0f)) {
+    mag = 0x7E;
+  } else if (a < 0x1p-6f) {
+    mag = (uint32_t)nearbyintf(a * 512.0f);
+  } else {
+    uint32_t b = bits_of(a);
+    b += 0x7FFFF + ((b >> 20) & 1);
+    mag = (b >> 20) - (120u << 3);
+  }
+  return (uint8_t)(sign | mag);
+}
+
+int model_e4m3_codes(uint8_t* out, const float* v, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_code(v[i]);
+  return 0;
+}
+
+/*
+ * FP8 E4M3 quantised out: as model_add_rmsnorm_quant with 448 in place of
+ * 127 (scale = amax / 448, inv = 448 / amax), the threshold 2^-118, and
+ * codes e4m3_code(y_j * inv).
+ */
+int model_add_rmsnorm_quant_fp8(uint8_t* q, float* scale, uint16_t* residual_out,
+                                const uint16_t* x, const uint16_t* r, const uint16_t* w,
+                                int64_t n_rows, int64_t hidden, float eps) {
+  if (hidden <= 0 || !r != !residual_out) return -1;
+  int64_t padded = 1;
+  while (padded < (hidden + 7) / 8) padded *= 2;
+  float* seg = (float*)malloc(sizeof(float) * (size_t)padded);
+  float* acc = (float*)malloc(sizeof(float) * (size_t)hidden);
+  if (!seg || !acc) {
+    free(seg);
+    free(acc);
+    return -1;
+  }
+  for (int64_t i = 0; i < n_rows; ++i) {
+    const float rinv = row_rinv(acc, seg, padded, residual_out ? residual_out + i * hidden : NULL,
+                                x + i * hidden, r ? r + i * hidden : NULL, hidden, eps, NULL);
+    float amax = 0.0f;
+    for (int64_t j = 0; j < hidden; ++j) {
+      acc[j] = (acc[j] * rinv) * f32_of((uint32_t)w[j] << 16);
+      amax = max_nan(amax, fabsf(acc[j]));
+    }
+    const float inv = 448.0f / amax;
+    scale[i] = amax / 448.0f;
+    const int ok = isfinite(amax) && amax >= ldexpf(1.0f, -118);
+    for (int64_t j = 0; j < hidden; ++j) q[i * hidden + j] = ok ? e4m3_code(acc[j] * inv) : 0;
+  }
+  free(seg);
+  free(acc);
+  return 0;
+}

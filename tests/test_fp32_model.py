@@ -163,3 +163,63 @@ def test_partial_segment_is_zero_padding():
     full, _, s16 = fp32_model.add_rmsnorm(x, r, w, 1e-6, want_sumsq=True)
     part, _, s13 = fp32_model.add_rmsnorm(x[:, :13], r[:, :13], w[:13], 1e-6, want_sumsq=True)
     assert np.array_equal(s16.view(np.uint32), s13.view(np.uint32))
+
+
+def test_e4m3_model_codes_match_torch_and_the_oracle():
+    """The model's bit-arithmetic E4M3 rounding against torch's CPU
+    float8_e4m3fn cast (every 61st binary32 pattern below 464 in magnitude,
+    and every pattern within 64 units of each E4M3 value and midpoint), and
+    against the oracle's search on a sample."""
+    import torch
+
+    u = np.arange(0, 0x43E80000, 61, dtype=np.uint32)
+    vals = oracle.e4m3_to_f64(np.arange(127))
+    pts = np.concatenate([vals, (vals[:-1] + vals[1:]) / 2]).astype(np.float32).view(np.uint32)
+    near = (pts[:, None].astype(np.int64) + np.arange(-64, 65)[None, :]).ravel()
+    near = near[(near >= 0) & (near < 0x43E80000)].astype(np.uint32)
+    u = np.concatenate([u, near])
+    v = np.concatenate([u, u | np.uint32(0x80000000)]).view(np.float32)
+    got = fp32_model.e4m3_codes(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    rng = np.random.default_rng(91)
+    sample = v[rng.integers(0, v.size, 3000)]
+    assert all(int(c) == oracle.e4m3_rne(float(x)) for c, x in zip(fp32_model.e4m3_codes(sample), sample))
+
+
+def _code_steps(a, b):
+    """Distance in E4M3 codes between two code arrays (signed codes mapped to
+    a monotone integer line)."""
+    def line(c):
+        c = c.astype(np.int32)
+        return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+    return np.abs(line(a) - line(b))
+
+
+@pytest.mark.parametrize("n,h", [(64, 1024), (16, 4096), (4, 16384)])
+def test_fp8_model_agrees_with_the_oracle(n, h):
+    x, r, w = synth.workload(710 + h, n, h)
+    mq, ms, mr = fp32_model.add_rmsnorm_quant_fp8(x, r, w, 1e-6)
+    oq, os_, orr = oracle.add_rmsnorm_quant_fp8(x, r, w, 1e-6)
+    assert np.array_equal(mr, orr)
+    assert np.allclose(ms, os_, rtol=2e-6, atol=0)
+    d = _code_steps(mq, oq)
+    assert d.max() <= 1 and (d > 0).mean() < 1e-3
+    pq, ps, _ = fp32_model.add_rmsnorm_quant_fp8(x, None, w, 1e-6)
+    oq, os_, _ = oracle.add_rmsnorm_quant_fp8(x, None, w, 1e-6)
+    assert np.allclose(ps, os_, rtol=2e-6, atol=0)
+    d = _code_steps(pq, oq)
+    assert d.max() <= 1 and (d > 0).mean() < 1e-3
+
+
+def test_fp8_model_special_rows():
+    h = 64
+    w = synth.to_bf16_bits(np.linspace(0.5, 2.0, h))
+    x = np.zeros((4, h), np.uint16)
+    x[1] = 0x3F80
+    x[1, 3] = 0x7FC1
+    x[2] = 0x62C0
+    x[3] = 0x0001
+    q, sc, _ = fp32_model.add_rmsnorm_quant_fp8(x, x, w, 1e-6)
+    assert sc[0] == 0 and np.isnan(sc[1]) and sc[2] == 0 and 0 < sc[3] < 2.0 ** -118 / 448
+    assert (q == 0).all()
