@@ -251,22 +251,25 @@ DEV bool quantisable(float amax) {
   return amax >= (Q == kQInt8 ? 0x1p-120f : 0x1p-118f) && amax <= 3.40282347e38f;
 }
 
-// Codes of one segment.  int8: nearest-even integer of y * inv, kept within
-// [-127, 127].  E4M3: the packed conversion of y * inv, two values per
-// instruction.
+// Codes of one segment, for a quantisable row (|y| <= amax, so |y * inv| <=
+// qmax (1 + 2^-24)^2 < qmax + 1/2).
+//   int8: the nearest-even integer of t = y * inv, which is within [-127, 127]
+//   by the bound above.  t + 1.5 * 2^23 lies in [2^23, 2^24), where binary32
+//   steps by 1, so the add rounds t to the nearest integer n (ties to even,
+//   the default mode) and the sum's bit pattern is 0x4B400000 + n: its low
+//   byte is n's two's complement.  v_perm_b32 gathers four such bytes per word.
+//   E4M3: the packed conversion of y * inv, two values per instruction.
 template <int Q>
 DEV u32x2 quant8(const float (&y)[8], float inv) {
   if constexpr (Q == kQInt8) {
-    uint32_t w0 = 0, w1 = 0;
+    uint32_t g[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float t = __builtin_rintf(y[k] * inv);
-      t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
-      const uint32_t c = (uint32_t)(int)t & 0xFFu;
-      if (k < 4) w0 |= c << (8 * k);
-      else w1 |= c << (8 * (k - 4));
-    }
-    return u32x2{w0, w1};
+    for (int k = 0; k < 8; ++k) g[k] = __builtin_bit_cast(uint32_t, y[k] * inv + 0x1.8p23f);
+    const uint32_t a = __builtin_amdgcn_perm(g[1], g[0], 0x0C0C0400u);  // bytes g0, g1
+    const uint32_t b = __builtin_amdgcn_perm(g[3], g[2], 0x0C0C0400u);  // bytes g2, g3
+    const uint32_t c = __builtin_amdgcn_perm(g[5], g[4], 0x0C0C0400u);
+    const uint32_t d = __builtin_amdgcn_perm(g[7], g[6], 0x0C0C0400u);
+    return u32x2{__builtin_amdgcn_perm(b, a, 0x05040100u), __builtin_amdgcn_perm(d, c, 0x05040100u)};
   } else {
     float v[8];
 #pragma unroll
