@@ -152,8 +152,14 @@ DEV float seg_sumsq(const float (&a)[8]) {
   return t;
 }
 
-// Maximum in which a NaN operand wins.  Exact and order-free otherwise.
-DEV float max_nan(float m, float v) { return (m != m) ? m : ((v != v) || v > m) ? v : m; }
+// Row maxima of |y| are taken on bit patterns.  With the sign bit cleared,
+// unsigned integer order is the numeric order of binary32 values, and every
+// NaN pattern lies above +Inf, so a NaN anywhere makes the maximum a NaN.  An
+// integer maximum is exact and order-free, NaN payloads included; it costs an
+// AND and a max per element where a NaN-aware float maximum costs compares
+// and selects.
+DEV uint32_t abs_bits(float v) { return __builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu; }
+DEV uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 // Cross-lane moves.  Each level adds two aligned sibling sub-blocks; once a
 // sub-block holds one value in all its lanes, a mirror within the enclosing
@@ -176,17 +182,17 @@ DEV float wave_block_sum(float v) {
   return lo + hi;
 }
 
-// Maximum over the 64 lanes (NaN wins); the same in every lane.  Must be
+// Unsigned maximum over the 64 lanes; the same in every lane.  Must be
 // called with all 64 lanes active.
-DEV float wave_max(float v) {
-  v = max_nan(v, ADDRMS_DPP(v, 0xB1));
-  v = max_nan(v, ADDRMS_DPP(v, 0x4E));
-  v = max_nan(v, ADDRMS_DPP(v, 0x141));
-  v = max_nan(v, ADDRMS_DPP(v, 0x140));
-  v = max_nan(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F)));
-  float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  return max_nan(lo, hi);
+#define ADDRMS_DPP_U(v, ctrl) (uint32_t) __builtin_amdgcn_mov_dpp((int)(v), (ctrl), 0xF, 0xF, false)
+DEV uint32_t wave_max(uint32_t v) {
+  v = umax(v, ADDRMS_DPP_U(v, 0xB1));
+  v = umax(v, ADDRMS_DPP_U(v, 0x4E));
+  v = umax(v, ADDRMS_DPP_U(v, 0x141));
+  v = umax(v, ADDRMS_DPP_U(v, 0x140));
+  v = umax(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  return umax((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+              (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
 }
 
 // Balanced pairwise tree over N (a power of two) values in index order.
@@ -227,9 +233,10 @@ DEV u32x4 normalise8(const float (&acc)[8], float rinv, u32x4 wq) {
   return pack8_rne(y);
 }
 
-DEV float max_abs8(float m, const float (&y)[8]) {
+// Running maximum of |y| over a segment, as bit patterns.
+DEV uint32_t max_abs8(uint32_t m, const float (&y)[8]) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) m = max_nan(m, __builtin_fabsf(y[k]));
+  for (int k = 0; k < 8; ++k) m = umax(m, abs_bits(y[k]));
   return m;
 }
 
@@ -369,7 +376,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
     } else {
       // y twice (the same fp32 operations, so the same values): once for the
       // row maximum, once for the codes.
-      float m = 0.0f;
+      uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         float acc[8], y[8];
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
         scale8(acc, rinv, wl[opaque(lane + 64 * j)], y);
         if (lane + 64 * j < C) m = max_abs8(m, y);
       }
-      const float amax = wave_max(m);
+      const float amax = __builtin_bit_cast(float, wave_max(m));
       const float scale = amax / qmax<Q>();
       const float inv = qmax<Q>() / amax;
       const bool ok = quantisable<Q>(amax);
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
   constexpr int W = B / 64;
   constexpr int NB = W * J;
   __shared__ float blk[2][NB];  // alternates by row so one barrier per row suffices
-  __shared__ float mx[2][Q ? W : 1];
+  __shared__ uint32_t mx[2][Q ? W : 1];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
         if (s < C) store_stream(p.out + row * p.out_stride + s, normalise8(acc[j], rinv, wq[j]));
       }
     } else {
-      float m = 0.0f;
+      uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         float y[8];
@@ -469,9 +476,10 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
       m = wave_max(m);
       if (lane == 0) mx[parity][wave] = m;
       __syncthreads();
-      float amax = mx[parity][0];
+      uint32_t mb = mx[parity][0];
 #pragma unroll
-      for (int i = 1; i < W; ++i) amax = max_nan(amax, mx[parity][i]);
+      for (int i = 1; i < W; ++i) mb = umax(mb, mx[parity][i]);
+      const float amax = __builtin_bit_cast(float, mb);
       const float scale = amax / qmax<Q>();
       const float inv = qmax<Q>() / amax;
       const bool ok = quantisable<Q>(amax);
@@ -501,7 +509,7 @@ template <int B, int NB, int U, int Q, bool R>
 __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
   constexpr int W = B / 64;
   __shared__ float blk[NB];
-  __shared__ float mx[Q ? W : 1];
+  __shared__ uint32_t mx[Q ? W : 1];
   extern __shared__ float4 stage[];  // [2][C]: elements 0-3, then 4-7, of each segment
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -553,7 +561,7 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
       }
     } else {
       // y from the staged sums twice: for the row maximum, then for the codes.
-      float m = 0.0f;
+      uint32_t m = 0;
       for (int c = 0; c < chunks; ++c) {
         const int s = c * B + t;
         if (s < C) {
@@ -567,9 +575,10 @@ __global__ __launch_bounds__(B) void k_lds_two_pass(Params p) {
       m = wave_max(m);
       if (lane == 0) mx[wave] = m;
       __syncthreads();
-      float amax = mx[0];
+      uint32_t mb = mx[0];
 #pragma unroll
-      for (int i = 1; i < W; ++i) amax = max_nan(amax, mx[i]);
+      for (int i = 1; i < W; ++i) mb = umax(mb, mx[i]);
+      const float amax = __builtin_bit_cast(float, mb);
       const float scale = amax / qmax<Q>();
       const float inv = qmax<Q>() / amax;
       const bool ok = quantisable<Q>(amax);
