@@ -188,15 +188,21 @@ def test_cvt_range_errors():
     assert L.add_rmsnorm_test_cvt_range(A + 4, 0, 16, None) == arn.EALIGN
     assert L.add_rmsnorm_test_cvt_range(0, 0, 16, None) == arn.EINVAL
     assert L.add_rmsnorm_test_cvt_range(0, 0, 0, None) == arn.OK
+    assert L.add_rmsnorm_test_cvt_e4m3_range(A, 0, -8, None) == arn.EINVAL
+    assert L.add_rmsnorm_test_cvt_e4m3_range(A, 0, 12, None) == arn.EALIGN
+    assert L.add_rmsnorm_test_cvt_e4m3_range(A + 8, 0, 16, None) == arn.EALIGN
+    assert L.add_rmsnorm_test_cvt_e4m3_range(0, 0, 16, None) == arn.EINVAL
+    assert L.add_rmsnorm_test_cvt_e4m3_range(0, 0, 0, None) == arn.OK
 
 
 def qcall(q=A + 5 * MB, sc=A + 6 * MB, res=A + MB, x=A + 2 * MB, r=A + 3 * MB, w=A + 4 * MB,
-          n=4, h=64, eps=1e-6, cfg=None):
+          n=4, h=64, eps=1e-6, cfg=None, fp8=False):
     L = arn.lib()
+    name = "add_rmsnorm_quant_fp8_fwd" if fp8 else "add_rmsnorm_quant_fwd"
     if cfg is None:
-        return L.add_rmsnorm_quant_fwd(q, sc, res, x, r, w, n, h, eps, None)
+        return getattr(L, name)(q, sc, res, x, r, w, n, h, eps, None)
     c = arn.LaunchCfg(*cfg)
-    return L.add_rmsnorm_quant_fwd_cfg(q, sc, res, x, r, w, n, h, eps, ctypes.byref(c), None)
+    return getattr(L, name + "_cfg")(q, sc, res, x, r, w, n, h, eps, ctypes.byref(c), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -215,17 +221,22 @@ def qcall(q=A + 5 * MB, sc=A + 6 * MB, res=A + MB, x=A + 2 * MB, r=A + 3 * MB, w
     (dict(res=A + 3 * MB - 16), arn.EALIAS),            # residual_out partly on residual
     (dict(res=A + 4 * MB), arn.EALIAS),                 # residual_out on the weight
 ])
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
 @fake_addresses
-def test_quant_argument_errors(kw, status):
-    assert qcall(**kw) == status
+def test_quant_argument_errors(kw, status, fp8):
+    assert qcall(fp8=fp8, **kw) == status
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
 @fake_addresses
-def test_quant_zero_rows_and_in_place_validation():
-    assert qcall(q=0, sc=0, res=0, x=0, r=0, w=0, n=0) == arn.OK
+def test_quant_zero_rows_and_in_place_validation(fp8):
+    assert qcall(q=0, sc=0, res=0, x=0, r=0, w=0, n=0, fp8=fp8) == arn.OK
+    # The fused entry points need both residual pointers.
+    assert qcall(res=0, r=0, fp8=fp8) == arn.EINVAL
+    assert qcall(res=0, fp8=fp8) == arn.EINVAL
     # residual_out == residual passes the alias checks (ERANGE from the forced
     # path comes after them; nothing is launched).
-    assert qcall(res=A + 3 * MB, h=8192, cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.ERANGE
+    assert qcall(res=A + 3 * MB, h=8192, cfg=(arn.PATH_WAVE_ROW, 0, 0, 0), fp8=fp8) == arn.ERANGE
 
 
 def pcall(out=A, x=A + 2 * MB, w=A + 4 * MB, n=4, h=64, eps=1e-6, cfg=None):
@@ -237,12 +248,13 @@ def pcall(out=A, x=A + 2 * MB, w=A + 4 * MB, n=4, h=64, eps=1e-6, cfg=None):
 
 
 def pqcall(q=A + 5 * MB, sc=A + 6 * MB, x=A + 2 * MB, w=A + 4 * MB, n=4, h=64, eps=1e-6,
-           cfg=None):
+           cfg=None, fp8=False):
     L = arn.lib()
+    name = "rmsnorm_quant_fp8_fwd" if fp8 else "rmsnorm_quant_fwd"
     if cfg is None:
-        return L.rmsnorm_quant_fwd(q, sc, x, w, n, h, eps, None)
+        return getattr(L, name)(q, sc, x, w, n, h, eps, None)
     c = arn.LaunchCfg(*cfg)
-    return L.rmsnorm_quant_fwd_cfg(q, sc, x, w, n, h, eps, ctypes.byref(c), None)
+    return getattr(L, name + "_cfg")(q, sc, x, w, n, h, eps, ctypes.byref(c), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -281,15 +293,17 @@ def test_plain_argument_errors(kw, status):
     (dict(q=A + 4 * MB - 64), arn.EALIAS),              # codes reach the weight
     (dict(cfg=(arn.PATH_WG_ROW, 64, 0, 0), h=8192), arn.ERANGE),
 ])
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
 @fake_addresses
-def test_plain_quant_argument_errors(kw, status):
-    assert pqcall(**kw) == status
+def test_plain_quant_argument_errors(kw, status, fp8):
+    assert pqcall(fp8=fp8, **kw) == status
 
 
 @fake_addresses
 def test_plain_zero_rows_and_in_place_validation():
     assert pcall(out=0, x=0, w=0, n=0) == arn.OK
     assert pqcall(q=0, sc=0, x=0, w=0, n=0) == arn.OK
+    assert pqcall(q=0, sc=0, x=0, w=0, n=0, fp8=True) == arn.OK
     # out == x passes the alias checks; the forced path's ERANGE comes after
     # them, so nothing is launched.
     assert pcall(out=A + 2 * MB, h=8192, cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)) == arn.ERANGE

@@ -93,7 +93,8 @@ def test_two_streams_at_once():
         assert torch.equal(o2, ref[1][0]) and torch.equal(ro2, ref[1][1])
 
 
-@pytest.mark.parametrize("kind", ["plain", "plain_quant", "strided_general", "log1p"])
+@pytest.mark.parametrize("kind", ["plain", "plain_quant", "plain_quant_fp8", "strided_general",
+                                  "log1p"])
 def test_graph_replays_of_the_other_entry_points(kind):
     """Plain RMSNorm (resident grid by default), a strided view on the
     general kernels, and log1p (capped persistent grid), each captured once
@@ -131,12 +132,18 @@ def test_graph_replays_of_the_other_entry_points(kind):
 
             def call(o, x):
                 arn.rmsnorm_fwd(o, x, w, 1e-6)
-        else:
+        elif kind == "plain_quant":
             out = torch.empty(n, h, dtype=torch.int8, device=dev)
             sc = torch.empty(n, dtype=torch.float32, device=dev)
 
             def call(o, x):
                 arn.rmsnorm_quant_fwd(o, sc if o is out else torch.empty_like(sc), x, w, 1e-6)
+        else:
+            out = torch.empty(n, h, dtype=torch.uint8, device=dev)
+            sc = torch.empty(n, dtype=torch.float32, device=dev)
+
+            def call(o, x):
+                arn.rmsnorm_quant_fp8_fwd(o, sc if o is out else torch.empty_like(sc), x, w, 1e-6)
 
     def fresh(rep):
         if kind == "log1p":

@@ -225,6 +225,11 @@ def test_empty_inputs_through_every_entry_point():
                               e.clone(), w, 1e-6)
     arn.rmsnorm_quant_fwd(torch.empty(0, 1024, dtype=torch.int8, device=dev),
                           torch.empty(0, dtype=torch.float32, device=dev), e, w, 1e-6)
+    arn.add_rmsnorm_quant_fp8_fwd(torch.empty(0, 1024, dtype=torch.uint8, device=dev),
+                                  torch.empty(0, dtype=torch.float32, device=dev), e, e.clone(),
+                                  e.clone(), w, 1e-6)
+    arn.rmsnorm_quant_fp8_fwd(torch.empty(0, 1024, dtype=torch.uint8, device=dev),
+                              torch.empty(0, dtype=torch.float32, device=dev), e, w, 1e-6)
     arn.add_rmsnorm_fwd_strided(e, e.clone(), e.clone(), e.clone(), w, 1e-6)
     f = torch.empty(0, dtype=torch.float32, device=dev)
     arn.log1p_f32(f, f.clone())
