@@ -424,26 +424,44 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
     wq[j] = s < C ? p.weight[s] : u32x4{0, 0, 0, 0};
   }
 
-  // Rows are read and written through per-row buffer resources, as in
-  // k_wave_row: segments past the row read as zero and their stores are
-  // dropped, so nothing branches on the row's end.
+  // Plain quantised rows are read and written through per-row buffer
+  // resources, as in k_wave_row: segments past the row read as zero and their
+  // stores are dropped, so nothing branches on the row's end (measured 1-4%
+  // faster there).  The other variants use bounds-checked pointer accesses
+  // (measured 2% faster for plain bf16, the same for the fused forms).
+  constexpr bool BUF = Q != 0 && !R;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x, parity ^= 1) {
-    const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, p.x_stride, C, true);
-    const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, p.r_stride, C, R);
-    const __amdgpu_buffer_rsrc_t ro = row_rsrc(p.residual_out, row, p.ro_stride, C, R);
     u32x4 xq[J], rq[J];
+    if constexpr (BUF) {
+      const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, p.x_stride, C, true);
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      xq[j] = load_seg(rx, t + B * j);
-      rq[j] = R ? load_seg(rr, t + B * j) : u32x4{0, 0, 0, 0};
+      for (int j = 0; j < J; ++j) {
+        xq[j] = load_seg(rx, t + B * j);
+        rq[j] = u32x4{0, 0, 0, 0};
+      }
+    } else {
+      const u32x4* xr = p.x + row * p.x_stride;
+      const u32x4* rr = p.residual + (R ? row * p.r_stride : 0);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int s = t + B * j;
+        if (s < C) {
+          xq[j] = load_stream(xr + s);
+          rq[j] = R ? load_stream(rr + s) : u32x4{0, 0, 0, 0};
+        } else {
+          xq[j] = u32x4{0, 0, 0, 0};
+          rq[j] = u32x4{0, 0, 0, 0};
+        }
+      }
     }
     float acc[J][8];
     float bs[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
+      const int s = t + B * j;
       bs[j] = add_segment<R>(xq[j], rq[j], acc[j]);
-      if constexpr (R) store_seg(ro, t + B * j, pack8_rne(acc[j]));
+      if (R && s < C) store_stream(p.residual_out + row * p.ro_stride + s, pack8_rne(acc[j]));
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) bs[j] = wave_block_sum(bs[j]);
@@ -454,9 +472,11 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
     __syncthreads();
     const float rinv = row_rinv(pairwise_tree_lds<NB>(blk[parity]), p);
     if constexpr (!Q) {
-      const __amdgpu_buffer_rsrc_t oo = row_rsrc(p.out, row, p.out_stride, C, true);
 #pragma unroll
-      for (int j = 0; j < J; ++j) store_seg(oo, t + B * j, normalise8(acc[j], rinv, wq[j]));
+      for (int j = 0; j < J; ++j) {
+        const int s = t + B * j;
+        if (s < C) store_stream(p.out + row * p.out_stride + s, normalise8(acc[j], rinv, wq[j]));
+      }
     } else {
       uint32_t m = 0;
 #pragma unroll
@@ -478,10 +498,19 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
       const float inv = qmax<Q>() / amax;
       const bool ok = quantisable<Q>(amax);
       if (t == 0) p.qscale[row] = scale;
-      const __amdgpu_buffer_rsrc_t qo = code_row_rsrc(p.qout, row, C);
+      if constexpr (BUF) {
+        const __amdgpu_buffer_rsrc_t qo = code_row_rsrc(p.qout, row, C);
 #pragma unroll
-      for (int j = 0; j < J; ++j)
-        store_codes(qo, t + B * j, ok ? quant8<Q>(acc[j], inv) : u32x2{0, 0});
+        for (int j = 0; j < J; ++j)
+          store_codes(qo, t + B * j, ok ? quant8<Q>(acc[j], inv) : u32x2{0, 0});
+      } else {
+        const size_t base = (size_t)row * (size_t)C;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int s = t + B * j;
+          if (s < C) store_codes_stream(p.qout + base + s, ok ? quant8<Q>(acc[j], inv) : u32x2{0, 0});
+        }
+      }
     }
   }
 }
