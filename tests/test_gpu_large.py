@@ -57,3 +57,90 @@ def test_tensors_beyond_4gib(n, h, cfgs):
         del out, res
     del xd, rd
     torch.cuda.empty_cache()
+
+
+def _build(n, h, seed):
+    import torch
+
+    bx, br, w = synth.workload(seed, 256, h)
+    ix = np.arange(n) % 256
+    ir = (7 * np.arange(n) + 3) % 256
+    dev = torch.device("cuda:0")
+    xd = to_dev(bx)[torch.from_numpy(ix).to(dev)]
+    rd = to_dev(br)[torch.from_numpy(ir).to(dev)]
+    return bx, br, w, ix, ir, xd, rd, to_dev(w)
+
+
+def _rows(n, h):
+    edge = 2 ** 31 // h
+    return sorted({0, 1, 255, 256, n // 2, edge - 1, edge, edge + 1, n - 2, n - 1})
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+@pytest.mark.parametrize("n,h", [(2 ** 18 + 3, 8192), (2 ** 20 + 5, 2048)])
+def test_quantised_beyond_4gib(n, h, fmt):
+    """Codes and scales of the fused and plain quantised entry points on
+    tensors past 2^31 elements, sampled rows bit-exact against the fp32
+    model."""
+    require_gpu()
+    import torch
+
+    import fp32_model
+
+    assert n * h > 2 ** 31
+    announce("large quantised %s %dx%d" % (fmt, n, h))
+    bx, br, w, ix, ir, xd, rd, wd = _build(n, h, 5100 + h)
+    rows = _rows(n, h)
+    sel = torch.tensor(rows, device=xd.device)
+    code = torch.int8 if fmt == "int8" else torch.uint8
+    model = fp32_model.add_rmsnorm_quant if fmt == "int8" else fp32_model.add_rmsnorm_quant_fp8
+    for plain in (False, True):
+        announce("  %s" % ("plain" if plain else "fused"))
+        q = torch.empty(n, h, dtype=code, device=xd.device)
+        sc = torch.empty(n, dtype=torch.float32, device=xd.device)
+        res = None
+        if fmt == "int8" and plain:
+            arn.rmsnorm_quant_fwd(q, sc, xd, wd, 1e-6)
+        elif fmt == "int8":
+            res = torch.empty_like(xd)
+            arn.add_rmsnorm_quant_fwd(q, sc, res, xd, rd, wd, 1e-6)
+        elif plain:
+            arn.rmsnorm_quant_fp8_fwd(q, sc, xd, wd, 1e-6)
+        else:
+            res = torch.empty_like(xd)
+            arn.add_rmsnorm_quant_fp8_fwd(q, sc, res, xd, rd, wd, 1e-6)
+        torch.cuda.synchronize()
+        mq, ms, mr = model(bx[ix[rows]], None if plain else br[ir[rows]], w, 1e-6)
+        assert np.array_equal(q[sel].cpu().numpy().view(mq.dtype), mq), rows
+        assert np.array_equal(sc[sel].cpu().numpy().view(np.uint32), ms.view(np.uint32)), rows
+        if res is not None:
+            assert np.array_equal(res[sel].cpu().numpy().view(np.uint16), mr), rows
+        del q, sc, res
+    del xd, rd
+    torch.cuda.empty_cache()
+
+
+def test_general_kernel_beyond_4gib():
+    """hidden 8191 (no row 16-byte aligned) past 2^31 elements: the general
+    kernel's 64-bit row offsets, sampled rows bit-exact against the fp32
+    model."""
+    require_gpu()
+    import torch
+
+    import fp32_model
+
+    n, h = 2 ** 18 + 64, 8191
+    assert n * h > 2 ** 31
+    announce("large general %dx%d" % (n, h))
+    bx, br, w, ix, ir, xd, rd, wd = _build(n, h, 5200)
+    rows = _rows(n, h)
+    sel = torch.tensor(rows, device=xd.device)
+    out = torch.empty_like(xd)
+    res = torch.empty_like(xd)
+    arn.add_rmsnorm_fwd(out, res, xd, rd, wd, 1e-6)
+    torch.cuda.synchronize()
+    m_out, m_res = fp32_model.add_rmsnorm(bx[ix[rows]], br[ir[rows]], w, 1e-6)
+    assert np.array_equal(out[sel].cpu().numpy().view(np.uint16), m_out), rows
+    assert np.array_equal(res[sel].cpu().numpy().view(np.uint16), m_res), rows
+    del out, res, xd, rd
+    torch.cuda.empty_cache()
