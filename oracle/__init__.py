@@ -94,6 +94,9 @@ class Oracle:
         L.orc_add_rmsnorm_quant_fp8.restype = ctypes.c_int
         L.orc_add_rmsnorm_quant_fp8.argtypes = [ctypes.c_void_p] * 7 + [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_float]
+        L.orc_qk_rmsnorm.restype = ctypes.c_int
+        L.orc_qk_rmsnorm.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 6 + [
+            ctypes.c_float]
         self.path = path
         self.lib = L
 
@@ -227,6 +230,47 @@ class Oracle:
         return (q, sc, y) if want_exact else (q, sc)
 
 
+    # ------------------------------------------------------------ per-head q/k norm
+
+    @staticmethod
+    def _head_view(t, name):
+        """(array, token stride in elements) of a [tokens, heads, head_dim] uint16
+        view whose heads are contiguous within a token."""
+        t = np.asarray(t)
+        if t.dtype != np.uint16 or t.ndim != 3:
+            raise ValueError("%s must be a [tokens, heads, head_dim] uint16 array" % name)
+        d = t.shape[2]
+        if t.shape[0] > 1 and t.strides[0] % 2:
+            raise ValueError("%s: odd token stride" % name)
+        if t.strides[2] != 2 or (t.shape[1] > 1 and t.strides[1] != 2 * d):
+            raise ValueError("%s: heads must be contiguous within a token" % name)
+        stride = t.strides[0] // 2 if t.shape[0] > 1 else t.shape[1] * d
+        return t, stride
+
+    def qk_rmsnorm(self, q, k, q_weight, k_weight, eps: float = 1e-6):
+        """Per-head RMSNorm of q [T, Hq, D] with q_weight [D] and of k
+        [T, Hk, D] with k_weight [D] (views with any token stride and heads
+        contiguous within a token).  Returns (q_out, k_out), contiguous."""
+        q, qs = self._head_view(q, "q")
+        k, ks = self._head_view(k, "k")
+        t_n, hq, d = q.shape
+        if k.shape[0] != t_n or k.shape[2] != d:
+            raise ValueError("q and k need the same tokens and head_dim")
+        hk = k.shape[1]
+        qw = np.ascontiguousarray(q_weight, dtype=np.uint16)
+        kw = np.ascontiguousarray(k_weight, dtype=np.uint16)
+        if qw.shape != (d,) or kw.shape != (d,):
+            raise ValueError("q_weight and k_weight must be [head_dim]")
+        q_out = np.empty((t_n, hq, d), np.uint16)
+        k_out = np.empty((t_n, hk, d), np.uint16)
+        rc = self.lib.orc_qk_rmsnorm(
+            _ptr(q_out) if q_out.size else None, _ptr(k_out) if k_out.size else None,
+            q.ctypes.data if q.size else None, k.ctypes.data if k.size else None,
+            _ptr(qw), _ptr(kw), t_n, hq, hk, d, qs, ks, ctypes.c_float(eps))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+        return q_out, k_out
+
     # ------------------------------------------------------------ fp8 e4m3 out
 
     def e4m3_rne(self, v: float) -> int:
@@ -336,6 +380,10 @@ def rmsnorm(x, weight, eps: float = 1e-6, rounding: int = RNE, want_exact: bool 
 
 def rmsnorm_quant(x, weight, eps: float = 1e-6, want_exact: bool = False):
     return default().rmsnorm_quant(x, weight, eps, want_exact)
+
+
+def qk_rmsnorm(q, k, q_weight, k_weight, eps: float = 1e-6):
+    return default().qk_rmsnorm(q, k, q_weight, k_weight, eps)
 
 
 # ---------------------------------------------------------------- measurements

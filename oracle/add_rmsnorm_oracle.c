@@ -356,3 +356,46 @@ int orc_add_rmsnorm_quant_fp8(uint8_t* q, float* scale, uint16_t* residual_out, 
   }
   return 0;
 }
+
+/*
+ * Per-head RMSNorm of q and k.  The notes of the aiter issue list a fused q/k
+ * norm kernel among those whose bf16 stores were not audited for rounding; the
+ * page names that kernel but does not spell out its arithmetic.  The reading
+ * taken here is the q/k normalisation of the decoder the issue's RL run uses
+ * (Qwen3-8B): each head vector of head_dim elements is normalised on its own,
+ * exactly as one plain RMSNorm row (acc = fp32(x), no residual, the population
+ * mean over head_dim, eps inside the square root), q heads with q_weight and
+ * k heads with k_weight (both [head_dim]), each out element rounded once to
+ * bf16, ties to even.
+ *
+ * Layouts: q is [n_tokens][n_q_heads][head_dim] with consecutive tokens
+ * q_stride elements apart and the heads of a token contiguous; k likewise
+ * with k_stride.  q_out and k_out are written contiguous
+ * ([n_tokens][n_heads][head_dim]).  A tensor with no heads is not touched and
+ * its pointers may be NULL.  Returns 0, or -1 on a bad argument.
+ */
+int orc_qk_rmsnorm(uint16_t* q_out, uint16_t* k_out, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* q_weight, const uint16_t* k_weight, int64_t n_tokens,
+                   int64_t n_q_heads, int64_t n_k_heads, int64_t head_dim, int64_t q_stride,
+                   int64_t k_stride, float eps) {
+  if (n_tokens < 0 || n_q_heads < 0 || n_k_heads < 0 || head_dim <= 0) return -1;
+  if (n_q_heads > 0 && (!q_out || !q || !q_weight || q_stride < n_q_heads * head_dim))
+    return -1;
+  if (n_k_heads > 0 && (!k_out || !k || !k_weight || k_stride < n_k_heads * head_dim))
+    return -1;
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    for (int64_t h = 0; h < n_q_heads; ++h) {
+      const uint16_t* row = q + t * q_stride + h * head_dim;
+      uint16_t* dst = q_out + (t * n_q_heads + h) * head_dim;
+      if (orc_add_rmsnorm(dst, NULL, NULL, row, NULL, q_weight, 1, head_dim, eps, ORC_RNE))
+        return -1;
+    }
+    for (int64_t h = 0; h < n_k_heads; ++h) {
+      const uint16_t* row = k + t * k_stride + h * head_dim;
+      uint16_t* dst = k_out + (t * n_k_heads + h) * head_dim;
+      if (orc_add_rmsnorm(dst, NULL, NULL, row, NULL, k_weight, 1, head_dim, eps, ORC_RNE))
+        return -1;
+    }
+  }
+  return 0;
+}
