@@ -38,11 +38,12 @@ CACHE_DEFEAT_BYTES = 1 << 30  # rotate buffer sets until the footprint is >= 1 G
 
 
 OPS = ("bf16", "quant", "quant_fp8", "plain", "plain_quant", "plain_quant_fp8", "general",
-       "log1p")
+       "log1p", "qk")
 ENTRY = {"bf16": "add_rmsnorm_fwd", "quant": "add_rmsnorm_quant_fwd",
          "quant_fp8": "add_rmsnorm_quant_fp8_fwd", "plain": "rmsnorm_fwd",
          "plain_quant": "rmsnorm_quant_fwd", "plain_quant_fp8": "rmsnorm_quant_fp8_fwd",
-         "general": "add_rmsnorm_fwd (general kernel)", "log1p": "log1p_f32"}
+         "general": "add_rmsnorm_fwd (general kernel)", "log1p": "log1p_f32",
+         "qk": "qk_rmsnorm_fwd"}
 QUANT_OPS = ("quant", "quant_fp8", "plain_quant", "plain_quant_fp8")
 PLAIN_OPS = ("plain", "plain_quant", "plain_quant_fp8")
 
@@ -71,7 +72,14 @@ def parse_args(argv=None):
                         "plain_quant_fp8: RMSNorm without the residual add; "
                         "general: the fused op on the general kernel (the workload's hidden "
                         "minus one, so rows leave 16-byte alignment); "
-                        "log1p: the correctly rounded binary32 log1p")
+                        "log1p: the correctly rounded binary32 log1p; "
+                        "qk: per-head RMSNorm of q and k read from a fused qkv tensor "
+                        "(--qk-shape)")
+    p.add_argument("--no-compare", action="store_true",
+                   help="--op qk: skip the same-rows comparison launches (for profiling)")
+    p.add_argument("--qk-shape", default="4096x32x8x128",
+                   help="tokens x q heads x k heads x head_dim of --op qk (default: "
+                        "Qwen3-8B attention at 4096 tokens)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU oracle baseline")
@@ -258,6 +266,108 @@ def bench_log1p(args, torch, arn, hip_build, synth):
     return 0
 
 
+def bench_qk(args, torch, arn, hip_build, synth):
+    """One step: qk_rmsnorm_fwd over a [tokens, (q_heads + 2 k_heads) head_dim]
+    bf16 qkv tensor (q and k read as strided views, written to contiguous q_out
+    and k_out), rotating over buffer sets.  4 bytes per q or k element (read,
+    write) plus the two weights."""
+    import numpy as np
+
+    t, hq, hk, d = (int(v) for v in args.qk_shape.split("x"))
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(11)
+    qkv = synth.to_bf16_bits(rng.standard_normal((t, (hq + 2 * hk) * d)))
+    qw = synth.to_bf16_bits(1 + 0.1 * rng.standard_normal(d))
+    kw = synth.to_bf16_bits(1 + 0.1 * rng.standard_normal(d))
+    elems = t * (hq + hk) * d
+    nbytes = 4 * elems + 4 * d
+    sets = max(1, -(-CACHE_DEFEAT_BYTES // (2 * qkv.size + 2 * elems)))
+    base = torch.from_numpy(qkv.view(np.int16)).to(dev)
+    bufs = []
+    for i in range(sets):
+        b = base if i == 0 else base.clone()
+        q = b[:, :hq * d].view(t, hq, d)
+        k = b[:, hq * d:(hq + hk) * d].view(t, hk, d)
+        bufs.append((torch.empty(t, hq, d, dtype=torch.int16, device=dev),
+                     torch.empty(t, hk, d, dtype=torch.int16, device=dev), q, k))
+    qwd = torch.from_numpy(qw.view(np.int16)).to(dev)
+    kwd = torch.from_numpy(kw.view(np.int16)).to(dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        qo, ko, q, k = bufs[i % sets]
+        arn.qk_rmsnorm_fwd(qo, ko, q, k, qwd, kwd, 1e-6)
+
+    ms, wall_s = time_steps(torch, step, args.steps, args.warmup, stream)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+
+    # The same head rows, contiguous, through rmsnorm_fwd: one wavefront per
+    # row (the path before the packed kernel) and the packed path, two
+    # launches per step (q rows, then k rows).
+    rows = [(torch.empty(t * hq, d, dtype=torch.int16, device=dev),
+             torch.empty(t * hk, d, dtype=torch.int16, device=dev)) for _ in range(sets)]
+    outs = [(torch.empty_like(a), torch.empty_like(b)) for a, b in rows]
+
+    def rows_step(path):
+        def f(i):
+            (qr, kr), (qo, ko) = rows[i % sets], outs[i % sets]
+            arn.rmsnorm_fwd_cfg(qo, qr, qwd, 1e-6, path=path)
+            arn.rmsnorm_fwd_cfg(ko, kr, kwd, 1e-6, path=path)
+        return f
+
+    steps_cmp = min(args.steps, 500)
+    if not args.no_compare:
+        ms_wave, _ = time_steps(torch, rows_step(arn.PATH_WAVE_ROW), steps_cmp, 10, stream)
+        ms_pack, _ = time_steps(torch, rows_step(arn.PATH_PACKED), steps_cmp, 10, stream)
+    traffic = traffic_from_profiles("pack_rows_qk", args.qk_shape, hip_build.source_digest())
+    line = {
+        "metric": "per-head q/k RMSNorm (qk_rmsnorm_fwd) HBM GB/s and % of peak",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qk_rmsnorm_fwd tokens=%d q_heads=%d k_heads=%d head_dim=%d "
+                               "bf16 from a fused qkv tensor, eps=1e-6, q,k~N(0,1), "
+                               "weights~1+0.1N(0,1)" % (t, hq, hk, d),
+                   "tokens": t, "q_heads": hq, "k_heads": hk, "head_dim": d,
+                   "kernel": "pack_rows", "buffer_sets": sets,
+                   "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+                   "wall_s_timed_region": round(wall_s, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_compare:
+        line["same_rows_two_rmsnorm_calls"] = {
+            "wave_row_ms": round(ms_wave, 6), "packed_ms": round(ms_pack, 6),
+            "wave_row_gbps": round(nbytes / (ms_wave * 1e-3) / 1e9, 2),
+            "packed_gbps": round(nbytes / (ms_pack * 1e-3) / 1e9, 2),
+            "what": "the q and k head rows as contiguous [rows, head_dim] tensors, one "
+                    "rmsnorm_fwd_cfg call each, forced onto one wavefront per row or the "
+                    "packed path"}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.default()
+        ts = min(t, 256)
+        qs = qkv[:ts, :hq * d].reshape(ts, hq, d)
+        ks = qkv[:ts, hq * d:(hq + hk) * d].reshape(ts, hk, d)
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            oracle.qk_rmsnorm(qs, ks, qw, kw, 1e-6)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        line["cpu_baseline"] = {
+            "value": round(4 * ts * (hq + hk) * d * passes / el / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "%d passes over the first %d tokens of the workload in %.1f s "
+                      "(single thread)" % (passes, ts, el)}
+    print(json.dumps(line))
+    return 0
+
+
 def ceilings(args, torch, arn, synth):
     """Streaming rates of the device with the fused kernels' access pattern,
     at the bytes of one fused call on the workload (x and residual read, out
@@ -343,6 +453,8 @@ def main(argv=None):
         return ceilings(args, torch, arn, synth)
     if args.op == "log1p":
         return bench_log1p(args, torch, arn, hip_build, synth)
+    if args.op == "qk":
+        return bench_qk(args, torch, arn, hip_build, synth)
 
     n_rows, hidden = (int(v) for v in args.workload.split("x"))
     cfg = synth.CONFIGS.get(args.workload, dict(seed=3, n_rows=n_rows, hidden=hidden))
@@ -415,6 +527,8 @@ def main(argv=None):
 
     if args.op == "general":
         path = "general"
+    elif args.op in ("bf16", "plain") and hidden <= 256:
+        path = "pack_rows"
     elif args.op == "bf16":
         path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"
     else:  # the quantised and plain variants keep rows in registers up to 16384

@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -31,6 +31,7 @@ PATH_WAVE_ROW = 1
 PATH_WG_ROW = 2
 PATH_LDS_TWO_PASS = 3
 PATH_GENERAL = 4
+PATH_PACKED = 5
 
 
 class AddRmsnormError(RuntimeError):
@@ -60,7 +61,8 @@ EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_fwd_strided",
            "rmsnorm_fwd_strided", "add_rmsnorm_quant_fwd", "add_rmsnorm_quant_fwd_cfg",
            "rmsnorm_fwd", "rmsnorm_fwd_cfg", "rmsnorm_quant_fwd", "rmsnorm_quant_fwd_cfg",
            "add_rmsnorm_quant_fp8_fwd", "add_rmsnorm_quant_fp8_fwd_cfg", "rmsnorm_quant_fp8_fwd",
-           "rmsnorm_quant_fp8_fwd_cfg", "log1p_f32", "log1p_f32_cfg",
+           "rmsnorm_quant_fp8_fwd_cfg", "qk_rmsnorm_fwd", "qk_rmsnorm_fwd_cfg",
+           "log1p_f32", "log1p_f32_cfg",
            "add_rmsnorm_test_cvt_range", "add_rmsnorm_test_cvt_e4m3_range",
            "add_rmsnorm_test_copy2",
            "add_rmsnorm_test_stream", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
@@ -116,6 +118,10 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(LaunchCfg), vp]
     L.add_rmsnorm_test_cvt_e4m3_range.restype = i32
     L.add_rmsnorm_test_cvt_e4m3_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
+    L.qk_rmsnorm_fwd.restype = i32
+    L.qk_rmsnorm_fwd.argtypes = [vp] * 6 + [i64] * 8 + [f32, vp]
+    L.qk_rmsnorm_fwd_cfg.restype = i32
+    L.qk_rmsnorm_fwd_cfg.argtypes = [vp] * 6 + [i64] * 8 + [f32, ctypes.POINTER(LaunchCfg), vp]
     L.log1p_f32.argtypes = [vp, vp, i64, vp]
     L.log1p_f32_cfg.restype = i32
     L.log1p_f32_cfg.argtypes = [vp, vp, i64, ctypes.POINTER(Log1pCfg), vp]
@@ -246,11 +252,12 @@ def add_rmsnorm_fwd(out, residual_out, x, residual, weight, eps: float = 1e-6,
 
 def add_rmsnorm_fwd_cfg(out, residual_out, x, residual, weight, eps: float = 1e-6,
                         path: int = PATH_AUTO, block_threads: int = 0, grid_blocks: int = 0,
-                        stream=None) -> None:
-    """add_rmsnorm_fwd with an explicit launch configuration (same results)."""
+                        stream=None, rows_per_lane: int = 0) -> None:
+    """add_rmsnorm_fwd with an explicit launch configuration (same results).
+    rows_per_lane goes to the configuration's flags (the packed path only)."""
     n_rows, hidden, dev = _marshal(out, residual_out, x, residual, weight)
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_fwd_cfg(
         out.data_ptr(), residual_out.data_ptr(), x.data_ptr(), residual.data_ptr(),
@@ -347,7 +354,7 @@ def _row_view(t, hidden, dev, name):
 
 def add_rmsnorm_fwd_strided(out, residual_out, x, residual, weight, eps: float = 1e-6,
                             path: int = PATH_AUTO, block_threads: int = 0, grid_blocks: int = 0,
-                            stream=None) -> None:
+                            stream=None, rows_per_lane: int = 0) -> None:
     """The fused forward on 2-D views whose rows may be strided (e.g. column
     slices of wider matrices): each tensor [n_rows, hidden] with unit column
     stride; weight [hidden] contiguous."""
@@ -362,7 +369,7 @@ def add_rmsnorm_fwd_strided(out, residual_out, x, residual, weight, eps: float =
     if not (out.shape[0] == residual_out.shape[0] == residual.shape[0] == n_rows):
         raise ValueError("all views need the same number of rows")
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_fwd_strided(
         po, so, pro, sro, px, sx, pr, sr, weight.data_ptr(), n_rows, hidden, eps,
@@ -370,7 +377,8 @@ def add_rmsnorm_fwd_strided(out, residual_out, x, residual, weight, eps: float =
 
 
 def rmsnorm_fwd_strided(out, x, weight, eps: float = 1e-6, path: int = PATH_AUTO,
-                        block_threads: int = 0, grid_blocks: int = 0, stream=None) -> None:
+                        block_threads: int = 0, grid_blocks: int = 0, stream=None,
+                        rows_per_lane: int = 0) -> None:
     """Plain RMSNorm on 2-D views whose rows may be strided."""
     if weight.dim() != 1 or not weight.is_cuda or not weight.is_contiguous():
         raise ValueError("weight must be a contiguous 1-D GPU tensor")
@@ -380,7 +388,7 @@ def rmsnorm_fwd_strided(out, x, weight, eps: float = 1e-6, path: int = PATH_AUTO
     if out.shape[0] != x.shape[0]:
         raise ValueError("out and x need the same number of rows")
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.rmsnorm_fwd_strided(
         po, so, px, sx, weight.data_ptr(), x.shape[0], hidden, eps, ctypes.byref(cfg), h)))
@@ -397,11 +405,12 @@ def rmsnorm_fwd(out, x, weight, eps: float = 1e-6, stream=None) -> None:
 
 
 def rmsnorm_fwd_cfg(out, x, weight, eps: float = 1e-6, path: int = PATH_AUTO,
-                    block_threads: int = 0, grid_blocks: int = 0, stream=None) -> None:
+                    block_threads: int = 0, grid_blocks: int = 0, stream=None,
+                    rows_per_lane: int = 0) -> None:
     """rmsnorm_fwd with an explicit launch configuration (same results)."""
     n_rows, hidden, dev = _marshal(out, out, x, x, weight)
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.rmsnorm_fwd_cfg(
         out.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden, eps,
@@ -452,6 +461,74 @@ def rmsnorm_quant_fp8_fwd_cfg(out_q, out_scale, x, weight, eps: float = 1e-6,
     _check(_on_device(dev, lambda: L.rmsnorm_quant_fp8_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
         eps, ctypes.byref(cfg), h)))
+
+
+def _head_view(t, dev, name, head_dim):
+    """(pointer, heads, token stride in elements) of a [tokens, heads, head_dim]
+    bf16 view with heads contiguous within a token, or (0, 0, 0) for None."""
+    import torch
+
+    if t is None:
+        return 0, 0, 0
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.get_device() != dev:
+        raise ValueError("%s must be a GPU tensor on the weights' device" % name)
+    if t.dtype not in _dtypes():
+        raise TypeError("%s must hold bf16 (bfloat16, or raw 16-bit patterns)" % name)
+    if t.dim() != 3 or t.shape[2] != head_dim:
+        raise ValueError("%s must be [tokens, heads, head_dim]" % name)
+    heads = t.shape[1]
+    if heads > 0 and (t.stride(2) != 1 or (heads > 1 and t.stride(1) != head_dim)):
+        raise ValueError("%s: heads must be contiguous within a token" % name)
+    stride = t.stride(0) if t.shape[0] > 1 else heads * head_dim
+    return t.data_ptr(), heads, stride
+
+
+def _qk_call(q_out, k_out, q, k, q_weight, k_weight, eps, cfg, stream):
+    import torch
+
+    for w, name in ((q_weight, "q_weight"), (k_weight, "k_weight")):
+        if not isinstance(w, torch.Tensor) or not w.is_cuda or w.dim() != 1 or \
+                not w.is_contiguous() or w.dtype not in _dtypes():
+            raise ValueError("%s must be a contiguous 1-D bf16 GPU tensor" % name)
+    d, dev = q_weight.shape[0], q_weight.get_device()
+    if k_weight.shape[0] != d or k_weight.get_device() != dev:
+        raise ValueError("q_weight and k_weight must have one length and device")
+    pq, hq, sq = _head_view(q, dev, "q", d)
+    pk, hk, sk = _head_view(k, dev, "k", d)
+    pqo, hqo, sqo = _head_view(q_out, dev, "q_out", d)
+    pko, hko, sko = _head_view(k_out, dev, "k_out", d)
+    if hqo != hq or hko != hk:
+        raise ValueError("q_out and k_out must have the heads of q and k")
+    tokens = [t.shape[0] for t in (q, k, q_out, k_out) if t is not None and t.shape[1] > 0]
+    if len(set(tokens)) > 1:
+        raise ValueError("q, k and the outputs need the same number of tokens")
+    n_tokens = tokens[0] if tokens else 0
+    L = lib()
+    h = _stream_handle(dev, stream)
+    args = (pqo or None, pko or None, pq or None, pk or None, q_weight.data_ptr(),
+            k_weight.data_ptr(), n_tokens, hq, hk, d, sq, sk, sqo, sko, eps)
+    if cfg is None:
+        _check(_on_device(dev, lambda: L.qk_rmsnorm_fwd(*args, h)))
+    else:
+        _check(_on_device(dev, lambda: L.qk_rmsnorm_fwd_cfg(*args, ctypes.byref(cfg), h)))
+
+
+def qk_rmsnorm_fwd(q_out, k_out, q, k, q_weight, k_weight, eps: float = 1e-6,
+                   stream=None) -> None:
+    """Per-head RMSNorm of q [tokens, q_heads, head_dim] with q_weight
+    [head_dim] and of k [tokens, k_heads, head_dim] with k_weight, into q_out
+    and k_out (same shapes; may be q and k themselves).  Views may have any
+    token stride (e.g. column slices of a fused qkv tensor, reshaped); heads
+    are contiguous within a token.  k and k_out may be None (q only)."""
+    _qk_call(q_out, k_out, q, k, q_weight, k_weight, eps, None, stream)
+
+
+def qk_rmsnorm_fwd_cfg(q_out, k_out, q, k, q_weight, k_weight, eps: float = 1e-6,
+                       path: int = PATH_AUTO, block_threads: int = 0, grid_blocks: int = 0,
+                       rows_per_lane: int = 0, stream=None) -> None:
+    """qk_rmsnorm_fwd with an explicit launch configuration (same results)."""
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
+    _qk_call(q_out, k_out, q, k, q_weight, k_weight, eps, cfg, stream)
 
 
 def _marshal_log1p(out, x):

@@ -38,6 +38,7 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 bool aligned16(const void* p) { return aligned(p, 16); }
 
 bool valid_block(int b) { return b == 64 || b == 128 || b == 256 || b == 512 || b == 1024; }
+bool valid_rows_per_lane(int u) { return u == 1 || u == 2 || u == 4; }
 
 // Smallest of 1, 2, 4, 8 that is >= need (0 if none).
 int pow2_at_least(int64_t need) {
@@ -47,6 +48,9 @@ int pow2_at_least(int64_t need) {
 }
 
 // Default workgroup sizes per path.
+constexpr int kPackThreads = 256;
+constexpr int64_t kPackAutoMaxHidden = 256;
+constexpr int kPackRowsPerLane = 2;
 constexpr int kWaveRowThreads = 256;
 constexpr int kWgRowThreads = 512;
 constexpr int kTwoPassThreads = 512;
@@ -107,8 +111,10 @@ int check_scalars_any_hidden(int64_t n_rows, int64_t hidden, float eps,
   if (hidden > ADD_RMSNORM_MAX_HIDDEN) return ADD_RMSNORM_ERANGE;
   *c = add_rmsnorm_launch_cfg{ADD_RMSNORM_PATH_AUTO, 0, 0, 0};
   if (cfg) *c = *cfg;
-  if (c->flags != 0 || c->grid_blocks < -1) return ADD_RMSNORM_EINVAL;
-  if (c->path < ADD_RMSNORM_PATH_AUTO || c->path > ADD_RMSNORM_PATH_GENERAL)
+  if (c->grid_blocks < -1) return ADD_RMSNORM_EINVAL;
+  if (c->path < ADD_RMSNORM_PATH_AUTO || c->path > ADD_RMSNORM_PATH_PACKED)
+    return ADD_RMSNORM_EINVAL;
+  if (c->flags != 0 && !(c->path == ADD_RMSNORM_PATH_PACKED && valid_rows_per_lane(c->flags)))
     return ADD_RMSNORM_EINVAL;
   if (c->block_threads != 0 && !valid_block(c->block_threads)) return ADD_RMSNORM_EINVAL;
   return ADD_RMSNORM_OK;
@@ -146,6 +152,23 @@ bool views_overlap(View a, View b, int64_t n, uint64_t width) {
   return false;
 }
 
+// views_overlap for views of different widths (wa, wb bytes per row): with
+// one stride s they meet exactly when some row difference q in [-(n-1), n-1]
+// puts r = d + q s, d = b - a, inside (-wb, wa).  Different strides: as above.
+bool views_overlap2(View a, uint64_t wa, View b, uint64_t wb, int64_t n) {
+  const uint64_t span_a = (uint64_t)(n - 1) * a.stride + wa;
+  const uint64_t span_b = (uint64_t)(n - 1) * b.stride + wb;
+  if (!overlap(a.p, span_a, b.p, span_b)) return false;
+  if (a.stride != b.stride) return true;
+  const int64_t d = (int64_t)(reinterpret_cast<uintptr_t>(b.p) - reinterpret_cast<uintptr_t>(a.p));
+  const int64_t s = (int64_t)a.stride;
+  int64_t q_lo = floor_div(-(int64_t)wb - d, s) + 1;      // first q with r > -wb
+  int64_t q_hi = -floor_div(-((int64_t)wa - d), s) - 1;  // last q with r < wa
+  if (q_lo < -(n - 1)) q_lo = -(n - 1);
+  if (q_hi > n - 1) q_hi = n - 1;
+  return q_lo <= q_hi;
+}
+
 // Whether a view of n rows of `width` bytes shares a byte with the range
 // [q, q + len): some row i in [0, n) with i s < d + len and i s + width > d,
 // d = q - base.
@@ -176,6 +199,12 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   // on MI355X, one workgroup per row beats one wavefront per row at hidden
   // 2048 (by 5-13%) and the LDS two-pass kernel up to 16384 (by 7-25%).
   const bool variant = a.qout != nullptr || a.residual == nullptr;
+  // bf16-out rows of at most 32 segments pack several to a wavefront: measured
+  // on MI355X 1.2-3.9x one wavefront per row at hidden 64-256 (the fused and
+  // the plain op); at 512 the wavefront per row is as fast or faster.
+  if (path == ADD_RMSNORM_PATH_AUTO && a.qout == nullptr && hidden <= kPackAutoMaxHidden &&
+      a.n_rows < addrms::kPackMaxRows)
+    path = ADD_RMSNORM_PATH_PACKED;
   if (path == ADD_RMSNORM_PATH_AUTO && variant) {
     if (hidden <= kVariantWaveRowMaxHidden) {
       path = ADD_RMSNORM_PATH_WAVE_ROW;
@@ -199,6 +228,19 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   const int64_t segs = hidden / 8;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (path == ADD_RMSNORM_PATH_PACKED) {
+    if (a.qout != nullptr) return ADD_RMSNORM_EINVAL;
+    if (hidden > addrms::kPackMaxHidden || a.n_rows >= addrms::kPackMaxRows)
+      return ADD_RMSNORM_ERANGE;
+    const addrms::PackTensors g0 = {a.out, a.residual_out, a.x, a.residual, a.weight,
+                                    a.x_stride, a.r_stride, a.out_stride, a.ro_stride,
+                                    a.n_rows, 1};
+    const addrms::PackTensors g1 = {};
+    e = addrms::launch_pack_rows(g0, g1, (int32_t)hidden, a.eps, block ? block : kPackThreads,
+                                 c.flags ? c.flags : kPackRowsPerLane,
+                                 c.grid_blocks ? c.grid_blocks : -1, s);
+    return e != hipSuccess ? hip_failure(e) : ADD_RMSNORM_OK;
+  }
   // Plain RMSNorm (bf16 or int8 out) launches, by default, as many
   // workgroups as fit, looping over rows: each workgroup then reads the
   // weight once, which for these rows is as many bytes as x itself (measured
@@ -580,6 +622,106 @@ const char* add_rmsnorm_strerror(int status) {
 }
 
 const char* add_rmsnorm_last_hip_error(void) { return g_hip_error; }
+
+int qk_rmsnorm_fwd_cfg(uint16_t* q_out, uint16_t* k_out, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* q_weight, const uint16_t* k_weight, int64_t n_tokens,
+                       int64_t n_q_heads, int64_t n_k_heads, int64_t head_dim,
+                       int64_t q_stride, int64_t k_stride, int64_t q_out_stride,
+                       int64_t k_out_stride, float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                       struct ihipStream_t* stream) {
+  if (n_tokens < 0 || n_q_heads < 0 || n_k_heads < 0 || head_dim <= 0 || !std::isfinite(eps) ||
+      eps < 0.0f)
+    return ADD_RMSNORM_EINVAL;
+  add_rmsnorm_launch_cfg c = {ADD_RMSNORM_PATH_AUTO, 0, 0, 0};
+  if (cfg) c = *cfg;
+  if (c.path != ADD_RMSNORM_PATH_AUTO && c.path != ADD_RMSNORM_PATH_PACKED)
+    return ADD_RMSNORM_EINVAL;
+  if (c.grid_blocks < -1 || (c.flags != 0 && !valid_rows_per_lane(c.flags)) ||
+      (c.block_threads != 0 && !valid_block(c.block_threads)))
+    return ADD_RMSNORM_EINVAL;
+  if (head_dim > ADD_RMSNORM_MAX_HIDDEN) return ADD_RMSNORM_ERANGE;
+  if (head_dim % 8 != 0) return ADD_RMSNORM_EALIGN;
+  if (n_tokens == 0) return ADD_RMSNORM_OK;
+
+  struct Side {
+    uint16_t* out;
+    const uint16_t* in;
+    const uint16_t* weight;
+    int64_t heads, stride, out_stride;
+  };
+  const Side sides[2] = {{q_out, q, q_weight, n_q_heads, q_stride, q_out_stride},
+                         {k_out, k, k_weight, n_k_heads, k_stride, k_out_stride}};
+  int64_t rows = 0;
+  bool too_many = false;
+  for (const Side& d : sides) {
+    if (d.heads == 0) continue;
+    if (!d.out || !d.in || !d.weight) return ADD_RMSNORM_EINVAL;
+    if (d.heads > addrms::kPackMaxRows) return ADD_RMSNORM_ERANGE;
+    const int64_t width = d.heads * head_dim;
+    if (d.stride < width || d.out_stride < width) return ADD_RMSNORM_EINVAL;
+    if (!aligned16(d.out) || !aligned16(d.in) || !aligned16(d.weight) || d.stride % 8 != 0 ||
+        d.out_stride % 8 != 0)
+      return ADD_RMSNORM_EALIGN;
+    if (n_tokens > 0 && d.heads > (addrms::kPackMaxRows - 1) / n_tokens) {
+      too_many = true;
+    } else {
+      rows += n_tokens * d.heads;
+    }
+    for (int64_t st : {d.stride, d.out_stride})
+      if (n_tokens > 0 &&
+          (uint64_t)(n_tokens - 1) > ((uint64_t)INT64_MAX / 2 - (uint64_t)width) / (uint64_t)st)
+        return ADD_RMSNORM_ERANGE;
+  }
+  if (n_q_heads == 0 && n_k_heads == 0) return ADD_RMSNORM_OK;
+
+  // Outputs: each one either exactly its input's view (in place) or disjoint
+  // from it; disjoint from the other tensor, the other output and the weights.
+  const uint64_t hd_bytes = (uint64_t)head_dim * 2;
+  for (int i = 0; i < 2; ++i) {
+    const Side& d = sides[i];
+    if (d.heads == 0) continue;
+    const uint64_t width = (uint64_t)d.heads * hd_bytes;
+    const View vo = {d.out, (uint64_t)d.out_stride * 2}, vi = {d.in, (uint64_t)d.stride * 2};
+    if (output_meets_input(vo, vi, n_tokens, width)) return ADD_RMSNORM_EALIAS;
+    for (const Side& e : sides) {
+      if (e.heads == 0) continue;
+      if (view_meets_range(vo, n_tokens, width, e.weight, hd_bytes)) return ADD_RMSNORM_EALIAS;
+    }
+    const Side& o = sides[1 - i];
+    if (o.heads == 0) continue;
+    const uint64_t owidth = (uint64_t)o.heads * hd_bytes;
+    const View oo = {o.out, (uint64_t)o.out_stride * 2}, oi = {o.in, (uint64_t)o.stride * 2};
+    if (views_overlap2(vo, width, oi, owidth, n_tokens)) return ADD_RMSNORM_EALIAS;
+    if (i == 0 && views_overlap2(vo, width, oo, owidth, n_tokens)) return ADD_RMSNORM_EALIAS;
+  }
+
+  // Range limits last, so that a caller's views are checked whatever their size.
+  if (head_dim > addrms::kPackMaxHidden || too_many || rows >= addrms::kPackMaxRows)
+    return ADD_RMSNORM_ERANGE;
+
+  addrms::PackTensors g[2] = {};
+  for (int i = 0; i < 2; ++i) {
+    const Side& d = sides[i];
+    if (d.heads == 0) continue;
+    g[i] = addrms::PackTensors{d.out, nullptr, d.in, nullptr, d.weight, d.stride, 0,
+                               d.out_stride, 0, n_tokens, d.heads};
+  }
+  const hipError_t e = addrms::launch_pack_rows(
+      g[0], g[1], (int32_t)head_dim, eps, c.block_threads ? c.block_threads : kPackThreads,
+      c.flags ? c.flags : kPackRowsPerLane, c.grid_blocks ? c.grid_blocks : -1,
+      reinterpret_cast<hipStream_t>(stream));
+  return e != hipSuccess ? hip_failure(e) : ADD_RMSNORM_OK;
+}
+
+int qk_rmsnorm_fwd(uint16_t* q_out, uint16_t* k_out, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* q_weight, const uint16_t* k_weight, int64_t n_tokens,
+                   int64_t n_q_heads, int64_t n_k_heads, int64_t head_dim, int64_t q_stride,
+                   int64_t k_stride, int64_t q_out_stride, int64_t k_out_stride, float eps,
+                   struct ihipStream_t* stream) {
+  return qk_rmsnorm_fwd_cfg(q_out, k_out, q, k, q_weight, k_weight, n_tokens, n_q_heads,
+                            n_k_heads, head_dim, q_stride, k_stride, q_out_stride, k_out_stride,
+                            eps, nullptr, stream);
+}
 
 int add_rmsnorm_abi_version(void) { return ADD_RMSNORM_ABI_VERSION; }
 

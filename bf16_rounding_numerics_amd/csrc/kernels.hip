@@ -908,6 +908,129 @@ __global__ __launch_bounds__(WAVES * 64) void k_general_wave(GenParams p) {
   }
 }
 
+// ---------------------------------------------------------------- packed short rows
+
+// Rows of at most 64 segments (hidden <= 512), several per wavefront: P lanes
+// per row (the power of two >= the row's segments), 64 / P rows per
+// wavefront, lane l holding segment l % P of row slot l / P.  The P-lane
+// butterfly below is the canonical tree over the row's segments padded with
+// +0 to P leaves; the levels from P up to 64 leaves would add only +0 to a
+// sum of squares (never -0), which changes no bit, so every path gives the
+// same sums.  Each wavefront takes U row groups of 64 / P rows per iteration,
+// their loads issued together.
+//
+// Rows are addressed in two levels: row i of a group is head h = i % heads of
+// token t = i / heads, at segment t * token_stride + h * segs of each tensor
+// (a plain row tensor is one head per token).  Two groups, e.g. the q heads
+// and the k heads of attention with their own weights, share one launch: the
+// packed row index runs over group 0, padded to whole wavefront iterations,
+// then group 1, so each wavefront iteration lies in one group.
+struct PackGroup {
+  u32x4* out;
+  u32x4* residual_out;
+  const u32x4* x;
+  const u32x4* residual;
+  const u32x4* weight;
+  int64_t x_ts, r_ts, out_ts, ro_ts;  // token strides, in segments
+  uint32_t n_rows;                    // tokens * heads
+  uint32_t heads;
+  // ceil(2^64 / heads) for heads > 1, split in 32-bit halves: for i < 2^32,
+  // the high 64 bits of i * magic are exactly i / heads.
+  uint32_t magic_lo, magic_hi;
+};
+
+struct PackParams {
+  PackGroup g[2];
+  uint32_t first1;  // packed index of group 1's first row
+  uint32_t total;   // first1 + group 1's rows
+  int32_t segs;
+  float hidden_f;
+  float eps;
+};
+
+DEV uint32_t div_by_heads(uint32_t i, const PackGroup& g) {
+  if (g.heads == 1) return i;
+  const uint64_t a = (uint64_t)i * g.magic_hi + __umulhi(i, g.magic_lo);
+  return (uint32_t)(a >> 32);
+}
+
+// Sum over aligned blocks of P lanes (a power of two), the same bits in every
+// lane of a block: the first levels of wave_block_sum.  All 64 lanes active.
+template <int P>
+DEV float lane_block_sum(float v) {
+  if constexpr (P >= 2) v = v + ADDRMS_DPP(v, 0xB1);
+  if constexpr (P >= 4) v = v + ADDRMS_DPP(v, 0x4E);
+  if constexpr (P >= 8) v = v + ADDRMS_DPP(v, 0x141);
+  if constexpr (P >= 16) v = v + ADDRMS_DPP(v, 0x140);
+  if constexpr (P >= 32)
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  if constexpr (P >= 64) {
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    v = lo + hi;
+  }
+  return v;
+}
+
+template <int WAVES, int P, int U, bool R>
+__global__ __launch_bounds__(WAVES * 64) void k_pack_rows(PackParams p) {
+  constexpr int RW = 64 / P;  // rows per wavefront per row group
+  __shared__ u32x4 wl[2][P];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int C = p.segs;
+  const int s = lane % P;
+  const int slot = lane / P;
+  for (int i = threadIdx.x; i < 2 * P; i += WAVES * 64) {
+    const int g = i / P, k = i % P;
+    const u32x4* w = g ? p.g[1].weight : p.g[0].weight;
+    wl[g][k] = (k < C && w) ? w[k] : u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+
+  const int64_t step = (int64_t)gridDim.x * WAVES * RW * U;
+  for (int64_t base = ((int64_t)blockIdx.x * WAVES + wave) * RW * U; base < p.total;
+       base += step) {
+    const int g = base >= p.first1 ? 1 : 0;
+    const PackGroup G = g ? p.g[1] : p.g[0];
+    const uint32_t row0 = (uint32_t)base - (g ? p.first1 : 0u);
+    int64_t xo[U], oo[U], ro[U], rso[U];
+    bool valid[U];
+    u32x4 xq[U], rq[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = row0 + (uint32_t)(u * RW + slot);
+      valid[u] = i < G.n_rows && s < C;
+      const uint32_t t = div_by_heads(i, G);
+      const int64_t hs = (int64_t)(i - t * G.heads) * C + s;
+      xo[u] = (int64_t)t * G.x_ts + hs;
+      oo[u] = (int64_t)t * G.out_ts + hs;
+      ro[u] = (int64_t)t * G.r_ts + hs;
+      rso[u] = (int64_t)t * G.ro_ts + hs;
+      xq[u] = valid[u] ? load_stream(G.x + xo[u]) : u32x4{0, 0, 0, 0};
+      rq[u] = (R && valid[u]) ? load_stream(G.residual + ro[u]) : u32x4{0, 0, 0, 0};
+    }
+    float sum[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc[8];
+      sum[u] = add_segment<R>(xq[u], rq[u], acc);
+      if constexpr (R)
+        if (valid[u]) store_stream(G.residual_out + rso[u], pack8_rne(acc));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) sum[u] = lane_block_sum<P>(sum[u]);
+    const u32x4 w = wl[g][s];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float rinv = 1.0f / __builtin_sqrtf(sum[u] / p.hidden_f + p.eps);
+      float acc[8];
+      add8<R>(opaque(xq[u]), opaque(rq[u]), acc);
+      if (valid[u]) store_stream(G.out + oo[u], normalise8(acc, rinv, w));
+    }
+  }
+}
+
 // ---------------------------------------------------------------- epilogue test
 
 __global__ __launch_bounds__(256) void k_cvt_range(u32x4* out, uint32_t start, int64_t groups) {
@@ -1313,6 +1436,96 @@ hipError_t launch_general(const FwdArgs& a, int block_threads, int64_t grid_bloc
 
 size_t general_lds_bytes(int hidden) {
   return (size_t)((hidden + 7) / 8) * 32 + (size_t)two_pass_nb(hidden) * 4 + 64;
+}
+
+namespace {
+
+template <int P, int U, bool R>
+hipError_t go_pack(const PackParams& p, int block_threads, int64_t grid_blocks, hipStream_t s) {
+  const int64_t iters = ((int64_t)p.total + (64 / P) * U - 1) / ((64 / P) * U);
+  const int waves = block_threads / 64;
+  const int64_t groups = (iters + waves - 1) / waves;
+  switch (block_threads) {
+#define ADDRMS_PACK_CASE(B)                                                          \
+  case B: {                                                                          \
+    auto k = k_pack_rows<B / 64, P, U, R>;                                           \
+    const int64_t g = grid_blocks == -1 ? resident(k, B, 0) : grid_blocks;          \
+    hipLaunchKernelGGL(k, dim3(grid_for(g, groups)), dim3(B), 0, s, p);              \
+    return hipGetLastError();                                                        \
+  }
+    ADDRMS_PACK_CASE(64)
+    ADDRMS_PACK_CASE(128)
+    ADDRMS_PACK_CASE(256)
+    ADDRMS_PACK_CASE(512)
+    ADDRMS_PACK_CASE(1024)
+#undef ADDRMS_PACK_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int P, bool R>
+hipError_t pack_by_u(const PackParams& p, int b, int u, int64_t grid, hipStream_t s) {
+  switch (u) {
+    case 1: return go_pack<P, 1, R>(p, b, grid, s);
+    case 2: return go_pack<P, 2, R>(p, b, grid, s);
+    case 4: return go_pack<P, 4, R>(p, b, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool R>
+hipError_t pack_by_p(const PackParams& p, int lanes, int b, int u, int64_t grid,
+                     hipStream_t s) {
+  switch (lanes) {
+    case 1: return pack_by_u<1, R>(p, b, u, grid, s);
+    case 2: return pack_by_u<2, R>(p, b, u, grid, s);
+    case 4: return pack_by_u<4, R>(p, b, u, grid, s);
+    case 8: return pack_by_u<8, R>(p, b, u, grid, s);
+    case 16: return pack_by_u<16, R>(p, b, u, grid, s);
+    case 32: return pack_by_u<32, R>(p, b, u, grid, s);
+    case 64: return pack_by_u<64, R>(p, b, u, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+PackGroup make_group(const PackTensors& t) {
+  PackGroup g;
+  g.out = reinterpret_cast<u32x4*>(t.out);
+  g.residual_out = reinterpret_cast<u32x4*>(t.residual_out);
+  g.x = reinterpret_cast<const u32x4*>(t.x);
+  g.residual = reinterpret_cast<const u32x4*>(t.residual);
+  g.weight = reinterpret_cast<const u32x4*>(t.weight);
+  g.x_ts = t.x_token_stride / 8;
+  g.r_ts = t.r_token_stride / 8;
+  g.out_ts = t.out_token_stride / 8;
+  g.ro_ts = t.ro_token_stride / 8;
+  g.n_rows = (uint32_t)(t.n_tokens * t.heads);
+  g.heads = t.heads > 0 ? (uint32_t)t.heads : 1u;
+  const uint64_t m = g.heads > 1 ? ~0ull / g.heads + 1 : 0;
+  g.magic_lo = (uint32_t)m;
+  g.magic_hi = (uint32_t)(m >> 32);
+  return g;
+}
+
+}  // namespace
+
+hipError_t launch_pack_rows(const PackTensors& g0, const PackTensors& g1, int32_t hidden,
+                            float eps, int block_threads, int rows_per_lane,
+                            int64_t grid_blocks, hipStream_t s) {
+  PackParams p;
+  p.g[0] = make_group(g0);
+  p.g[1] = make_group(g1);
+  p.segs = hidden / 8;
+  int lanes = 1;
+  while (lanes < p.segs) lanes *= 2;
+  const uint64_t per_iter = (uint64_t)(64 / lanes) * (uint64_t)rows_per_lane;
+  const uint64_t first1 = ((uint64_t)p.g[0].n_rows + per_iter - 1) / per_iter * per_iter;
+  p.first1 = (uint32_t)first1;
+  p.total = (uint32_t)(first1 + p.g[1].n_rows);
+  p.hidden_f = (float)hidden;
+  p.eps = eps;
+  return g0.residual ? pack_by_p<true>(p, lanes, block_threads, rows_per_lane, grid_blocks, s)
+                     : pack_by_p<false>(p, lanes, block_threads, rows_per_lane, grid_blocks, s);
 }
 
 hipError_t launch_stream(uint16_t* dst, const uint16_t* src, int64_t count, int mode,

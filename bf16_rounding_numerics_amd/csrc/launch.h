@@ -56,6 +56,32 @@ hipError_t launch_general(const FwdArgs& a, int block_threads, int64_t grid_bloc
                           hipStream_t stream);
 size_t general_lds_bytes(int hidden);
 
+// One tensor group of the packed short-row kernel: n_tokens * heads rows of
+// `hidden` elements each, row (t, h) at element t * token_stride + h * hidden
+// of each tensor.  residual and residual_out are null for plain RMSNorm (then
+// in both groups).  heads == 0 or n_tokens == 0: no rows.
+struct PackTensors {
+  uint16_t* out;
+  uint16_t* residual_out;
+  const uint16_t* x;
+  const uint16_t* residual;
+  const uint16_t* weight;
+  int64_t x_token_stride, r_token_stride, out_token_stride, ro_token_stride;
+  int64_t n_tokens;
+  int64_t heads;
+};
+
+// Rows of hidden <= 512 packed several to a wavefront (the power of two P >=
+// hidden / 8 lanes per row), two groups in one launch (g1 may be empty),
+// bf16 out.  Needs hidden % 8 == 0, every pointer and token stride on 16
+// bytes, and fewer than 2^31 rows in all.  rows_per_lane (1, 2 or 4): row
+// groups each wavefront loads together; grid_blocks as launch_wave_row.
+hipError_t launch_pack_rows(const PackTensors& g0, const PackTensors& g1, int32_t hidden,
+                            float eps, int block_threads, int rows_per_lane,
+                            int64_t grid_blocks, hipStream_t stream);
+constexpr int64_t kPackMaxHidden = 512;
+constexpr int64_t kPackMaxRows = (int64_t)1 << 31;
+
 // Which (workgroup size, segments per thread) pairs are built: those whose
 // per-thread row share fits the register file without spilling.
 bool wave_row_supported(int block_threads, int segs_per_lane);

@@ -49,7 +49,7 @@ extern "C" {
 /* hipStream_t is a pointer to this opaque struct. */
 struct ihipStream_t;
 
-#define ADD_RMSNORM_ABI_VERSION 6
+#define ADD_RMSNORM_ABI_VERSION 7
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768
@@ -72,17 +72,18 @@ struct ihipStream_t;
  *   1 <= hidden <= ADD_RMSNORM_MAX_HIDDEN,
  *   eps finite and >= 0, added to the mean of squares inside the square root.
  * Pointers need only 2-byte alignment.  When hidden % 8 == 0 and every
- * pointer is 16-byte aligned one of the three fast kernels below runs;
+ * pointer is 16-byte aligned one of the fast kernels below runs;
  * otherwise the general kernel (element-wise loads and stores, the same
  * reduction tree, so the same results).
  * In place: an output may be the very same buffer as x or residual (e.g.
  * out == x and residual_out == residual, the usual residual-stream update);
  * any other overlap of an output with an input, the weight or the other
  * output is rejected with ADD_RMSNORM_EALIAS.
- * The fast kernel is chosen by hidden: one wavefront per row up to 2048, one
- * workgroup per row with the row held in registers up to 8192, and above
- * that one workgroup per row that stages the row's fp32 sums in LDS and
- * normalises in a second pass over LDS.
+ * The fast kernel is chosen by hidden: up to 256, several rows per
+ * wavefront (the power of two >= hidden / 8 lanes per row); one wavefront
+ * per row up to 2048, one workgroup per row with the row held in registers
+ * up to 8192, and above that one workgroup per row that stages the row's
+ * fp32 sums in LDS and normalises in a second pass over LDS.
  * Returns ADD_RMSNORM_OK or a negative status.
  */
 int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
@@ -115,6 +116,7 @@ int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residua
 #define ADD_RMSNORM_PATH_WG_ROW 2       /* hidden <= min(64 * block_threads, 16384) when forced */
 #define ADD_RMSNORM_PATH_LDS_TWO_PASS 3 /* any supported hidden */
 #define ADD_RMSNORM_PATH_GENERAL 4      /* any hidden, strides and 2-byte alignment (bf16 out only) */
+#define ADD_RMSNORM_PATH_PACKED 5       /* hidden <= 512, several rows per wavefront (bf16 out only) */
 
 /*
  * Launch configuration, for tests and benchmarks that must show that results
@@ -128,7 +130,8 @@ int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residua
  *                  general kernels; > 0: exactly that many workgroups, each
  *                  looping over rows (a persistent grid); -1: as many as fit
  *                  on the device at once.
- *   flags          must be 0.
+ *   flags          0, or on ADD_RMSNORM_PATH_PACKED the row groups each
+ *                  wavefront loads together: 1, 2 or 4.
  */
 struct add_rmsnorm_launch_cfg {
   int32_t path;
@@ -271,6 +274,51 @@ int rmsnorm_quant_fp8_fwd_cfg(uint8_t* out_q, float* out_scale, const uint16_t* 
                               const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
                               const struct add_rmsnorm_launch_cfg* cfg,
                               struct ihipStream_t* stream);
+
+/*
+ * Per-head RMSNorm of attention queries and keys, bf16 out.  The aiter
+ * issue's notes list a fused q/k norm kernel among those whose bf16 stores
+ * were not audited for rounding; the page does not spell out its arithmetic.
+ * This entry point takes the reading of the q/k normalisation in the decoder
+ * the issue's RL run uses (Qwen3-8B): every head vector of head_dim elements
+ * is one rmsnorm_fwd row over head_dim, q heads with q_weight and k heads
+ * with k_weight, the same eps, each out element rounded once to bf16 (nearest,
+ * ties to even).  Results are bit for bit rmsnorm_fwd's on the same rows, and
+ * do not depend on the launch.  Both tensors go in one launch.
+ *
+ * Layout: token t, head h of q is the head_dim elements at
+ * q + t * q_stride + h * head_dim (heads contiguous within a token, tokens
+ * q_stride elements apart: q may be a column slice of a fused qkv
+ * projection).  k, q_out and k_out likewise with their own token strides.
+ *   q_out, k_out  written; q_out may be exactly q's view (same pointer and
+ *                 stride: in place), k_out exactly k's; any other overlap of
+ *                 an output with an input, the other output or a weight is
+ *                 ADD_RMSNORM_EALIAS.
+ *   q, k          read.  q_weight, k_weight [head_dim] bf16, read.
+ *   n_tokens >= 0 (0: a no-op, nothing checked beyond the scalars);
+ *   n_q_heads, n_k_heads >= 0 (a tensor with no heads is not touched and its
+ *   pointers may be NULL); strides in elements, each at least
+ *   heads * head_dim.
+ * Requirements: head_dim in [8, 512] and a multiple of 8, every pointer
+ * 16-byte aligned and every stride a multiple of 8 (else ADD_RMSNORM_EALIGN;
+ * head_dim above 512 is ADD_RMSNORM_ERANGE), fewer than 2^31 head rows in
+ * all (else ADD_RMSNORM_ERANGE).  eps finite and >= 0.  Other errors,
+ * ownership and stream as add_rmsnorm_fwd.
+ */
+int qk_rmsnorm_fwd(uint16_t* q_out, uint16_t* k_out, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* q_weight, const uint16_t* k_weight, int64_t n_tokens,
+                   int64_t n_q_heads, int64_t n_k_heads, int64_t head_dim, int64_t q_stride,
+                   int64_t k_stride, int64_t q_out_stride, int64_t k_out_stride, float eps,
+                   struct ihipStream_t* stream);
+
+/* qk_rmsnorm_fwd with an explicit launch configuration (path AUTO or
+ * ADD_RMSNORM_PATH_PACKED; same results). */
+int qk_rmsnorm_fwd_cfg(uint16_t* q_out, uint16_t* k_out, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* q_weight, const uint16_t* k_weight, int64_t n_tokens,
+                       int64_t n_q_heads, int64_t n_k_heads, int64_t head_dim,
+                       int64_t q_stride, int64_t k_stride, int64_t q_out_stride,
+                       int64_t k_out_stride, float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                       struct ihipStream_t* stream);
 
 /*
  * Test hook for the store epilogue: out[i] = bf16_rne of the fp32 whose bit

@@ -157,7 +157,10 @@ def test_exact_in_place_aliases_pass_validation(kw):
 @pytest.mark.parametrize("cfg,status", [
     ((0, 0, 0, 1), arn.EINVAL),                 # flags must be 0
     ((9, 0, 0, 0), arn.EINVAL),                 # unknown path
-    ((5, 0, 0, 0), arn.EINVAL),
+    ((6, 0, 0, 0), arn.EINVAL),
+    ((arn.PATH_PACKED, 0, 0, 3), arn.EINVAL),   # rows per lane 1, 2 or 4
+    ((arn.PATH_PACKED, 0, 0, 8), arn.EINVAL),
+    ((arn.PATH_WAVE_ROW, 0, 0, 2), arn.EINVAL),  # flags only on the packed path
     ((-1, 0, 0, 0), arn.EINVAL),
     ((0, 100, 0, 0), arn.EINVAL),               # not a supported workgroup size
     ((0, 2048, 0, 0), arn.EINVAL),
@@ -174,6 +177,8 @@ def test_bad_launch_configuration(cfg, status):
     (arn.PATH_WG_ROW, 64, 8192),
     (arn.PATH_WG_ROW, 1024, 32768),     # 4 per thread at 1024 threads is not built
     (arn.PATH_WG_ROW, 0, 32768),
+    (arn.PATH_PACKED, 0, 520),          # more than 64 segments
+    (arn.PATH_PACKED, 0, 8192),
 ])
 @fake_addresses
 def test_forced_path_outside_its_range(path, block, h):
@@ -478,3 +483,127 @@ def test_strided_alias_check_against_brute_force():
         assert (got == arn.EALIAS) == expect_alias, (n, s_out, s_x, out - A, x - A, got)
         if not expect_alias:
             assert got in PASSED
+
+
+# ------------------------------------------------------------------ per-head q/k norm
+
+def qkcall(qo=A, ko=A + MB, q=A + 2 * MB, k=A + 3 * MB, qw=A + 4 * MB, kw=A + 5 * MB, t=4,
+          hq=4, hk=2, d=520, sq=None, sk=None, sqo=None, sko=None, eps=1e-6, cfg=None):
+    """qk_rmsnorm_fwd(_cfg) with fake addresses.  The default head_dim 520 is
+    beyond the kernel's 512 and is rejected after every other check, so a
+    call that passes them returns ERANGE and launches nothing."""
+    L = arn.lib()
+    sq = hq * d if sq is None else sq
+    sk = hk * d if sk is None else sk
+    sqo = hq * d if sqo is None else sqo
+    sko = hk * d if sko is None else sko
+    args = (qo, ko, q, k, qw, kw, t, hq, hk, d, sq, sk, sqo, sko, eps)
+    if cfg is None:
+        return L.qk_rmsnorm_fwd(*args, None)
+    c = arn.LaunchCfg(*cfg)
+    return L.qk_rmsnorm_fwd_cfg(*args, ctypes.byref(c), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), arn.ERANGE),                       # every check passed, head_dim too large
+    (dict(t=-1), arn.EINVAL),
+    (dict(hq=-1), arn.EINVAL),
+    (dict(d=0), arn.EINVAL),
+    (dict(eps=math.nan), arn.EINVAL),
+    (dict(eps=-1e-6), arn.EINVAL),
+    (dict(d=12), arn.EALIGN),
+    (dict(d=40000), arn.ERANGE),
+    (dict(q=0), arn.EINVAL),
+    (dict(ko=0), arn.EINVAL),
+    (dict(kw=0), arn.EINVAL),
+    (dict(q=A + 2 * MB + 8), arn.EALIGN),
+    (dict(kw=A + 5 * MB + 2), arn.EALIGN),
+    (dict(sq=4 * 520 - 8), arn.EINVAL),         # token stride below the heads' width
+    (dict(sko=2 * 520 + 4), arn.EALIGN),        # stride not on 8 elements
+    (dict(cfg=(arn.PATH_WAVE_ROW, 0, 0, 0)), arn.EINVAL),
+    (dict(cfg=(arn.PATH_PACKED, 0, 0, 3)), arn.EINVAL),
+    (dict(cfg=(arn.PATH_PACKED, 96, 0, 0)), arn.EINVAL),
+    (dict(cfg=(arn.PATH_PACKED, 0, -2, 0)), arn.EINVAL),
+    (dict(cfg=(arn.PATH_PACKED, 256, -1, 4)), arn.ERANGE),
+    (dict(qo=A + 2 * MB + 16), arn.EALIAS),     # q_out partly over q
+    (dict(qo=A + 3 * MB), arn.EALIAS),          # q_out on k
+    (dict(ko=A + 2 * MB + 1040), arn.EALIAS),   # k_out inside q
+    (dict(ko=A + 64), arn.EALIAS),              # k_out over q_out
+    (dict(qo=A + 5 * MB - 1040), arn.EALIAS),   # q_out runs over k's weight
+    (dict(qo=A + 2 * MB, ko=A + 3 * MB), arn.ERANGE),  # both in place: accepted
+    (dict(t=1 << 28, hq=8, hk=0, qo=A, q=A + (1 << 44), qw=A + (1 << 46)),
+     arn.ERANGE),                               # 2^31 head rows
+])
+@fake_addresses
+def test_qk_argument_errors(kw, status):
+    assert qkcall(**kw) == status
+
+
+@fake_addresses
+def test_qk_no_tokens_or_no_heads_are_no_ops():
+    assert qkcall(qo=0, ko=0, q=0, k=0, qw=0, kw=0, t=0, d=128) == arn.OK
+    assert qkcall(qo=0, ko=0, q=0, k=0, qw=0, kw=0, hq=0, hk=0, d=128) == arn.OK
+    # k absent: its pointers may be NULL, q is still checked
+    assert qkcall(ko=0, k=0, kw=0, hk=0) == arn.ERANGE
+    assert qkcall(ko=0, k=0, kw=0, hk=0, q=0) == arn.EINVAL
+
+
+@fake_addresses
+def test_qk_fused_qkv_layout_in_place():
+    # q, k, v as column blocks of one [t, (hq + 2 hk) d] tensor, normalised in place
+    d, hq, hk = 520, 4, 2
+    ld = (hq + 2 * hk) * d
+    base = A
+    kq = base + 2 * hq * d
+    assert qkcall(qo=base, q=base, ko=kq, k=kq, sq=ld, sk=ld, sqo=ld, sko=ld) == arn.ERANGE
+    # k_out shifted one head left: it covers q's last head
+    assert qkcall(qo=base, q=base, ko=kq - 2 * d, k=kq, sq=ld, sk=ld, sqo=ld,
+                 sko=ld) == arn.EALIAS
+    # q_out a separate contiguous tensor, k in place: accepted
+    assert qkcall(qo=A + 8 * MB, q=base, ko=kq, k=kq, sq=ld, sk=ld, sqo=hq * d,
+                  sko=ld) == arn.ERANGE
+    # q_out on v's columns: as wide as q, so it runs into the next token's q
+    assert qkcall(qo=kq + 2 * hk * d, q=base, ko=kq, k=kq, sq=ld, sk=ld, sqo=ld,
+                  sko=ld) == arn.EALIAS
+
+
+@fake_addresses
+def test_qk_alias_check_against_brute_force():
+    import random
+
+    rnd = random.Random(9)
+    d = 520
+    for _ in range(300):
+        t = rnd.choice([1, 2, 3, 5])
+        hq, hk = rnd.choice([1, 2, 3]), rnd.choice([1, 2])
+        ld = rnd.choice([(hq + 2 * hk) * d, (hq + hk) * d + 8, 4 * (hq + hk) * d])
+        sq = ld
+        sk = ld if rnd.random() < 0.8 else ld + 8
+        q = A + 16 * rnd.randrange(0, 2 * d)
+        k = A + 16 * rnd.randrange(0, 2 * d)
+        qo = A + 4 * MB
+        ko = A + 6 * MB
+        got = qkcall(qo=qo, ko=ko, q=q, k=k, qw=A + 10 * MB, kw=A + 11 * MB, t=t, hq=hq, hk=hk,
+                    d=d, sq=sq, sk=sk, sqo=ld, sko=ld)
+        # outputs far away; only the inputs may overlap each other, which is allowed
+        assert got == arn.ERANGE, (t, hq, hk, ld, sq, sk, q - A, k - A, got)
+        # now put k_out on top of q's region
+        ko2 = q + 16 * rnd.randrange(-d // 4, d // 2)
+        got = qkcall(qo=qo, ko=ko2, q=q, k=k, qw=A + 10 * MB, kw=A + 11 * MB, t=t, hq=hq,
+                    hk=hk, d=d, sq=sq, sk=sk, sqo=ld, sko=sk)
+        shared = bool(_bytes_of(ko2, sk, t, hk * d) & _bytes_of(q, sq, t, hq * d))
+        if not shared and sk == sq:
+            shared_k = ko2 == k or bool(_bytes_of(ko2, sk, t, hk * d) & _bytes_of(k, sk, t, hk * d))
+            if ko2 == k:
+                shared_k = False                        # exactly k's view: in place
+            expect = shared_k
+        elif sk == sq:
+            expect = True
+        else:
+            lo_a, hi_a = ko2, ko2 + 2 * ((t - 1) * sk + hk * d)
+            lo_b, hi_b = q, q + 2 * ((t - 1) * sq + hq * d)
+            span = lo_a < hi_b and lo_b < hi_a
+            shared_k = ko2 != k and bool(_bytes_of(ko2, sk, t, hk * d) &
+                                         _bytes_of(k, sk, t, hk * d))
+            expect = span or shared_k
+        assert (got == arn.EALIAS) == expect, (t, hq, hk, ld, sq, sk, q - A, k - A, ko2 - A, got)

@@ -25,11 +25,14 @@ def _gpu():
 BLOCKS = (64, 128, 256, 512, 1024)
 
 
-def configurations(h):
-    """Every (path, block, grid) that the library accepts for hidden h."""
+def configurations(h, packed=True):
+    """Every (path, block, grid) that the library accepts for hidden h (the
+    packed path only for bf16 out: packed=False leaves it out)."""
     segs = h // 8
     cfgs = []
     for b in BLOCKS:
+        if packed and segs <= 64:
+            cfgs.append((arn.PATH_PACKED, b))
         if segs <= 512 and not (b == 1024 and segs > 256):
             cfgs.append((arn.PATH_WAVE_ROW, b))
         j = -(-segs // b)
@@ -44,7 +47,8 @@ def configurations(h):
     return out
 
 
-@pytest.mark.parametrize("h", [64, 1000, 1024, 2048, 3000, 4096, 8192, 12288, 16384])
+@pytest.mark.parametrize("h", [64, 200, 512, 1000, 1024, 2048, 3000, 4096, 8192, 12288,
+                               16384])
 def test_every_launch_configuration_gives_the_same_bits(h):
     n = 37
     x, r, w = synth.workload(2000 + h, n, h)
