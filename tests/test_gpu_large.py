@@ -20,6 +20,7 @@ CASES = [
     (2 ** 20 + 5, 2048, [(arn.PATH_WG_ROW, 256, 0)]),
     (2 ** 18 + 3, 8192, [(arn.PATH_LDS_TWO_PASS, 1024, -1)]),
     (2 ** 17 + 3, 16384, [(arn.PATH_WG_ROW, 512, 0)]),
+    (2 ** 24 + 5, 128, [(arn.PATH_PACKED, 1024, 3), (arn.PATH_WAVE_ROW, 256, 0)]),
 ]
 
 

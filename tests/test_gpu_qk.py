@@ -241,3 +241,75 @@ def test_packed_path_strided_views():
     assert np.array_equal(got[:, 2 * h:3 * h], exp_res)
     assert np.array_equal(got[:, :h], m_out)
     assert (got[:, h:2 * h] == POISON).all() and (got[:, 3 * h:] == POISON).all()
+
+
+def test_qk_graph_replays_match_eager():
+    """qk_rmsnorm_fwd captured once in a HIP graph, in place on a qkv buffer,
+    replayed on fresh inputs with eager work in between; every replay equals
+    an eager call on the same inputs."""
+    import torch
+
+    t, hq, hk, d = 64, 8, 2, 128
+    dev = "cuda:0"
+    buf = torch.empty(t, (hq + 2 * hk) * d, dtype=torch.int16, device=dev)
+    q, k = _views(buf, hq, hk, d)
+    _, qw, kw = _qkv(6000, t, hq, hk, d)
+    qwd, kwd = to_dev(qw), to_dev(kw)
+
+    def fresh(rep):
+        return to_dev(_qkv(6001 + rep, t, hq, hk, d)[0])
+
+    announce("qk graph capture")
+    buf.copy_(fresh(0))
+    arn.qk_rmsnorm_fwd(q, k, q, k, qwd, kwd, 1e-6)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        arn.qk_rmsnorm_fwd(q, k, q, k, qwd, kwd, 1e-6)
+    torch.cuda.synchronize()
+    for rep in range(1, 4):
+        announce("qk graph replay %d" % rep)
+        x = fresh(rep)
+        buf.copy_(x)
+        g.replay()
+        xq, xk = _views(x, hq, hk, d)
+        eq = torch.empty(t, hq, d, dtype=torch.int16, device=dev)
+        ek = torch.empty(t, hk, d, dtype=torch.int16, device=dev)
+        arn.qk_rmsnorm_fwd(eq, ek, xq, xk, qwd, kwd, 1e-6)
+        _ = (x.float() * 2).sum()
+        torch.cuda.synchronize()
+        assert torch.equal(q, eq) and torch.equal(k, ek), rep
+        assert torch.equal(buf[:, (hq + hk) * d:], x[:, (hq + hk) * d:]), rep
+
+
+def test_qk_tensors_beyond_4gib():
+    """A qkv tensor of more than 2^31 elements per view: token offsets past
+    2^31 elements exercise the packed kernel's 64-bit addressing.  Tokens are
+    copies of a seeded block of 256 (token i is block token (5 i + 1) mod 256);
+    sampled tokens, on both sides of the boundary, are checked against the
+    oracle and the fp32 model."""
+    import torch
+
+    t, hq, hk, d = 2 ** 19 + 3, 32, 8, 128
+    width = (hq + 2 * hk) * d
+    assert t * width > 2 ** 31 and t * hq * d * 2 > 2 ** 32
+    block, qw, kw = _qkv(7000, 256, hq, hk, d)
+    idx = (5 * np.arange(t) + 1) % 256
+    dev = torch.device("cuda:0")
+    announce("qk large: %d tokens, %.1f GiB qkv" % (t, t * width * 2 / 2 ** 30))
+    buf = to_dev(block)[torch.from_numpy(idx).to(dev)]
+    q, k = _views(buf, hq, hk, d)
+    q_out = torch.empty(t, hq, d, dtype=torch.int16, device=dev)
+    k_out = torch.empty(t, hk, d, dtype=torch.int16, device=dev)
+    arn.qk_rmsnorm_fwd(q_out, k_out, q, k, to_dev(qw), to_dev(kw), 1e-6)
+    torch.cuda.synchronize()
+    edge = 2 ** 31 // width
+    toks = sorted({0, 1, 255, 256, t // 2, edge - 1, edge, edge + 1, 2 ** 31 // (hq * d),
+                   2 ** 31 // (hq * d) + 1, t - 2, t - 1})
+    sel = torch.tensor(toks, device=dev)
+    got_q = q_out[sel].cpu().numpy().view(np.uint16)
+    got_k = k_out[sel].cpu().numpy().view(np.uint16)
+    _check_heads(block[idx[toks]], hq, hk, d, qw, kw, 1e-6, got_q, got_k,
+                 "qk large tokens %s" % toks)
+    del buf, q_out, k_out
+    torch.cuda.empty_cache()
