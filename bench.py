@@ -527,7 +527,8 @@ def main(argv=None):
 
     if args.op == "general":
         path = "general"
-    elif args.op in ("bf16", "plain") and hidden <= 256:
+    elif (args.op in ("bf16", "plain") and hidden <= 256) or (args.op in QUANT_OPS and
+                                                                hidden <= 512):
         path = "pack_rows"
     elif args.op == "bf16":
         path = "wave_row" if hidden <= 2048 else "wg_row" if hidden <= 8192 else "lds_two_pass"

@@ -50,6 +50,7 @@ int pow2_at_least(int64_t need) {
 // Default workgroup sizes per path.
 constexpr int kPackThreads = 256;
 constexpr int64_t kPackAutoMaxHidden = 256;
+constexpr int64_t kPackAutoMaxHiddenQuant = 512;
 constexpr int kPackRowsPerLane = 2;
 constexpr int kWaveRowThreads = 256;
 constexpr int kWgRowThreads = 512;
@@ -85,8 +86,11 @@ int check_scalars(int64_t n_rows, int64_t hidden, float eps,
   if (hidden > ADD_RMSNORM_MAX_HIDDEN) return ADD_RMSNORM_ERANGE;
   *c = add_rmsnorm_launch_cfg{ADD_RMSNORM_PATH_AUTO, 0, 0, 0};
   if (cfg) *c = *cfg;
-  if (c->flags != 0 || c->grid_blocks < -1) return ADD_RMSNORM_EINVAL;
-  if (c->path < ADD_RMSNORM_PATH_AUTO || c->path > ADD_RMSNORM_PATH_LDS_TWO_PASS)
+  if (c->grid_blocks < -1) return ADD_RMSNORM_EINVAL;
+  if (c->path < ADD_RMSNORM_PATH_AUTO ||
+      (c->path > ADD_RMSNORM_PATH_LDS_TWO_PASS && c->path != ADD_RMSNORM_PATH_PACKED))
+    return ADD_RMSNORM_EINVAL;
+  if (c->flags != 0 && !(c->path == ADD_RMSNORM_PATH_PACKED && valid_rows_per_lane(c->flags)))
     return ADD_RMSNORM_EINVAL;
   if (c->block_threads != 0 && !valid_block(c->block_threads)) return ADD_RMSNORM_EINVAL;
   return ADD_RMSNORM_OK;
@@ -199,10 +203,11 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   // on MI355X, one workgroup per row beats one wavefront per row at hidden
   // 2048 (by 5-13%) and the LDS two-pass kernel up to 16384 (by 7-25%).
   const bool variant = a.qout != nullptr || a.residual == nullptr;
-  // bf16-out rows of at most 32 segments pack several to a wavefront: measured
-  // on MI355X 1.2-3.9x one wavefront per row at hidden 64-256 (the fused and
-  // the plain op); at 512 the wavefront per row is as fast or faster.
-  if (path == ADD_RMSNORM_PATH_AUTO && a.qout == nullptr && hidden <= kPackAutoMaxHidden &&
+  // Short rows pack several to a wavefront.  Measured on MI355X against one
+  // wavefront per row: bf16 out 1.2-3.9x at hidden 64-256, and as fast or
+  // slower at 512; quantised out 1.5-6x at 64-256 and 2-8% faster at 512.
+  if (path == ADD_RMSNORM_PATH_AUTO &&
+      hidden <= (a.qout ? kPackAutoMaxHiddenQuant : kPackAutoMaxHidden) &&
       a.n_rows < addrms::kPackMaxRows)
     path = ADD_RMSNORM_PATH_PACKED;
   if (path == ADD_RMSNORM_PATH_AUTO && variant) {
@@ -229,14 +234,14 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (path == ADD_RMSNORM_PATH_PACKED) {
-    if (a.qout != nullptr) return ADD_RMSNORM_EINVAL;
     if (hidden > addrms::kPackMaxHidden || a.n_rows >= addrms::kPackMaxRows)
       return ADD_RMSNORM_ERANGE;
-    const addrms::PackTensors g0 = {a.out, a.residual_out, a.x, a.residual, a.weight,
-                                    a.x_stride, a.r_stride, a.out_stride, a.ro_stride,
-                                    a.n_rows, 1};
+    const addrms::PackTensors g0 = {a.out, a.qout, a.qscale, a.residual_out, a.x, a.residual,
+                                    a.weight, a.x_stride, a.r_stride, a.out_stride,
+                                    a.ro_stride, a.n_rows, 1};
     const addrms::PackTensors g1 = {};
-    e = addrms::launch_pack_rows(g0, g1, (int32_t)hidden, a.eps, block ? block : kPackThreads,
+    e = addrms::launch_pack_rows(g0, g1, (int32_t)hidden, a.eps, a.qout ? a.qfmt : 0,
+                                 block ? block : kPackThreads,
                                  c.flags ? c.flags : kPackRowsPerLane,
                                  c.grid_blocks ? c.grid_blocks : -1, s);
     return e != hipSuccess ? hip_failure(e) : ADD_RMSNORM_OK;
@@ -703,11 +708,11 @@ int qk_rmsnorm_fwd_cfg(uint16_t* q_out, uint16_t* k_out, const uint16_t* q, cons
   for (int i = 0; i < 2; ++i) {
     const Side& d = sides[i];
     if (d.heads == 0) continue;
-    g[i] = addrms::PackTensors{d.out, nullptr, d.in, nullptr, d.weight, d.stride, 0,
-                               d.out_stride, 0, n_tokens, d.heads};
+    g[i] = addrms::PackTensors{d.out, nullptr, nullptr, nullptr, d.in, nullptr, d.weight,
+                               d.stride, 0, d.out_stride, 0, n_tokens, d.heads};
   }
   const hipError_t e = addrms::launch_pack_rows(
-      g[0], g[1], (int32_t)head_dim, eps, c.block_threads ? c.block_threads : kPackThreads,
+      g[0], g[1], (int32_t)head_dim, eps, 0, c.block_threads ? c.block_threads : kPackThreads,
       c.flags ? c.flags : kPackRowsPerLane, c.grid_blocks ? c.grid_blocks : -1,
       reinterpret_cast<hipStream_t>(stream));
   return e != hipSuccess ? hip_failure(e) : ADD_RMSNORM_OK;

@@ -927,6 +927,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_general_wave(GenParams p) {
 // then group 1, so each wavefront iteration lies in one group.
 struct PackGroup {
   u32x4* out;
+  u32x2* qout;    // 1-byte codes, contiguous [n_rows][segs * 8] (quantised out)
+  float* qscale;  // per-row scale (quantised out)
   u32x4* residual_out;
   const u32x4* x;
   const u32x4* residual;
@@ -954,6 +956,20 @@ DEV uint32_t div_by_heads(uint32_t i, const PackGroup& g) {
   return (uint32_t)(a >> 32);
 }
 
+// Unsigned maximum over aligned blocks of P lanes; all 64 lanes active.
+template <int P>
+DEV uint32_t lane_block_max(uint32_t v) {
+  if constexpr (P >= 2) v = umax(v, ADDRMS_DPP_U(v, 0xB1));
+  if constexpr (P >= 4) v = umax(v, ADDRMS_DPP_U(v, 0x4E));
+  if constexpr (P >= 8) v = umax(v, ADDRMS_DPP_U(v, 0x141));
+  if constexpr (P >= 16) v = umax(v, ADDRMS_DPP_U(v, 0x140));
+  if constexpr (P >= 32) v = umax(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  if constexpr (P >= 64)
+    v = umax((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+             (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+  return v;
+}
+
 // Sum over aligned blocks of P lanes (a power of two), the same bits in every
 // lane of a block: the first levels of wave_block_sum.  All 64 lanes active.
 template <int P>
@@ -972,7 +988,7 @@ DEV float lane_block_sum(float v) {
   return v;
 }
 
-template <int WAVES, int P, int U, bool R>
+template <int WAVES, int P, int U, int Q, bool R>
 __global__ __launch_bounds__(WAVES * 64) void k_pack_rows(PackParams p) {
   constexpr int RW = 64 / P;  // rows per wavefront per row group
   __shared__ u32x4 wl[2][P];
@@ -995,11 +1011,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_pack_rows(PackParams p) {
     const PackGroup G = g ? p.g[1] : p.g[0];
     const uint32_t row0 = (uint32_t)base - (g ? p.first1 : 0u);
     int64_t xo[U], oo[U], ro[U], rso[U];
+    uint32_t row[U];
     bool valid[U];
     u32x4 xq[U], rq[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t i = row0 + (uint32_t)(u * RW + slot);
+      row[u] = i;
       valid[u] = i < G.n_rows && s < C;
       const uint32_t t = div_by_heads(i, G);
       const int64_t hs = (int64_t)(i - t * G.heads) * C + s;
@@ -1021,12 +1039,43 @@ __global__ __launch_bounds__(WAVES * 64) void k_pack_rows(PackParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) sum[u] = lane_block_sum<P>(sum[u]);
     const u32x4 w = wl[g][s];
+    if constexpr (!Q) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float rinv = 1.0f / __builtin_sqrtf(sum[u] / p.hidden_f + p.eps);
-      float acc[8];
-      add8<R>(opaque(xq[u]), opaque(rq[u]), acc);
-      if (valid[u]) store_stream(G.out + oo[u], normalise8(acc, rinv, w));
+      for (int u = 0; u < U; ++u) {
+        const float rinv = 1.0f / __builtin_sqrtf(sum[u] / p.hidden_f + p.eps);
+        float acc[8];
+        add8<R>(opaque(xq[u]), opaque(rq[u]), acc);
+        if (valid[u]) store_stream(G.out + oo[u], normalise8(acc, rinv, w));
+      }
+    } else {
+      // y twice (the same fp32 operations, so the same values): once for the
+      // row maximum over the row's lanes, once for the codes.  Codes are
+      // contiguous per row, so a row's codes start at row * segs.
+      float rinv[U];
+      uint32_t m[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        rinv[u] = 1.0f / __builtin_sqrtf(sum[u] / p.hidden_f + p.eps);
+        float acc[8], y[8];
+        add8<R>(opaque(xq[u]), opaque(rq[u]), acc);
+        scale8(acc, rinv[u], w, y);
+        m[u] = valid[u] ? max_abs8(0u, y) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) m[u] = lane_block_max<P>(m[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float amax = __builtin_bit_cast(float, m[u]);
+        const float inv = qmax<Q>() / amax;
+        const bool ok = quantisable<Q>(amax);
+        if (valid[u] && s == 0) G.qscale[row[u]] = amax / qmax<Q>();
+        float acc[8], y[8];
+        add8<R>(opaque(xq[u]), opaque(rq[u]), acc);
+        scale8(acc, rinv[u], w, y);
+        if (valid[u])
+          store_codes_stream(G.qout + (int64_t)row[u] * C + s,
+                             ok ? quant8<Q>(y, inv) : u32x2{0, 0});
+      }
     }
   }
 }
@@ -1440,7 +1489,7 @@ size_t general_lds_bytes(int hidden) {
 
 namespace {
 
-template <int P, int U, bool R>
+template <int P, int U, int Q, bool R>
 hipError_t go_pack(const PackParams& p, int block_threads, int64_t grid_blocks, hipStream_t s) {
   const int64_t iters = ((int64_t)p.total + (64 / P) * U - 1) / ((64 / P) * U);
   const int waves = block_threads / 64;
@@ -1448,7 +1497,7 @@ hipError_t go_pack(const PackParams& p, int block_threads, int64_t grid_blocks, 
   switch (block_threads) {
 #define ADDRMS_PACK_CASE(B)                                                          \
   case B: {                                                                          \
-    auto k = k_pack_rows<B / 64, P, U, R>;                                           \
+    auto k = k_pack_rows<B / 64, P, U, Q, R>;                                        \
     const int64_t g = grid_blocks == -1 ? resident(k, B, 0) : grid_blocks;          \
     hipLaunchKernelGGL(k, dim3(grid_for(g, groups)), dim3(B), 0, s, p);              \
     return hipGetLastError();                                                        \
@@ -1463,27 +1512,27 @@ hipError_t go_pack(const PackParams& p, int block_threads, int64_t grid_blocks, 
   return hipErrorInvalidValue;
 }
 
-template <int P, bool R>
+template <int P, int Q, bool R>
 hipError_t pack_by_u(const PackParams& p, int b, int u, int64_t grid, hipStream_t s) {
   switch (u) {
-    case 1: return go_pack<P, 1, R>(p, b, grid, s);
-    case 2: return go_pack<P, 2, R>(p, b, grid, s);
-    case 4: return go_pack<P, 4, R>(p, b, grid, s);
+    case 1: return go_pack<P, 1, Q, R>(p, b, grid, s);
+    case 2: return go_pack<P, 2, Q, R>(p, b, grid, s);
+    case 4: return go_pack<P, 4, Q, R>(p, b, grid, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <bool R>
+template <int Q, bool R>
 hipError_t pack_by_p(const PackParams& p, int lanes, int b, int u, int64_t grid,
                      hipStream_t s) {
   switch (lanes) {
-    case 1: return pack_by_u<1, R>(p, b, u, grid, s);
-    case 2: return pack_by_u<2, R>(p, b, u, grid, s);
-    case 4: return pack_by_u<4, R>(p, b, u, grid, s);
-    case 8: return pack_by_u<8, R>(p, b, u, grid, s);
-    case 16: return pack_by_u<16, R>(p, b, u, grid, s);
-    case 32: return pack_by_u<32, R>(p, b, u, grid, s);
-    case 64: return pack_by_u<64, R>(p, b, u, grid, s);
+    case 1: return pack_by_u<1, Q, R>(p, b, u, grid, s);
+    case 2: return pack_by_u<2, Q, R>(p, b, u, grid, s);
+    case 4: return pack_by_u<4, Q, R>(p, b, u, grid, s);
+    case 8: return pack_by_u<8, Q, R>(p, b, u, grid, s);
+    case 16: return pack_by_u<16, Q, R>(p, b, u, grid, s);
+    case 32: return pack_by_u<32, Q, R>(p, b, u, grid, s);
+    case 64: return pack_by_u<64, Q, R>(p, b, u, grid, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1491,6 +1540,8 @@ hipError_t pack_by_p(const PackParams& p, int lanes, int b, int u, int64_t grid,
 PackGroup make_group(const PackTensors& t) {
   PackGroup g;
   g.out = reinterpret_cast<u32x4*>(t.out);
+  g.qout = reinterpret_cast<u32x2*>(t.qout);
+  g.qscale = t.qscale;
   g.residual_out = reinterpret_cast<u32x4*>(t.residual_out);
   g.x = reinterpret_cast<const u32x4*>(t.x);
   g.residual = reinterpret_cast<const u32x4*>(t.residual);
@@ -1510,7 +1561,7 @@ PackGroup make_group(const PackTensors& t) {
 }  // namespace
 
 hipError_t launch_pack_rows(const PackTensors& g0, const PackTensors& g1, int32_t hidden,
-                            float eps, int block_threads, int rows_per_lane,
+                            float eps, int qfmt, int block_threads, int rows_per_lane,
                             int64_t grid_blocks, hipStream_t s) {
   PackParams p;
   p.g[0] = make_group(g0);
@@ -1524,8 +1575,16 @@ hipError_t launch_pack_rows(const PackTensors& g0, const PackTensors& g1, int32_
   p.total = (uint32_t)(first1 + p.g[1].n_rows);
   p.hidden_f = (float)hidden;
   p.eps = eps;
-  return g0.residual ? pack_by_p<true>(p, lanes, block_threads, rows_per_lane, grid_blocks, s)
-                     : pack_by_p<false>(p, lanes, block_threads, rows_per_lane, grid_blocks, s);
+  const int b = block_threads, u = rows_per_lane;
+  if (qfmt == kQInt8)
+    return g0.residual ? pack_by_p<kQInt8, true>(p, lanes, b, u, grid_blocks, s)
+                       : pack_by_p<kQInt8, false>(p, lanes, b, u, grid_blocks, s);
+  if (qfmt == kQFp8)
+    return g0.residual ? pack_by_p<kQFp8, true>(p, lanes, b, u, grid_blocks, s)
+                       : pack_by_p<kQFp8, false>(p, lanes, b, u, grid_blocks, s);
+  if (qfmt != 0) return hipErrorInvalidValue;
+  return g0.residual ? pack_by_p<0, true>(p, lanes, b, u, grid_blocks, s)
+                     : pack_by_p<0, false>(p, lanes, b, u, grid_blocks, s);
 }
 
 hipError_t launch_stream(uint16_t* dst, const uint16_t* src, int64_t count, int mode,

@@ -61,7 +61,9 @@ size_t general_lds_bytes(int hidden);
 // of each tensor.  residual and residual_out are null for plain RMSNorm (then
 // in both groups).  heads == 0 or n_tokens == 0: no rows.
 struct PackTensors {
-  uint16_t* out;
+  uint16_t* out;       // bf16 out, or null for quantised out
+  void* qout;          // 1-byte codes, contiguous [rows][hidden] (quantised out), else null
+  float* qscale;       // per-row scale (quantised out), else null
   uint16_t* residual_out;
   const uint16_t* x;
   const uint16_t* residual;
@@ -72,12 +74,14 @@ struct PackTensors {
 };
 
 // Rows of hidden <= 512 packed several to a wavefront (the power of two P >=
-// hidden / 8 lanes per row), two groups in one launch (g1 may be empty),
-// bf16 out.  Needs hidden % 8 == 0, every pointer and token stride on 16
-// bytes, and fewer than 2^31 rows in all.  rows_per_lane (1, 2 or 4): row
-// groups each wavefront loads together; grid_blocks as launch_wave_row.
+// hidden / 8 lanes per row), two groups in one launch (g1 may be empty).
+// qfmt 0: bf16 out; 1 int8, 2 E4M3 codes with a per-row scale (the rows'
+// codes contiguous per group, row i at i * hidden bytes).  Needs hidden % 8
+// == 0, every pointer and token stride on 16 bytes, and fewer than 2^31 rows
+// in all.  rows_per_lane (1, 2 or 4): row groups each wavefront loads
+// together; grid_blocks as launch_wave_row.
 hipError_t launch_pack_rows(const PackTensors& g0, const PackTensors& g1, int32_t hidden,
-                            float eps, int block_threads, int rows_per_lane,
+                            float eps, int qfmt, int block_threads, int rows_per_lane,
                             int64_t grid_blocks, hipStream_t stream);
 constexpr int64_t kPackMaxHidden = 512;
 constexpr int64_t kPackMaxRows = (int64_t)1 << 31;

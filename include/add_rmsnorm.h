@@ -116,7 +116,7 @@ int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residua
 #define ADD_RMSNORM_PATH_WG_ROW 2       /* hidden <= min(64 * block_threads, 16384) when forced */
 #define ADD_RMSNORM_PATH_LDS_TWO_PASS 3 /* any supported hidden */
 #define ADD_RMSNORM_PATH_GENERAL 4      /* any hidden, strides and 2-byte alignment (bf16 out only) */
-#define ADD_RMSNORM_PATH_PACKED 5       /* hidden <= 512, several rows per wavefront (bf16 out only) */
+#define ADD_RMSNORM_PATH_PACKED 5       /* hidden <= 512, several rows per wavefront */
 
 /*
  * Launch configuration, for tests and benchmarks that must show that results
@@ -175,7 +175,8 @@ int add_rmsnorm_fwd_cfg(uint16_t* out, uint16_t* residual_out, const uint16_t* x
  * Codes and scales must not overlap any other buffer (ADD_RMSNORM_EALIAS).
  * Unlike add_rmsnorm_fwd, the quantised entry points need hidden % 8 == 0
  * and 16-byte aligned rows (ADD_RMSNORM_EALIGN otherwise) and take no general
- * path; everything else (sizes, errors, stream) as add_rmsnorm_fwd.
+ * path; everything else (sizes, errors, stream) as add_rmsnorm_fwd.  Rows up
+ * to hidden 512 take the packed kernel (several rows per wavefront).
  */
 int add_rmsnorm_quant_fwd(int8_t* out_q, float* out_scale, uint16_t* residual_out,
                           const uint16_t* x, const uint16_t* residual, const uint16_t* weight,

@@ -234,6 +234,17 @@ def test_quant_argument_errors(kw, status, fp8):
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
 @fake_addresses
+def test_quant_packed_path_configuration(fp8):
+    # the packed path takes quantised rows up to hidden 512; rows per lane 1, 2, 4
+    assert qcall(fp8=fp8, h=520, cfg=(arn.PATH_PACKED, 0, 0, 0)) == arn.ERANGE
+    assert qcall(fp8=fp8, h=1024, cfg=(arn.PATH_PACKED, 256, -1, 4)) == arn.ERANGE
+    assert qcall(fp8=fp8, cfg=(arn.PATH_PACKED, 0, 0, 3)) == arn.EINVAL
+    assert qcall(fp8=fp8, cfg=(arn.PATH_GENERAL, 0, 0, 0)) == arn.EINVAL
+    assert qcall(fp8=fp8, cfg=(arn.PATH_WG_ROW, 0, 0, 2)) == arn.EINVAL
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
+@fake_addresses
 def test_quant_zero_rows_and_in_place_validation(fp8):
     assert qcall(q=0, sc=0, res=0, x=0, r=0, w=0, n=0, fp8=fp8) == arn.OK
     # The fused entry points need both residual pointers.

@@ -26,8 +26,8 @@ BLOCKS = (64, 128, 256, 512, 1024)
 
 
 def configurations(h, packed=True):
-    """Every (path, block, grid) that the library accepts for hidden h (the
-    packed path only for bf16 out: packed=False leaves it out)."""
+    """Every (path, block, grid) that the library accepts for hidden h
+    (packed=False leaves the packed path out)."""
     segs = h // 8
     cfgs = []
     for b in BLOCKS:

@@ -187,8 +187,6 @@ def test_plain_every_launch_configuration(h):
     for path, b, grid in configurations(h):
         got = gpu_plain(x, w, path=path, block=b, grid=grid, xd=xd, wd=wd)
         assert np.array_equal(got, ref), (path, b, grid)
-        if path == arn.PATH_PACKED:
-            continue  # bf16 out only
         gq = gpu_plain_quant(x, w, path=path, block=b, grid=grid, xd=xd, wd=wd)
         assert np.array_equal(gq[0], qref[0]) and same_scale_bits(gq[1], qref[1]), (path, b, grid)
 

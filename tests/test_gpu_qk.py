@@ -313,3 +313,34 @@ def test_qk_tensors_beyond_4gib():
                  "qk large tokens %s" % toks)
     del buf, q_out, k_out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("h", [8, 24, 64, 128, 200, 256, 512])
+def test_packed_quantised_matches_wave_row(h):
+    """int8 and E4M3 codes, scales and residual_out on the packed kernel equal
+    one wavefront per row's, fused and plain, over several launches."""
+    from test_gpu_plain import gpu_plain_quant
+    from test_gpu_quant import check_model, gpu_quant, same_scale_bits
+    from test_gpu_quant_fp8 import gpu_fp8
+
+    n = 700 + h % 37
+    x, r, w = synth.workload(90 + h, n, h)
+    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    runs = {
+        "int8": lambda **c: gpu_quant(x, r, w, xd=xd, rd=rd, wd=wd, **c),
+        "fp8": lambda **c: gpu_fp8(x, r, w, xd=xd, rd=rd, wd=wd, **c),
+        "plain int8": lambda **c: gpu_plain_quant(x, w, xd=xd, wd=wd, **c) + (None,),
+        "plain fp8": lambda **c: gpu_fp8(x, None, w, xd=xd, wd=wd, **c),
+    }
+    for name, run in runs.items():
+        announce("packed quantised %s h=%d" % (name, h))
+        ref = run(path=arn.PATH_WAVE_ROW)
+        if name == "int8":
+            check_model(x, r, w, 1e-6, *ref, "wave_row int8 h=%d" % h)
+        for path, block, grid in ((0, 0, 0), (arn.PATH_PACKED, 64, 5), (arn.PATH_PACKED, 1024, -1),
+                                  (arn.PATH_PACKED, 256, 0)):
+            got = run(path=path, block=block, grid=grid)
+            assert np.array_equal(got[0], ref[0]), (name, h, path, block, grid)
+            assert same_scale_bits(got[1], ref[1]), (name, h, path, block, grid)
+            if ref[2] is not None:
+                assert np.array_equal(got[2], ref[2]), (name, h, path, block, grid)

@@ -139,7 +139,7 @@ def test_quant_every_launch_configuration(h):
     ref = gpu_quant(x, r, w)
     check_model(x, r, w, 1e-6, *ref, "auto h=%d" % h)
     xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
-    for path, b, grid in configurations(h, packed=False):
+    for path, b, grid in configurations(h):
         got = gpu_quant(x, r, w, path=path, block=b, grid=grid, xd=xd, rd=rd, wd=wd)
         assert np.array_equal(got[0], ref[0]), (path, b, grid)
         assert same_scale_bits(got[1], ref[1]), (path, b, grid)

@@ -219,7 +219,7 @@ def test_fp8_every_launch_configuration(h):
     for rr, rdd in ((r, rd), (None, None)):
         ref = gpu_fp8(x, rr, w, xd=xd, rd=rdd, wd=wd)
         check_model(x, rr, w, 1e-6, *ref, "auto h=%d" % h)
-        for path, b, grid in configurations(h, packed=False):
+        for path, b, grid in configurations(h):
             got = gpu_fp8(x, rr, w, path=path, block=b, grid=grid, xd=xd, rd=rdd, wd=wd)
             assert np.array_equal(got[0], ref[0]), (rr is None, path, b, grid)
             assert same_scale_bits(got[1], ref[1]), (rr is None, path, b, grid)
