@@ -91,6 +91,32 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
+def env_info(torch, arn):
+    """The run's environment: device, software versions, host CPU and the
+    library's build identity (target, flags, source digest)."""
+    props = torch.cuda.get_device_properties(0)
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
+            "hip": torch.version.hip, "torch": torch.__version__, "host_cpu": cpu,
+            "host_nproc": os.cpu_count(), "library_build": arn.add_rmsnorm_build_info()}
+
+
+def sha256_of(*arrays):
+    """Short SHA-256 digests of input buffers (the seeded generator's output
+    depends on the host's libm, so the digests identify the inputs)."""
+    import hashlib
+
+    return [hashlib.sha256(a.tobytes()).hexdigest()[:16] for a in arrays]
+
+
 def traffic_from_profiles(kernel_tag: str, workload: str, digest: str):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; else None."""
@@ -244,6 +270,8 @@ def bench_log1p(args, torch, arn, hip_build, synth):
                          "kernel_frac_of_copy": round(gbps / copy_gbps, 4),
                          "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
                          "what": "add_rmsnorm_test_copy2 moving x's two halves into out"},
+        "inputs_sha256": {"x": sha256_of(x)[0]},
+        "env": env_info(torch, arn),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -336,6 +364,8 @@ def bench_qk(args, torch, arn, hip_build, synth):
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
+        "inputs_sha256": dict(zip(("qkv", "q_weight", "k_weight"), sha256_of(qkv, qw, kw))),
+        "env": env_info(torch, arn),
     }
     if not args.no_compare:
         line["same_rows_two_rmsnorm_calls"] = {
@@ -577,6 +607,8 @@ def main(argv=None):
                          "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
                          "what": "add_rmsnorm_test_copy2 over the same bytes: two 16-byte "
                                  "nontemporal streaming copies, no arithmetic, same buffer rotation"},
+        "inputs_sha256": dict(zip(("x", "residual", "weight"), sha256_of(x, r, w))),
+        "env": env_info(torch, arn),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, r, w, eps, n_rows, hidden, args.cpu_seconds,

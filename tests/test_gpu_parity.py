@@ -231,6 +231,10 @@ def test_empty_inputs_through_every_entry_point():
     arn.rmsnorm_quant_fp8_fwd(torch.empty(0, 1024, dtype=torch.uint8, device=dev),
                               torch.empty(0, dtype=torch.float32, device=dev), e, w, 1e-6)
     arn.add_rmsnorm_fwd_strided(e, e.clone(), e.clone(), e.clone(), w, 1e-6)
+    hw = torch.ones(128, dtype=torch.int16, device=dev)
+    qe = torch.empty(0, 32, 128, dtype=torch.int16, device=dev)
+    ke = torch.empty(0, 8, 128, dtype=torch.int16, device=dev)
+    arn.qk_rmsnorm_fwd(qe, ke, qe.clone(), ke.clone(), hw, hw, 1e-6)
     f = torch.empty(0, dtype=torch.float32, device=dev)
     arn.log1p_f32(f, f.clone())
     torch.cuda.synchronize()
