@@ -17,7 +17,7 @@ MODES = ["out=x,residual_out=residual", "out=x", "residual_out=residual",
 
 @pytest.mark.parametrize("grid", [0, -1])
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("h", [1024, 2048, 4096, 8192, 16384])
+@pytest.mark.parametrize("h", [24, 128, 256, 1024, 2048, 4096, 8192, 16384])
 def test_in_place_matches_out_of_place(h, mode, grid):
     require_gpu()
     import torch
