@@ -189,9 +189,9 @@ def _marshal(out, residual_out, x, residual, weight):
     dts = _dtypes()
     if not isinstance(x, torch.Tensor) or not isinstance(weight, torch.Tensor):
         raise TypeError("expected torch tensors")
-    if not x.is_cuda:
+    dev = x.get_device()  # -1 for a CPU tensor
+    if dev < 0:
         raise ValueError("tensors must live on the GPU")
-    dev = x.get_device()
     shape = x.shape
     for t in (x, out, residual_out, residual):
         if not isinstance(t, torch.Tensor):
@@ -213,23 +213,43 @@ def _marshal(out, residual_out, x, residual, weight):
     return (x.numel() // hidden if hidden else 0), hidden, dev
 
 
+_RAW_STREAM = None
+
+
 def _stream_handle(dev, stream):
+    """The HIP stream to enqueue on: the given torch stream, else torch's
+    current stream for the device."""
+    global _RAW_STREAM
     if stream is not None:
         return stream.cuda_stream
-    import torch
+    if _RAW_STREAM is None:
+        import torch
 
-    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-    if raw is not None:
-        return raw(dev)
-    return torch.cuda.current_stream(dev).cuda_stream
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None) or (
+            lambda d: torch.cuda.current_stream(d).cuda_stream)
+    return _RAW_STREAM(dev)
+
+
+_CURRENT_DEVICE = None
+
+
+def _current_device():
+    """HIP's current device index.  The caller's tensors already live on a GPU,
+    so torch's lazy initialisation has run and its raw query is enough."""
+    global _CURRENT_DEVICE
+    if _CURRENT_DEVICE is None:
+        import torch
+
+        _CURRENT_DEVICE = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+    return _CURRENT_DEVICE()
 
 
 def _on_device(dev, fn):
     """Call fn with HIP's current device set to dev (switching only if needed)."""
+    if _current_device() == dev:
+        return fn()
     import torch
 
-    if torch.cuda.current_device() == dev:
-        return fn()
     with torch.cuda.device(dev):
         return fn()
 
@@ -302,11 +322,12 @@ def add_rmsnorm_quant_fwd(out_q, out_scale, residual_out, x, residual, weight,
 
 def add_rmsnorm_quant_fwd_cfg(out_q, out_scale, residual_out, x, residual, weight,
                               eps: float = 1e-6, path: int = PATH_AUTO, block_threads: int = 0,
-                              grid_blocks: int = 0, stream=None) -> None:
+                              grid_blocks: int = 0, stream=None,
+                              rows_per_lane: int = 0) -> None:
     """add_rmsnorm_quant_fwd with an explicit launch configuration."""
     n_rows, hidden, dev = _marshal_quant(out_q, out_scale, residual_out, x, residual, weight)
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
@@ -328,11 +349,12 @@ def add_rmsnorm_quant_fp8_fwd(out_q, out_scale, residual_out, x, residual, weigh
 def add_rmsnorm_quant_fp8_fwd_cfg(out_q, out_scale, residual_out, x, residual, weight,
                                   eps: float = 1e-6, path: int = PATH_AUTO,
                                   block_threads: int = 0, grid_blocks: int = 0,
-                                  stream=None) -> None:
+                                  stream=None,
+                                  rows_per_lane: int = 0) -> None:
     """add_rmsnorm_quant_fp8_fwd with an explicit launch configuration."""
     n_rows, hidden, dev = _marshal_quant(out_q, out_scale, residual_out, x, residual, weight, True)
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_quant_fp8_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), residual_out.data_ptr(), x.data_ptr(),
@@ -429,11 +451,12 @@ def rmsnorm_quant_fwd(out_q, out_scale, x, weight, eps: float = 1e-6, stream=Non
 
 
 def rmsnorm_quant_fwd_cfg(out_q, out_scale, x, weight, eps: float = 1e-6, path: int = PATH_AUTO,
-                          block_threads: int = 0, grid_blocks: int = 0, stream=None) -> None:
+                          block_threads: int = 0, grid_blocks: int = 0, stream=None,
+                          rows_per_lane: int = 0) -> None:
     """rmsnorm_quant_fwd with an explicit launch configuration."""
     n_rows, hidden, dev = _marshal_quant(out_q, out_scale, x, x, x, weight)
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.rmsnorm_quant_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
@@ -452,57 +475,64 @@ def rmsnorm_quant_fp8_fwd(out_q, out_scale, x, weight, eps: float = 1e-6, stream
 
 def rmsnorm_quant_fp8_fwd_cfg(out_q, out_scale, x, weight, eps: float = 1e-6,
                               path: int = PATH_AUTO, block_threads: int = 0,
-                              grid_blocks: int = 0, stream=None) -> None:
+                              grid_blocks: int = 0, stream=None,
+                              rows_per_lane: int = 0) -> None:
     """rmsnorm_quant_fp8_fwd with an explicit launch configuration."""
     n_rows, hidden, dev = _marshal_quant(out_q, out_scale, x, x, x, weight, True)
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, 0)
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.rmsnorm_quant_fp8_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
         eps, ctypes.byref(cfg), h)))
 
 
-def _head_view(t, dev, name, head_dim):
-    """(pointer, heads, token stride in elements) of a [tokens, heads, head_dim]
-    bf16 view with heads contiguous within a token, or (0, 0, 0) for None."""
-    import torch
-
+def _head_view(t, dev, name, head_dim, tensor_type, dts):
+    """(pointer, tokens, heads, token stride in elements) of a [tokens, heads,
+    head_dim] bf16 view with heads contiguous within a token, or
+    (0, 0, 0, 0) for None."""
     if t is None:
-        return 0, 0, 0
-    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.get_device() != dev:
+        return 0, 0, 0, 0
+    if not isinstance(t, tensor_type) or t.get_device() != dev:
         raise ValueError("%s must be a GPU tensor on the weights' device" % name)
-    if t.dtype not in _dtypes():
+    if t.dtype not in dts:
         raise TypeError("%s must hold bf16 (bfloat16, or raw 16-bit patterns)" % name)
-    if t.dim() != 3 or t.shape[2] != head_dim:
+    sh = t.shape
+    if len(sh) != 3 or sh[2] != head_dim:
         raise ValueError("%s must be [tokens, heads, head_dim]" % name)
-    heads = t.shape[1]
-    if heads > 0 and (t.stride(2) != 1 or (heads > 1 and t.stride(1) != head_dim)):
+    tokens, heads = sh[0], sh[1]
+    st = t.stride()
+    if heads > 0 and (st[2] != 1 or (heads > 1 and st[1] != head_dim)):
         raise ValueError("%s: heads must be contiguous within a token" % name)
-    stride = t.stride(0) if t.shape[0] > 1 else heads * head_dim
-    return t.data_ptr(), heads, stride
+    stride = st[0] if tokens > 1 else heads * head_dim
+    return t.data_ptr(), tokens, heads, stride
 
 
 def _qk_call(q_out, k_out, q, k, q_weight, k_weight, eps, cfg, stream):
     import torch
 
+    T, dts = torch.Tensor, _dtypes()
     for w, name in ((q_weight, "q_weight"), (k_weight, "k_weight")):
-        if not isinstance(w, torch.Tensor) or not w.is_cuda or w.dim() != 1 or \
-                not w.is_contiguous() or w.dtype not in _dtypes():
+        if not isinstance(w, T) or w.get_device() < 0 or len(w.shape) != 1 or \
+                not w.is_contiguous() or w.dtype not in dts:
             raise ValueError("%s must be a contiguous 1-D bf16 GPU tensor" % name)
     d, dev = q_weight.shape[0], q_weight.get_device()
     if k_weight.shape[0] != d or k_weight.get_device() != dev:
         raise ValueError("q_weight and k_weight must have one length and device")
-    pq, hq, sq = _head_view(q, dev, "q", d)
-    pk, hk, sk = _head_view(k, dev, "k", d)
-    pqo, hqo, sqo = _head_view(q_out, dev, "q_out", d)
-    pko, hko, sko = _head_view(k_out, dev, "k_out", d)
+    pq, tq, hq, sq = _head_view(q, dev, "q", d, T, dts)
+    pk, tk, hk, sk = _head_view(k, dev, "k", d, T, dts)
+    pqo, tqo, hqo, sqo = _head_view(q_out, dev, "q_out", d, T, dts)
+    pko, tko, hko, sko = _head_view(k_out, dev, "k_out", d, T, dts)
     if hqo != hq or hko != hk:
         raise ValueError("q_out and k_out must have the heads of q and k")
-    tokens = [t.shape[0] for t in (q, k, q_out, k_out) if t is not None and t.shape[1] > 0]
-    if len(set(tokens)) > 1:
+    tokens = set()
+    if hq > 0:
+        tokens.update((tq, tqo))
+    if hk > 0:
+        tokens.update((tk, tko))
+    if len(tokens) > 1:
         raise ValueError("q, k and the outputs need the same number of tokens")
-    n_tokens = tokens[0] if tokens else 0
+    n_tokens = tokens.pop() if tokens else 0
     L = lib()
     h = _stream_handle(dev, stream)
     args = (pqo or None, pko or None, pq or None, pk or None, q_weight.data_ptr(),

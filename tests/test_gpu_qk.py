@@ -344,3 +344,45 @@ def test_packed_quantised_matches_wave_row(h):
             assert same_scale_bits(got[1], ref[1]), (name, h, path, block, grid)
             if ref[2] is not None:
                 assert np.array_equal(got[2], ref[2]), (name, h, path, block, grid)
+
+
+@pytest.mark.parametrize("h", [16, 128, 512])
+def test_packed_quantised_rows_per_lane(h):
+    """Every rows-per-lane setting of the packed kernel gives one wavefront
+    per row's codes and scales, int8 and E4M3, fused and plain."""
+    import torch
+
+    from test_gpu_quant import same_scale_bits
+
+    n = 300 + h % 29
+    x, r, w = synth.workload(95 + h, n, h)
+    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    calls = {
+        "int8": (torch.int8, lambda q, sc, res, **c: arn.add_rmsnorm_quant_fwd_cfg(
+            q, sc, res, xd, rd, wd, 1e-6, **c)),
+        "fp8": (torch.uint8, lambda q, sc, res, **c: arn.add_rmsnorm_quant_fp8_fwd_cfg(
+            q, sc, res, xd, rd, wd, 1e-6, **c)),
+        "plain int8": (torch.int8, lambda q, sc, res, **c: arn.rmsnorm_quant_fwd_cfg(
+            q, sc, xd, wd, 1e-6, **c)),
+        "plain fp8": (torch.uint8, lambda q, sc, res, **c: arn.rmsnorm_quant_fp8_fwd_cfg(
+            q, sc, xd, wd, 1e-6, **c)),
+    }
+    for name, (dtype, call) in calls.items():
+        def run(**c):
+            q = torch.full((n, h), 99, dtype=dtype, device=xd.device)
+            sc = torch.full((n,), float("nan"), dtype=torch.float32, device=xd.device)
+            res = poisoned_like(xd)
+            call(q, sc, res, **c)
+            torch.cuda.synchronize()
+            return q.cpu().numpy(), sc.cpu().numpy(), from_dev(res)
+
+        announce("packed quantised rows per lane %s h=%d" % (name, h))
+        ref = run(path=arn.PATH_WAVE_ROW)
+        for rpl in (1, 2, 4):
+            for block, grid in ((64, 0), (512, 3)):
+                got = run(path=arn.PATH_PACKED, block_threads=block, grid_blocks=grid,
+                          rows_per_lane=rpl)
+                assert np.array_equal(got[0], ref[0]), (name, h, rpl, block, grid)
+                assert same_scale_bits(got[1], ref[1]), (name, h, rpl, block, grid)
+                if not name.startswith("plain"):
+                    assert np.array_equal(got[2], ref[2]), (name, h, rpl, block, grid)
