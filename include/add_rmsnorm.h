@@ -49,6 +49,11 @@ extern "C" {
 /* hipStream_t is a pointer to this opaque struct. */
 struct ihipStream_t;
 
+/* Declared below; named here so that every prototype refers to the one
+ * file-scope type (in C a struct first named in a parameter list would be
+ * local to that prototype). */
+struct add_rmsnorm_launch_cfg;
+
 #define ADD_RMSNORM_ABI_VERSION 7
 
 /* Largest supported hidden size. */
