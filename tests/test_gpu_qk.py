@@ -386,3 +386,26 @@ def test_packed_quantised_rows_per_lane(h):
                 assert same_scale_bits(got[1], ref[1]), (name, h, rpl, block, grid)
                 if not name.startswith("plain"):
                     assert np.array_equal(got[2], ref[2]), (name, h, rpl, block, grid)
+
+
+def test_qk_benchmark_workload_sampled():
+    """The benchmark's q/k workload at full size (4096 tokens x (32 + 8) heads
+    x 128 from a [4096, 6144] qkv tensor) in its default launch; sampled
+    tokens against the oracle and the fp32 model, and q_out and k_out fully
+    written (no poison left)."""
+    import torch
+
+    t, hq, hk, d = 4096, 32, 8, 128
+    buf, qw, kw = _qkv(8000, t, hq, hk, d)
+    dev = to_dev(buf)
+    q, k = _views(dev, hq, hk, d)
+    q_out = poisoned_like(q.contiguous())
+    k_out = poisoned_like(k.contiguous())
+    announce("qk benchmark workload 4096 x (32 + 8) x 128")
+    arn.qk_rmsnorm_fwd(q_out, k_out, q, k, to_dev(qw), to_dev(kw), 1e-6)
+    torch.cuda.synchronize()
+    qo, ko = from_dev(q_out), from_dev(k_out)
+    # finite inputs give finite outputs, so any poison NaN left is an unwritten element
+    assert not (qo == POISON).any() and not (ko == POISON).any()
+    toks = sorted({0, 1, 2, 3, 63, 64, 1000, 2047, 2048, 4093, 4094, 4095})
+    _check_heads(buf[toks], hq, hk, d, qw, kw, 1e-6, qo[toks], ko[toks], "qk benchmark workload")
