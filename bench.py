@@ -552,7 +552,7 @@ def ceilings(args, torch, arn, synth):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(rows would shard across GPUs with no communication); run with --gpus 1",
               file=sys.stderr)
         return 2
