@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -61,7 +61,9 @@ EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_fwd_strided",
            "rmsnorm_fwd_strided", "add_rmsnorm_quant_fwd", "add_rmsnorm_quant_fwd_cfg",
            "rmsnorm_fwd", "rmsnorm_fwd_cfg", "rmsnorm_quant_fwd", "rmsnorm_quant_fwd_cfg",
            "add_rmsnorm_quant_fp8_fwd", "add_rmsnorm_quant_fp8_fwd_cfg", "rmsnorm_quant_fp8_fwd",
-           "rmsnorm_quant_fp8_fwd_cfg", "qk_rmsnorm_fwd", "qk_rmsnorm_fwd_cfg",
+           "rmsnorm_quant_fp8_fwd_cfg", "add_rmsnorm_quant_fwd_strided",
+           "add_rmsnorm_quant_fp8_fwd_strided", "rmsnorm_quant_fwd_strided",
+           "rmsnorm_quant_fp8_fwd_strided", "qk_rmsnorm_fwd", "qk_rmsnorm_fwd_cfg",
            "log1p_f32", "log1p_f32_cfg",
            "add_rmsnorm_test_cvt_range", "add_rmsnorm_test_cvt_e4m3_range",
            "add_rmsnorm_test_copy2",
@@ -118,6 +120,14 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(LaunchCfg), vp]
     L.add_rmsnorm_test_cvt_e4m3_range.restype = i32
     L.add_rmsnorm_test_cvt_e4m3_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
+    for name in ("add_rmsnorm_quant_fwd_strided", "add_rmsnorm_quant_fp8_fwd_strided"):
+        getattr(L, name).restype = i32
+        getattr(L, name).argtypes = [vp, vp, vp, i64, vp, i64, vp, i64, vp, i64, i64, f32,
+                                     ctypes.POINTER(LaunchCfg), vp]
+    for name in ("rmsnorm_quant_fwd_strided", "rmsnorm_quant_fp8_fwd_strided"):
+        getattr(L, name).restype = i32
+        getattr(L, name).argtypes = [vp, vp, vp, i64, vp, i64, i64, f32,
+                                     ctypes.POINTER(LaunchCfg), vp]
     L.qk_rmsnorm_fwd.restype = i32
     L.qk_rmsnorm_fwd.argtypes = [vp] * 6 + [i64] * 8 + [f32, vp]
     L.qk_rmsnorm_fwd_cfg.restype = i32
@@ -485,6 +495,65 @@ def rmsnorm_quant_fp8_fwd_cfg(out_q, out_scale, x, weight, eps: float = 1e-6,
     _check(_on_device(dev, lambda: L.rmsnorm_quant_fp8_fwd_cfg(
         out_q.data_ptr(), out_scale.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden,
         eps, ctypes.byref(cfg), h)))
+
+
+def _code_view(q, sc, n_rows, hidden, dev, fp8):
+    """Check contiguous codes [n_rows, hidden] and scales [n_rows]."""
+    import torch
+
+    cd = torch.uint8 if fp8 else torch.int8
+    if not isinstance(q, torch.Tensor) or q.dtype != cd or tuple(q.shape) != (n_rows, hidden) \
+            or not q.is_contiguous() or q.get_device() != dev:
+        raise ValueError("out_q must be a contiguous [n_rows, hidden] %s GPU tensor" % cd)
+    if not isinstance(sc, torch.Tensor) or sc.dtype != torch.float32 or \
+            tuple(sc.shape) != (n_rows,) or not sc.is_contiguous() or sc.get_device() != dev:
+        raise ValueError("out_scale must be a contiguous [n_rows] float32 GPU tensor")
+
+
+def add_rmsnorm_quant_fwd_strided(out_q, out_scale, residual_out, x, residual, weight,
+                                  eps: float = 1e-6, fp8: bool = False, path: int = PATH_AUTO,
+                                  block_threads: int = 0, grid_blocks: int = 0,
+                                  rows_per_lane: int = 0, stream=None) -> None:
+    """Quantised fused forward (int8, or E4M3 with fp8=True) on 2-D views of
+    x, residual and residual_out whose rows may be strided; codes [n_rows,
+    hidden] and scales [n_rows] contiguous."""
+    if weight.dim() != 1 or not weight.is_cuda or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous 1-D GPU tensor")
+    hidden, dev = weight.shape[0], weight.get_device()
+    pro, sro = _row_view(residual_out, hidden, dev, "residual_out")
+    px, sx = _row_view(x, hidden, dev, "x")
+    pr, sr = _row_view(residual, hidden, dev, "residual")
+    n_rows = x.shape[0]
+    if not (residual_out.shape[0] == residual.shape[0] == n_rows):
+        raise ValueError("all views need the same number of rows")
+    _code_view(out_q, out_scale, n_rows, hidden, dev, fp8)
+    L = lib()
+    fn = L.add_rmsnorm_quant_fp8_fwd_strided if fp8 else L.add_rmsnorm_quant_fwd_strided
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: fn(out_q.data_ptr(), out_scale.data_ptr(), pro, sro, px, sx,
+                                      pr, sr, weight.data_ptr(), n_rows, hidden, eps,
+                                      ctypes.byref(cfg), h)))
+
+
+def rmsnorm_quant_fwd_strided(out_q, out_scale, x, weight, eps: float = 1e-6, fp8: bool = False,
+                              path: int = PATH_AUTO, block_threads: int = 0,
+                              grid_blocks: int = 0, rows_per_lane: int = 0,
+                              stream=None) -> None:
+    """Quantised plain RMSNorm on a 2-D view of x whose rows may be strided."""
+    if weight.dim() != 1 or not weight.is_cuda or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous 1-D GPU tensor")
+    hidden, dev = weight.shape[0], weight.get_device()
+    px, sx = _row_view(x, hidden, dev, "x")
+    n_rows = x.shape[0]
+    _code_view(out_q, out_scale, n_rows, hidden, dev, fp8)
+    L = lib()
+    fn = L.rmsnorm_quant_fp8_fwd_strided if fp8 else L.rmsnorm_quant_fwd_strided
+    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: fn(out_q.data_ptr(), out_scale.data_ptr(), px, sx,
+                                      weight.data_ptr(), n_rows, hidden, eps, ctypes.byref(cfg),
+                                      h)))
 
 
 def _head_view(t, dev, name, head_dim, tensor_type, dts):

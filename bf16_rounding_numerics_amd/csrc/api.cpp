@@ -384,11 +384,14 @@ int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
 namespace {
 
 // The quantised entry points, fused (residual set) or plain (residual and
-// residual_out null), with codes in format fmt (1 int8, 2 E4M3).
-int quant_fwd(void* out_q, float* out_scale, uint16_t* residual_out, const uint16_t* x,
-              const uint16_t* residual, const uint16_t* weight, int64_t n_rows, int64_t hidden,
-              float eps, const add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream,
-              int fmt) {
+// residual_out null), with codes in format fmt (1 int8, 2 E4M3).  x, residual
+// and residual_out are row-strided views (strides in elements); codes and
+// scales are contiguous.
+int quant_fwd_strided(void* out_q, float* out_scale, uint16_t* residual_out, int64_t ro_stride,
+                      const uint16_t* x, int64_t x_stride, const uint16_t* residual,
+                      int64_t r_stride, const uint16_t* weight, int64_t n_rows, int64_t hidden,
+                      float eps, const add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream,
+                      int fmt) {
   add_rmsnorm_launch_cfg c;
   int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
   if (rc != ADD_RMSNORM_OK) return rc;
@@ -397,34 +400,53 @@ int quant_fwd(void* out_q, float* out_scale, uint16_t* residual_out, const uint1
   const bool fused = residual != nullptr || residual_out != nullptr;
   if (!out_q || !out_scale || !x || !weight || (fused && (!residual || !residual_out)))
     return ADD_RMSNORM_EINVAL;
+  if (x_stride < hidden || (fused && (ro_stride < hidden || r_stride < hidden)))
+    return ADD_RMSNORM_EINVAL;
   if (!aligned16(out_q) || !aligned(out_scale, 4) || !aligned16(x) || !aligned16(weight) ||
-      (fused && (!aligned16(residual_out) || !aligned16(residual))))
+      x_stride % 8 != 0 ||
+      (fused && (!aligned16(residual_out) || !aligned16(residual) || ro_stride % 8 != 0 ||
+                 r_stride % 8 != 0)))
     return ADD_RMSNORM_EALIGN;
   const uint64_t row_bytes = (uint64_t)hidden * 2;
   if ((uint64_t)n_rows > (uint64_t)INT64_MAX / row_bytes) return ADD_RMSNORM_ERANGE;
-  const uint64_t t_bytes = (uint64_t)n_rows * row_bytes;
+  // Every view's span, (n_rows - 1) * stride + hidden elements, in bytes.
+  const int64_t strides[3] = {x_stride, fused ? r_stride : hidden, fused ? ro_stride : hidden};
+  for (int64_t st : strides)
+    if ((uint64_t)(n_rows - 1) > ((uint64_t)INT64_MAX / 2 - (uint64_t)hidden) / (uint64_t)st)
+      return ADD_RMSNORM_ERANGE;
   const uint64_t q_bytes = (uint64_t)n_rows * (uint64_t)hidden;
   const uint64_t s_bytes = (uint64_t)n_rows * 4;
-  // Codes and scales overlap nothing; residual_out as in the bf16 variant.
-  const void* ins[3] = {x, weight, residual};
-  const uint64_t in_bytes[3] = {t_bytes, row_bytes, t_bytes};
-  const int n_ins = fused ? 3 : 2;
+  const View vx = {x, (uint64_t)x_stride * 2}, vr = {residual, (uint64_t)r_stride * 2};
+  const View vro = {residual_out, (uint64_t)ro_stride * 2};
+  // Codes and scales overlap nothing: each other, the weight, any view.
   if (overlap(out_q, q_bytes, out_scale, s_bytes)) return ADD_RMSNORM_EALIAS;
-  if (fused && (overlap(out_q, q_bytes, residual_out, t_bytes) ||
-                overlap(out_scale, s_bytes, residual_out, t_bytes)))
+  if (overlap(out_q, q_bytes, weight, row_bytes) || overlap(out_scale, s_bytes, weight, row_bytes))
     return ADD_RMSNORM_EALIAS;
-  for (int i = 0; i < n_ins; ++i)
-    if (overlap(out_q, q_bytes, ins[i], in_bytes[i]) ||
-        overlap(out_scale, s_bytes, ins[i], in_bytes[i]))
+  const View* views[3] = {&vx, &vr, &vro};
+  for (int i = 0; i < (fused ? 3 : 1); ++i)
+    if (view_meets_range(*views[i], n_rows, row_bytes, out_q, q_bytes) ||
+        view_meets_range(*views[i], n_rows, row_bytes, out_scale, s_bytes))
       return ADD_RMSNORM_EALIAS;
-  if (fused && output_aliases_badly(residual_out, t_bytes, x, residual, weight, row_bytes))
+  // residual_out as in the bf16 variant: disjoint from the weight, and either
+  // exactly an input's view (in place) or disjoint from it.
+  if (fused && (view_meets_range(vro, n_rows, row_bytes, weight, row_bytes) ||
+                output_meets_input(vro, vx, n_rows, row_bytes) ||
+                output_meets_input(vro, vr, n_rows, row_bytes)))
     return ADD_RMSNORM_EALIAS;
 
-  const addrms::FwdArgs a = {nullptr,  out_q,  out_scale, residual_out,
-                             x,        residual, weight,  n_rows,
-                             (int32_t)hidden, eps, hidden, fused ? hidden : 0,
-                             hidden,   fused ? hidden : 0, fmt};
+  const addrms::FwdArgs a = {nullptr,  out_q,    out_scale, residual_out,
+                             x,        residual, weight,    n_rows,
+                             (int32_t)hidden, eps, x_stride, fused ? r_stride : 0,
+                             hidden,   fused ? ro_stride : 0, fmt};
   return dispatch(a, c, stream);
+}
+
+int quant_fwd(void* out_q, float* out_scale, uint16_t* residual_out, const uint16_t* x,
+              const uint16_t* residual, const uint16_t* weight, int64_t n_rows, int64_t hidden,
+              float eps, const add_rmsnorm_launch_cfg* cfg, struct ihipStream_t* stream,
+              int fmt) {
+  return quant_fwd_strided(out_q, out_scale, residual_out, hidden, x, hidden, residual, hidden,
+                           weight, n_rows, hidden, eps, cfg, stream, fmt);
 }
 
 constexpr int kFmtInt8 = 1;
@@ -627,6 +649,57 @@ const char* add_rmsnorm_strerror(int status) {
 }
 
 const char* add_rmsnorm_last_hip_error(void) { return g_hip_error; }
+
+int add_rmsnorm_quant_fwd_strided(int8_t* out_q, float* out_scale, uint16_t* residual_out,
+                                  int64_t residual_out_stride, const uint16_t* x,
+                                  int64_t x_stride, const uint16_t* residual,
+                                  int64_t residual_stride, const uint16_t* weight, int64_t n_rows,
+                                  int64_t hidden, float eps,
+                                  const struct add_rmsnorm_launch_cfg* cfg,
+                                  struct ihipStream_t* stream) {
+  if (!residual || !residual_out) {
+    add_rmsnorm_launch_cfg c;
+    const int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
+    return rc != ADD_RMSNORM_OK ? rc : n_rows == 0 ? ADD_RMSNORM_OK : ADD_RMSNORM_EINVAL;
+  }
+  return quant_fwd_strided(out_q, out_scale, residual_out, residual_out_stride, x, x_stride,
+                           residual, residual_stride, weight, n_rows, hidden, eps, cfg, stream,
+                           kFmtInt8);
+}
+
+int add_rmsnorm_quant_fp8_fwd_strided(uint8_t* out_q, float* out_scale, uint16_t* residual_out,
+                                      int64_t residual_out_stride, const uint16_t* x,
+                                      int64_t x_stride, const uint16_t* residual,
+                                      int64_t residual_stride, const uint16_t* weight,
+                                      int64_t n_rows, int64_t hidden, float eps,
+                                      const struct add_rmsnorm_launch_cfg* cfg,
+                                      struct ihipStream_t* stream) {
+  if (!residual || !residual_out) {
+    add_rmsnorm_launch_cfg c;
+    const int rc = check_scalars(n_rows, hidden, eps, cfg, &c);
+    return rc != ADD_RMSNORM_OK ? rc : n_rows == 0 ? ADD_RMSNORM_OK : ADD_RMSNORM_EINVAL;
+  }
+  return quant_fwd_strided(out_q, out_scale, residual_out, residual_out_stride, x, x_stride,
+                           residual, residual_stride, weight, n_rows, hidden, eps, cfg, stream,
+                           kFmtFp8);
+}
+
+int rmsnorm_quant_fwd_strided(int8_t* out_q, float* out_scale, const uint16_t* x,
+                              int64_t x_stride, const uint16_t* weight, int64_t n_rows,
+                              int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                              struct ihipStream_t* stream) {
+  return quant_fwd_strided(out_q, out_scale, nullptr, 0, x, x_stride, nullptr, 0, weight, n_rows,
+                           hidden, eps, cfg, stream, kFmtInt8);
+}
+
+int rmsnorm_quant_fp8_fwd_strided(uint8_t* out_q, float* out_scale, const uint16_t* x,
+                                  int64_t x_stride, const uint16_t* weight, int64_t n_rows,
+                                  int64_t hidden, float eps,
+                                  const struct add_rmsnorm_launch_cfg* cfg,
+                                  struct ihipStream_t* stream) {
+  return quant_fwd_strided(out_q, out_scale, nullptr, 0, x, x_stride, nullptr, 0, weight, n_rows,
+                           hidden, eps, cfg, stream, kFmtFp8);
+}
 
 int qk_rmsnorm_fwd_cfg(uint16_t* q_out, uint16_t* k_out, const uint16_t* q, const uint16_t* k,
                        const uint16_t* q_weight, const uint16_t* k_weight, int64_t n_tokens,

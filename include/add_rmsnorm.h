@@ -54,7 +54,7 @@ struct ihipStream_t;
  * local to that prototype). */
 struct add_rmsnorm_launch_cfg;
 
-#define ADD_RMSNORM_ABI_VERSION 7
+#define ADD_RMSNORM_ABI_VERSION 8
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768
@@ -280,6 +280,42 @@ int rmsnorm_quant_fp8_fwd_cfg(uint8_t* out_q, float* out_scale, const uint16_t* 
                               const uint16_t* weight, int64_t n_rows, int64_t hidden, float eps,
                               const struct add_rmsnorm_launch_cfg* cfg,
                               struct ihipStream_t* stream);
+
+/*
+ * The four quantised entry points over row-strided views of x, residual and
+ * residual_out (rows that are slices of wider matrices): row i of each view
+ * starts `*_stride` elements after row i - 1 (strides >= hidden, multiples of
+ * 8; ADD_RMSNORM_EINVAL below hidden, ADD_RMSNORM_EALIGN off 8).  Codes and
+ * scales stay contiguous ([n_rows, hidden] bytes and [n_rows] fp32) and
+ * overlap nothing.  residual_out may be exactly residual's or x's view (same
+ * pointer and stride: in place); any other shared element with an input or
+ * the weight is ADD_RMSNORM_EALIAS (with different strides, any overlap of
+ * the views' spans).  Results are those of the contiguous entry points on the
+ * same rows; everything else as there.  cfg may be NULL.
+ */
+int add_rmsnorm_quant_fwd_strided(int8_t* out_q, float* out_scale, uint16_t* residual_out,
+                                  int64_t residual_out_stride, const uint16_t* x,
+                                  int64_t x_stride, const uint16_t* residual,
+                                  int64_t residual_stride, const uint16_t* weight, int64_t n_rows,
+                                  int64_t hidden, float eps,
+                                  const struct add_rmsnorm_launch_cfg* cfg,
+                                  struct ihipStream_t* stream);
+int add_rmsnorm_quant_fp8_fwd_strided(uint8_t* out_q, float* out_scale, uint16_t* residual_out,
+                                      int64_t residual_out_stride, const uint16_t* x,
+                                      int64_t x_stride, const uint16_t* residual,
+                                      int64_t residual_stride, const uint16_t* weight,
+                                      int64_t n_rows, int64_t hidden, float eps,
+                                      const struct add_rmsnorm_launch_cfg* cfg,
+                                      struct ihipStream_t* stream);
+int rmsnorm_quant_fwd_strided(int8_t* out_q, float* out_scale, const uint16_t* x,
+                              int64_t x_stride, const uint16_t* weight, int64_t n_rows,
+                              int64_t hidden, float eps, const struct add_rmsnorm_launch_cfg* cfg,
+                              struct ihipStream_t* stream);
+int rmsnorm_quant_fp8_fwd_strided(uint8_t* out_q, float* out_scale, const uint16_t* x,
+                                  int64_t x_stride, const uint16_t* weight, int64_t n_rows,
+                                  int64_t hidden, float eps,
+                                  const struct add_rmsnorm_launch_cfg* cfg,
+                                  struct ihipStream_t* stream);
 
 /*
  * Per-head RMSNorm of attention queries and keys, bf16 out.  The aiter

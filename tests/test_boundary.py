@@ -618,3 +618,50 @@ def test_qk_alias_check_against_brute_force():
                                          _bytes_of(k, sk, t, hk * d))
             expect = span or shared_k
         assert (got == arn.EALIAS) == expect, (t, hq, hk, ld, sq, sk, q - A, k - A, ko2 - A, got)
+
+
+# ------------------------------------------------------------------ strided quantised views
+
+def sqcall(q=A + 10 * MB, sc=A + 12 * MB, res=A, sro=None, x=A + 2 * MB, sx=None, r=A + 4 * MB,
+           sr=None, w=A + 6 * MB, n=4, h=8192, cfg=(1, 0, 0, 0), fp8=False, plain=False):
+    """The strided quantised entry points with fake addresses.  The default
+    forced path (one wavefront per row) cannot take hidden 8192, so a call
+    that passes every check returns ERANGE and launches nothing."""
+    L = arn.lib()
+    c = arn.LaunchCfg(*cfg)
+    sx = h if sx is None else sx
+    if plain:
+        fn = L.rmsnorm_quant_fp8_fwd_strided if fp8 else L.rmsnorm_quant_fwd_strided
+        return fn(q, sc, x, sx, w, n, h, 1e-6, ctypes.byref(c), None)
+    sro = h if sro is None else sro
+    sr = h if sr is None else sr
+    fn = L.add_rmsnorm_quant_fp8_fwd_strided if fp8 else L.add_rmsnorm_quant_fwd_strided
+    return fn(q, sc, res, sro, x, sx, r, sr, w, n, h, 1e-6, ctypes.byref(c), None)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
+@fake_addresses
+def test_strided_quant_validation(fp8):
+    h = 8192
+    assert sqcall(fp8=fp8) == arn.ERANGE                       # every check passed
+    assert sqcall(fp8=fp8, sx=h - 8) == arn.EINVAL             # stride below hidden
+    assert sqcall(fp8=fp8, sro=h + 4) == arn.EALIGN            # stride off 8 elements
+    assert sqcall(fp8=fp8, x=A + 2 * MB + 8) == arn.EALIGN
+    assert sqcall(fp8=fp8, n=1 << 40, sx=1 << 30) == arn.ERANGE  # span overflows
+    # codes: inside x's first row, then in the gap between x's strided rows
+    assert sqcall(fp8=fp8, q=A + 2 * MB + 64) == arn.EALIAS
+    assert sqcall(fp8=fp8, sx=3 * h, q=A + 2 * MB + 2 * h) == arn.ERANGE
+    assert sqcall(fp8=fp8, sx=3 * h, q=A + 2 * MB + 2 * h + 16) == arn.EALIAS
+    # scales on residual_out's last row
+    assert sqcall(fp8=fp8, sc=A + 3 * 2 * h + 32) == arn.EALIAS
+    # residual_out in place on residual (same view), then the same pointer with another stride
+    assert sqcall(fp8=fp8, res=A + 4 * MB) == arn.ERANGE
+    assert sqcall(fp8=fp8, res=A + 4 * MB, sro=2 * h) == arn.EALIAS
+    # residual_out interleaved with x as column blocks of one matrix: accepted
+    assert sqcall(fp8=fp8, x=A + 2 * MB, sx=2 * h, res=A + 2 * MB + 2 * h, sro=2 * h) == arn.ERANGE
+    # the plain forms
+    assert sqcall(fp8=fp8, plain=True) == arn.ERANGE
+    assert sqcall(fp8=fp8, plain=True, sx=h - 8) == arn.EINVAL
+    assert sqcall(fp8=fp8, plain=True, q=A + 2 * MB + 3 * 2 * h) == arn.EALIAS
+    # zero rows: a no-op whatever the pointers
+    assert sqcall(fp8=fp8, n=0, q=0, sc=0, res=0, x=0, r=0, w=0) == arn.OK
