@@ -128,13 +128,14 @@ int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residua
  * do not depend on it.  Every field 0 means "the library's choice".
  *   path           one of ADD_RMSNORM_PATH_*.
  *   block_threads  workgroup size: 64, 128, 256, 512 or 1024 (the wave path
- *                  runs block_threads / 64 rows per workgroup).
+ *                  runs block_threads / 64 rows per workgroup, the packed
+ *                  path block_threads / 64 wavefronts of several rows each).
  *   grid_blocks    0: the library's choice: one workgroup per row (per row
  *                  group on the wave path) for the fused fast kernels, as
- *                  many as fit on the device for plain RMSNorm and the
- *                  general kernels; > 0: exactly that many workgroups, each
- *                  looping over rows (a persistent grid); -1: as many as fit
- *                  on the device at once.
+ *                  many as fit on the device for plain RMSNorm, the packed
+ *                  path and the general kernels; > 0: exactly that many
+ *                  workgroups, each looping over rows (a persistent grid);
+ *                  -1: as many as fit on the device at once.
  *   flags          0, or on ADD_RMSNORM_PATH_PACKED the row groups each
  *                  wavefront loads together: 1, 2 or 4.
  */
