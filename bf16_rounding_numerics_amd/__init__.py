@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -32,6 +32,7 @@ PATH_WG_ROW = 2
 PATH_LDS_TWO_PASS = 3
 PATH_GENERAL = 4
 PATH_PACKED = 5
+FLAG_LATE_WEIGHT = 1  # flags on PATH_WG_ROW: the weight read after each row's barrier
 
 
 class AddRmsnormError(RuntimeError):
@@ -282,12 +283,14 @@ def add_rmsnorm_fwd(out, residual_out, x, residual, weight, eps: float = 1e-6,
 
 def add_rmsnorm_fwd_cfg(out, residual_out, x, residual, weight, eps: float = 1e-6,
                         path: int = PATH_AUTO, block_threads: int = 0, grid_blocks: int = 0,
-                        stream=None, rows_per_lane: int = 0) -> None:
+                        stream=None, rows_per_lane: int = 0, late_weight: bool = False) -> None:
     """add_rmsnorm_fwd with an explicit launch configuration (same results).
-    rows_per_lane goes to the configuration's flags (the packed path only)."""
+    rows_per_lane (the packed path) or late_weight (the register path) go to
+    the configuration's flags."""
     n_rows, hidden, dev = _marshal(out, residual_out, x, residual, weight)
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
+    cfg = LaunchCfg(path, block_threads, grid_blocks,
+                    FLAG_LATE_WEIGHT if late_weight else rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_fwd_cfg(
         out.data_ptr(), residual_out.data_ptr(), x.data_ptr(), residual.data_ptr(),
@@ -438,11 +441,12 @@ def rmsnorm_fwd(out, x, weight, eps: float = 1e-6, stream=None) -> None:
 
 def rmsnorm_fwd_cfg(out, x, weight, eps: float = 1e-6, path: int = PATH_AUTO,
                     block_threads: int = 0, grid_blocks: int = 0, stream=None,
-                    rows_per_lane: int = 0) -> None:
+                    rows_per_lane: int = 0, late_weight: bool = False) -> None:
     """rmsnorm_fwd with an explicit launch configuration (same results)."""
     n_rows, hidden, dev = _marshal(out, out, x, x, weight)
     L = lib()
-    cfg = LaunchCfg(path, block_threads, grid_blocks, rows_per_lane)
+    cfg = LaunchCfg(path, block_threads, grid_blocks,
+                    FLAG_LATE_WEIGHT if late_weight else rows_per_lane)
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.rmsnorm_fwd_cfg(
         out.data_ptr(), x.data_ptr(), weight.data_ptr(), n_rows, hidden, eps,

@@ -406,8 +406,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 // B threads per row; thread t holds segments t, t + B, ..., t + B (J - 1).
 // For each j, wave w's butterfly yields the sum of block w + j * (B / 64);
 // the B / 64 * J block sums meet in LDS and every thread finishes the tree.
-template <int B, int J, int Q, bool R>
+// L (bf16 out only): the weight is not held in registers from the start but
+// read again for each row after the row's barrier, where the out stores need
+// it.  Measured on MI355X with one small workgroup per row (x and residual
+// together at most 64 MiB): 4-14% faster than holding it, as the row's
+// stores then follow its loads later (2048 x 4096: 12.0 against 13.1 us).
+template <int B, int J, int Q, bool R, bool L>
 __global__ __launch_bounds__(B) void k_wg_row(Params p) {
+  static_assert(!L || Q == 0, "the late weight read is built for bf16 out only");
   constexpr int W = B / 64;
   constexpr int NB = W * J;
   __shared__ float blk[2][NB];  // alternates by row so one barrier per row suffices
@@ -417,11 +423,13 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
   const int wave = t >> 6;
   const int C = p.segs;
 
-  u32x4 wq[J];
+  u32x4 wq[L ? 1 : J];
+  if constexpr (!L) {
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int s = t + B * j;
-    wq[j] = s < C ? p.weight[s] : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < J; ++j) {
+      const int s = t + B * j;
+      wq[j] = s < C ? p.weight[s] : u32x4{0, 0, 0, 0};
+    }
   }
 
   // Plain quantised rows are read and written through per-row buffer
@@ -475,14 +483,16 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int s = t + B * j;
-        if (s < C) store_stream(p.out + row * p.out_stride + s, normalise8(acc[j], rinv, wq[j]));
+        if (s < C)
+          store_stream(p.out + row * p.out_stride + s,
+                       normalise8(acc[j], rinv, L ? p.weight[s] : wq[L ? 0 : j]));
       }
     } else {
       uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         float y[8];
-        scale8(acc[j], rinv, wq[j], y);
+        scale8(acc[j], rinv, wq[L ? 0 : j], y);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[j][k] = y[k];
         if (t + B * j < C) m = max_abs8(m, y);
@@ -1230,21 +1240,31 @@ hipError_t go_wave(const Params& p, int j, int64_t grid, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int Q, bool R, int B>
+template <int Q, bool R, int B, bool L>
 hipError_t go_wg(const Params& p, int j, int64_t grid, hipStream_t s) {
   switch (j) {
-    case 1: return launch(k_wg_row<B, 1, Q, R>, B, 0, grid, p.n_rows, p, s);
-    case 2: return launch(k_wg_row<B, 2, Q, R>, B, 0, grid, p.n_rows, p, s);
+    case 1: return launch(k_wg_row<B, 1, Q, R, L>, B, 0, grid, p.n_rows, p, s);
+    case 2: return launch(k_wg_row<B, 2, Q, R, L>, B, 0, grid, p.n_rows, p, s);
     case 4:
       if constexpr (B * 4 <= 2048)
-        return launch(k_wg_row<B, 4, Q, R>, B, 0, grid, p.n_rows, p, s);
+        return launch(k_wg_row<B, 4, Q, R, L>, B, 0, grid, p.n_rows, p, s);
       break;
     case 8:
       if constexpr (B * 8 <= 2048)
-        return launch(k_wg_row<B, 8, Q, R>, B, 0, grid, p.n_rows, p, s);
+        return launch(k_wg_row<B, 8, Q, R, L>, B, 0, grid, p.n_rows, p, s);
       break;
   }
   return hipErrorInvalidValue;
+}
+
+template <int Q, bool R, int B>
+hipError_t go_wg_late(const Params& p, int j, int64_t grid, bool late, hipStream_t s) {
+  if constexpr (Q == 0) {
+    if (late) return go_wg<Q, R, B, true>(p, j, grid, s);
+  } else {
+    if (late) return hipErrorInvalidValue;
+  }
+  return go_wg<Q, R, B, false>(p, j, grid, s);
 }
 
 template <int Q, bool R, int B>
@@ -1269,13 +1289,13 @@ hipError_t wave_by_block(const Params& p, int b, int j, int64_t grid, hipStream_
 }
 
 template <int Q, bool R>
-hipError_t wg_by_block(const Params& p, int b, int j, int64_t grid, hipStream_t s) {
+hipError_t wg_by_block(const Params& p, int b, int j, int64_t grid, bool late, hipStream_t s) {
   switch (b) {
-    case 64: return go_wg<Q, R, 64>(p, j, grid, s);
-    case 128: return go_wg<Q, R, 128>(p, j, grid, s);
-    case 256: return go_wg<Q, R, 256>(p, j, grid, s);
-    case 512: return go_wg<Q, R, 512>(p, j, grid, s);
-    case 1024: return go_wg<Q, R, 1024>(p, j, grid, s);
+    case 64: return go_wg_late<Q, R, 64>(p, j, grid, late, s);
+    case 128: return go_wg_late<Q, R, 128>(p, j, grid, late, s);
+    case 256: return go_wg_late<Q, R, 256>(p, j, grid, late, s);
+    case 512: return go_wg_late<Q, R, 512>(p, j, grid, late, s);
+    case 1024: return go_wg_late<Q, R, 1024>(p, j, grid, late, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1408,18 +1428,19 @@ hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lan
 }
 
 hipError_t launch_wg_row(const FwdArgs& a, int block_threads, int segs_per_thread,
-                         int64_t grid_blocks, hipStream_t s) {
+                         int64_t grid_blocks, bool late_weight, hipStream_t s) {
   const Params p = make_params(a);
   const int b = block_threads, j = segs_per_thread;
+  const bool l = late_weight;
   if (a.qout && a.qfmt == kQInt8)
-    return a.residual ? wg_by_block<kQInt8, true>(p, b, j, grid_blocks, s)
-                      : wg_by_block<kQInt8, false>(p, b, j, grid_blocks, s);
+    return a.residual ? wg_by_block<kQInt8, true>(p, b, j, grid_blocks, l, s)
+                      : wg_by_block<kQInt8, false>(p, b, j, grid_blocks, l, s);
   if (a.qout && a.qfmt == kQFp8)
-    return a.residual ? wg_by_block<kQFp8, true>(p, b, j, grid_blocks, s)
-                      : wg_by_block<kQFp8, false>(p, b, j, grid_blocks, s);
+    return a.residual ? wg_by_block<kQFp8, true>(p, b, j, grid_blocks, l, s)
+                      : wg_by_block<kQFp8, false>(p, b, j, grid_blocks, l, s);
   if (a.qout) return hipErrorInvalidValue;
-  return a.residual ? wg_by_block<0, true>(p, b, j, grid_blocks, s)
-                    : wg_by_block<0, false>(p, b, j, grid_blocks, s);
+  return a.residual ? wg_by_block<0, true>(p, b, j, grid_blocks, l, s)
+                    : wg_by_block<0, false>(p, b, j, grid_blocks, l, s);
 }
 
 hipError_t launch_lds_two_pass(const FwdArgs& a, int block_threads, int64_t grid_blocks,

@@ -38,9 +38,11 @@ hipError_t launch_wave_row(const FwdArgs& a, int block_threads, int segs_per_lan
                            int64_t grid_blocks, hipStream_t stream);
 
 // One workgroup of block_threads per row, the row in registers:
-// segs_per_thread (1, 2, 4 or 8) segments per thread.
+// segs_per_thread (1, 2, 4 or 8) segments per thread.  late_weight (bf16 out
+// only; hipErrorInvalidValue for codes): the weight is read for each row after
+// the row's barrier instead of once per workgroup into registers.
 hipError_t launch_wg_row(const FwdArgs& a, int block_threads, int segs_per_thread,
-                         int64_t grid_blocks, hipStream_t stream);
+                         int64_t grid_blocks, bool late_weight, hipStream_t stream);
 
 // One workgroup per row; pass 1 streams the row in chunks of block_threads
 // segments, storing residual_out and staging fp32 sums in LDS; pass 2

@@ -54,7 +54,7 @@ struct ihipStream_t;
  * local to that prototype). */
 struct add_rmsnorm_launch_cfg;
 
-#define ADD_RMSNORM_ABI_VERSION 8
+#define ADD_RMSNORM_ABI_VERSION 9
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768
@@ -88,7 +88,10 @@ struct add_rmsnorm_launch_cfg;
  * wavefront (the power of two >= hidden / 8 lanes per row); one wavefront
  * per row up to 2048, one workgroup per row with the row held in registers
  * up to 8192, and above that one workgroup per row that stages the row's
- * fp32 sums in LDS and normalises in a second pass over LDS.
+ * fp32 sums in LDS and normalises in a second pass over LDS.  Small calls
+ * with hidden in [2048, 8192] (at most 4096 rows and 2^24 elements per
+ * tensor) take the register kernel with a smaller workgroup that reads the
+ * weight after each row's barrier (ADD_RMSNORM_FLAG_LATE_WEIGHT).
  * Returns ADD_RMSNORM_OK or a negative status.
  */
 int add_rmsnorm_fwd(uint16_t* out, uint16_t* residual_out, const uint16_t* x,
@@ -123,6 +126,11 @@ int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residua
 #define ADD_RMSNORM_PATH_GENERAL 4      /* any hidden, strides and 2-byte alignment (bf16 out only) */
 #define ADD_RMSNORM_PATH_PACKED 5       /* hidden <= 512, several rows per wavefront */
 
+/* flags value on ADD_RMSNORM_PATH_WG_ROW (bf16-out entry points only): the
+ * weight is read for each row after the row's barrier rather than held in
+ * registers from the workgroup's start.  The same results. */
+#define ADD_RMSNORM_FLAG_LATE_WEIGHT 1
+
 /*
  * Launch configuration, for tests and benchmarks that must show that results
  * do not depend on it.  Every field 0 means "the library's choice".
@@ -137,7 +145,9 @@ int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residua
  *                  workgroups, each looping over rows (a persistent grid);
  *                  -1: as many as fit on the device at once.
  *   flags          0, or on ADD_RMSNORM_PATH_PACKED the row groups each
- *                  wavefront loads together: 1, 2 or 4.
+ *                  wavefront loads together: 1, 2 or 4, or on
+ *                  ADD_RMSNORM_PATH_WG_ROW for bf16 out
+ *                  ADD_RMSNORM_FLAG_LATE_WEIGHT.
  */
 struct add_rmsnorm_launch_cfg {
   int32_t path;

@@ -49,7 +49,7 @@ def announce(msg: str) -> None:
 
 
 def gpu_fwd(x, r, w, eps=1e-6, path=0, block=0, grid=0, xd=None, rd=None, wd=None,
-            stream=None):
+            stream=None, late=False):
     """Run the HIP forward; returns (out, residual_out) as uint16 arrays."""
     import bf16_rounding_numerics_amd as arn
 
@@ -59,9 +59,9 @@ def gpu_fwd(x, r, w, eps=1e-6, path=0, block=0, grid=0, xd=None, rd=None, wd=Non
     wd = to_dev(w) if wd is None else wd
     out = poisoned_like(xd)
     res = poisoned_like(xd)
-    if path or block or grid:
+    if path or block or grid or late:
         arn.add_rmsnorm_fwd_cfg(out, res, xd, rd, wd, eps, path=path, block_threads=block,
-                                grid_blocks=grid, stream=stream)
+                                grid_blocks=grid, stream=stream, late_weight=late)
     else:
         arn.add_rmsnorm_fwd(out, res, xd, rd, wd, eps, stream=stream)
     torch.cuda.synchronize()

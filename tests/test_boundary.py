@@ -160,7 +160,11 @@ def test_exact_in_place_aliases_pass_validation(kw):
     ((6, 0, 0, 0), arn.EINVAL),
     ((arn.PATH_PACKED, 0, 0, 3), arn.EINVAL),   # rows per lane 1, 2 or 4
     ((arn.PATH_PACKED, 0, 0, 8), arn.EINVAL),
-    ((arn.PATH_WAVE_ROW, 0, 0, 2), arn.EINVAL),  # flags only on the packed path
+    ((arn.PATH_WAVE_ROW, 0, 0, 2), arn.EINVAL),  # flags only on the packed and register paths
+    ((arn.PATH_WAVE_ROW, 0, 0, 1), arn.EINVAL),
+    ((arn.PATH_WG_ROW, 0, 0, 2), arn.EINVAL),   # the register path's only flag is 1
+    ((arn.PATH_LDS_TWO_PASS, 0, 0, 1), arn.EINVAL),
+    ((arn.PATH_GENERAL, 0, 0, 1), arn.EINVAL),
     ((-1, 0, 0, 0), arn.EINVAL),
     ((0, 100, 0, 0), arn.EINVAL),               # not a supported workgroup size
     ((0, 2048, 0, 0), arn.EINVAL),
@@ -183,6 +187,8 @@ def test_bad_launch_configuration(cfg, status):
 @fake_addresses
 def test_forced_path_outside_its_range(path, block, h):
     assert call(h=h, cfg=(path, block, 0, 0)) == arn.ERANGE
+    if path == arn.PATH_WG_ROW:
+        assert call(h=h, cfg=(path, block, 0, arn.FLAG_LATE_WEIGHT)) == arn.ERANGE
 
 
 @fake_addresses
@@ -241,6 +247,8 @@ def test_quant_packed_path_configuration(fp8):
     assert qcall(fp8=fp8, cfg=(arn.PATH_PACKED, 0, 0, 3)) == arn.EINVAL
     assert qcall(fp8=fp8, cfg=(arn.PATH_GENERAL, 0, 0, 0)) == arn.EINVAL
     assert qcall(fp8=fp8, cfg=(arn.PATH_WG_ROW, 0, 0, 2)) == arn.EINVAL
+    # the late weight read is built for bf16 out only
+    assert qcall(fp8=fp8, cfg=(arn.PATH_WG_ROW, 0, 0, arn.FLAG_LATE_WEIGHT)) == arn.EINVAL
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])

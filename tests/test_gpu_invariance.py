@@ -25,9 +25,11 @@ def _gpu():
 BLOCKS = (64, 128, 256, 512, 1024)
 
 
-def configurations(h, packed=True):
+def configurations(h, packed=True, late=False):
     """Every (path, block, grid) that the library accepts for hidden h
-    (packed=False leaves the packed path out)."""
+    (packed=False leaves the packed path out); with late=True, (path, block,
+    grid, late_weight) for the bf16-out entry points, the register path also
+    with the weight read after each row's barrier."""
     segs = h // 8
     cfgs = []
     for b in BLOCKS:
@@ -43,7 +45,12 @@ def configurations(h, packed=True):
     out = []
     for path, b in cfgs:
         for grid in (0, 7, -1):
-            out.append((path, b, grid))
+            if not late:
+                out.append((path, b, grid))
+                continue
+            out.append((path, b, grid, False))
+            if path == arn.PATH_WG_ROW:
+                out.append((path, b, grid, True))
     return out
 
 
@@ -57,11 +64,12 @@ def test_every_launch_configuration_gives_the_same_bits(h):
     check_parity(x, r, w, 1e-6, ref_out, ref_res, label="auto h=%d" % h)
     xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
     groups = {}
-    for path, b, grid in configurations(h):
-        announce("  path %d block %d grid %d" % (path, b, grid))
-        out, res = gpu_fwd(x, r, w, 1e-6, path=path, block=b, grid=grid, xd=xd, rd=rd, wd=wd)
+    for path, b, grid, late in configurations(h, late=True):
+        announce("  path %d block %d grid %d late %d" % (path, b, grid, late))
+        out, res = gpu_fwd(x, r, w, 1e-6, path=path, block=b, grid=grid, xd=xd, rd=rd, wd=wd,
+                           late=late)
         key = (out.tobytes(), res.tobytes())
-        groups.setdefault(key, []).append((path, b, grid))
+        groups.setdefault(key, []).append((path, b, grid, late))
     assert len(groups) == 1, "%d result groups: %s" % (
         len(groups), [v[:3] for v in groups.values()])
     (only,) = groups

@@ -92,9 +92,11 @@ def test_association_order_rows_on_every_path(h):
     xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
     for eps in (0.0, 1e-6):
         m_out, m_res = fp32_model.add_rmsnorm(x, r, w, eps)
-        for path, b, grid in [(0, 0, 0)] + configurations(h):
-            announce("model tree rows hidden %d eps %g path %d block %d grid %d"
-                     % (h, eps, path, b, grid))
-            out, res = gpu_fwd(x, r, w, eps, path=path, block=b, grid=grid, xd=xd, rd=rd, wd=wd)
+        for path, b, grid, late in [(0, 0, 0, False)] + configurations(h, late=True):
+            announce("model tree rows hidden %d eps %g path %d block %d grid %d late %d"
+                     % (h, eps, path, b, grid, late))
+            out, res = gpu_fwd(x, r, w, eps, path=path, block=b, grid=grid, xd=xd, rd=rd, wd=wd,
+                               late=late)
             assert_same_bits(res, m_res, "tree h=%d residual_out" % h)
-            assert_same_bits(out, m_out, "tree h=%d path %d block %d grid %d" % (h, path, b, grid))
+            assert_same_bits(out, m_out, "tree h=%d path %d block %d grid %d late %d"
+                             % (h, path, b, grid, late))

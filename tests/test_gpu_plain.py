@@ -34,14 +34,15 @@ def _gpu():
     require_gpu()
 
 
-def gpu_plain(x, w, eps=1e-6, path=0, block=0, grid=0, xd=None, wd=None):
+def gpu_plain(x, w, eps=1e-6, path=0, block=0, grid=0, xd=None, wd=None, late=False):
     import torch
 
     xd = to_dev(x) if xd is None else xd
     wd = to_dev(w) if wd is None else wd
     out = poisoned_like(xd)
-    if path or block or grid:
-        arn.rmsnorm_fwd_cfg(out, xd, wd, eps, path=path, block_threads=block, grid_blocks=grid)
+    if path or block or grid or late:
+        arn.rmsnorm_fwd_cfg(out, xd, wd, eps, path=path, block_threads=block, grid_blocks=grid,
+                            late_weight=late)
     else:
         arn.rmsnorm_fwd(out, xd, wd, eps)
     torch.cuda.synchronize()
@@ -184,9 +185,11 @@ def test_plain_every_launch_configuration(h):
     check_plain(x, w, 1e-6, ref, "auto h=%d" % h)
     qref = gpu_plain_quant(x, w)
     xd, wd = to_dev(x), to_dev(w)
-    for path, b, grid in configurations(h):
-        got = gpu_plain(x, w, path=path, block=b, grid=grid, xd=xd, wd=wd)
-        assert np.array_equal(got, ref), (path, b, grid)
+    for path, b, grid, late in configurations(h, late=True):
+        got = gpu_plain(x, w, path=path, block=b, grid=grid, xd=xd, wd=wd, late=late)
+        assert np.array_equal(got, ref), (path, b, grid, late)
+        if late:
+            continue  # the late weight read is built for bf16 out only
         gq = gpu_plain_quant(x, w, path=path, block=b, grid=grid, xd=xd, wd=wd)
         assert np.array_equal(gq[0], qref[0]) and same_scale_bits(gq[1], qref[1]), (path, b, grid)
 
