@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -94,12 +95,26 @@ constexpr int64_t kVariantWaveRowMaxHidden = 1024;
 constexpr int64_t kVariantWgRowMaxHidden = 16384;
 constexpr int kVariantWgRowSmallThreads = 128;
 
+// The device's LDS limit per workgroup, asked of the runtime once per device
+// (a device attribute never changes; the query costs host time per call).
+constexpr int kMaxCachedDevices = 64;
+std::atomic<int> g_max_lds[kMaxCachedDevices];  // 0: not asked yet
+
 int device_max_lds(int* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_failure(e);
+  if (dev >= 0 && dev < kMaxCachedDevices) {
+    const int v = g_max_lds[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *out = v;
+      return ADD_RMSNORM_OK;
+    }
+  }
   e = hipDeviceGetAttribute(out, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess) return hip_failure(e);
+  if (dev >= 0 && dev < kMaxCachedDevices && *out > 0)
+    g_max_lds[dev].store(*out, std::memory_order_relaxed);
   return ADD_RMSNORM_OK;
 }
 

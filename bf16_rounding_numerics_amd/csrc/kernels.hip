@@ -48,6 +48,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+
 #include "launch.h"
 
 namespace addrms {
@@ -1187,17 +1190,47 @@ unsigned grid_for(int64_t grid_blocks, int64_t row_groups) {
   return (unsigned)g;
 }
 
+// Resident-workgroup counts already asked of the runtime, by (device, kernel,
+// workgroup size, LDS bytes): the occupancy query costs microseconds of host
+// time, and its answer never changes for a kernel on a device.  Shared by all
+// host threads.
+struct ResidentKey {
+  int dev;
+  const void* kernel;
+  int block_threads;
+  size_t lds;
+  bool operator<(const ResidentKey& o) const {
+    if (dev != o.dev) return dev < o.dev;
+    if (kernel != o.kernel) return kernel < o.kernel;
+    if (block_threads != o.block_threads) return block_threads < o.block_threads;
+    return lds < o.lds;
+  }
+};
+std::mutex g_resident_mu;
+std::map<ResidentKey, int64_t> g_resident;
+
 // Workgroups of a kernel that fit on the current device at once; 0 if unknown.
 template <typename K>
 int64_t resident(K kernel, int block_threads, size_t lds) {
   int dev = 0, per_cu = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const ResidentKey key{dev, reinterpret_cast<const void*>(kernel), block_threads, lds};
+  {
+    std::lock_guard<std::mutex> g(g_resident_mu);
+    const auto it = g_resident.find(key);
+    if (it != g_resident.end()) return it->second;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, lds) !=
       hipSuccess)
     return 0;
-  return (int64_t)per_cu * cus;
+  const int64_t n = (int64_t)per_cu * cus;
+  if (n > 0) {
+    std::lock_guard<std::mutex> g(g_resident_mu);
+    g_resident[key] = n;
+  }
+  return n;
 }
 
 // Padded block count of the two-pass tree: 32 blocks of 64 segments cover

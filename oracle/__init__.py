@@ -395,17 +395,24 @@ def bf16_to_f64(b: np.ndarray) -> np.ndarray:
 
 
 def magnitude_bias(got: np.ndarray, exp: np.ndarray) -> float:
-    """Mean relative magnitude error over the elements where exp is nonzero.
+    """Signed relative error of magnitudes, averaged per element.
 
-    Follows the page's magnitude_bias: (|got| - |exp|) / max(|exp|, 1e-30),
-    averaged over exp != 0; negative means the values shrank toward zero.
-    Both arguments are real-valued arrays (widen bf16 first).
+    The aiter issue ("Steps to Reproduce") measures the bias of a rounding
+    mode as a mean signed magnitude error relative to the exact values.
+    Written from that definition: over the elements whose exact value e is
+    not zero (a relative error is undefined at zero), the arithmetic mean of
+    (|g| - |e|) / |e|.  Negative means the results shrank toward zero.
+    Both arguments are real-valued arrays of one size (widen bf16 first);
+    at least one exact value must be nonzero.
     """
-    g = np.asarray(got, dtype=np.float64).ravel()
-    e = np.asarray(exp, dtype=np.float64).ravel()
-    nz = e != 0
-    rel = (np.abs(g[nz]) - np.abs(e[nz])) / np.maximum(np.abs(e[nz]), 1e-30)
-    return float(rel.mean())
+    g = np.abs(np.asarray(got, dtype=np.float64).ravel())
+    e = np.abs(np.asarray(exp, dtype=np.float64).ravel())
+    if g.shape != e.shape:
+        raise ValueError("got and exp differ in size")
+    keep = e > 0
+    if not keep.any():
+        raise ValueError("no nonzero exact value: the relative error is undefined")
+    return float(np.sum((g[keep] - e[keep]) / e[keep]) / np.count_nonzero(keep))
 
 
 def ratio_bias(got: np.ndarray, exp: np.ndarray) -> float:

@@ -15,6 +15,7 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle
 import synth
@@ -276,12 +277,25 @@ def pin_special_values(orc):
 # ------------------------------------------------------------------ metric
 
 def pin_magnitude_bias_metric(_orc=None):
-    """magnitude_bias on a hand example: ((1-2)/2 + (3-4)/4 + 0) / 3 = -0.25,
-    with the exp == 0 element left out."""
+    """magnitude_bias on hand examples.
+
+    ((1-2)/2 + (3-4)/4 + 0) / 3 = -0.25, with the exp == 0 element left out.
+    Signs do not matter, only magnitudes: got -3 against exp 2 is +1/2.
+    A uniform shrink by 2^-8 gives exactly -2^-8; growth gives a positive
+    value; a single element is its own relative error.
+    """
     got = np.array([1.0, -3.0, 2.0, 5.0])
     exp = np.array([2.0, -4.0, 2.0, 0.0])
     assert oracle.magnitude_bias(got, exp) == -0.25
     assert oracle.ratio_bias(got, exp) == (1 + 3 + 2 + 5 - 2 - 4 - 2) / 8.0
+    assert oracle.magnitude_bias(np.array([-3.0]), np.array([2.0])) == 0.5
+    e = np.array([1.0, -2.0, 4.0, 0.5, -0.25])
+    assert oracle.magnitude_bias(e * (1 - 2.0 ** -8), e) == -(2.0 ** -8)
+    assert oracle.magnitude_bias(np.array([3.0, 5.0]), np.array([2.0, 4.0])) == (0.5 + 0.25) / 2
+    # the mean is over the nonzero exact values only: zeros neither count nor divide
+    assert oracle.magnitude_bias(np.array([9.0, 1.5, 7.0]), np.array([0.0, 1.0, 0.0])) == 0.5
+    with pytest.raises(ValueError):
+        oracle.magnitude_bias(np.array([1.0]), np.array([0.0]))
 
 
 # ------------------------------------------------------------------ page experiments

@@ -128,17 +128,38 @@ def test_power_of_two_scaling_bitwise(k):
 
 
 def test_zero_rows_writes_nothing():
+    """n_rows = 0 through the C ABI, with the outputs pointing into poisoned
+    buffers of real rows: every path returns OK and leaves them untouched."""
+    import ctypes
+
     import torch
 
     import bf16_rounding_numerics_amd as arn
 
     announce("zero rows")
-    x = to_dev(np.zeros((0, 1024), np.uint16))
-    w = to_dev(np.ones(1024, np.uint16))
-    canary = poisoned_like(to_dev(np.zeros((4, 1024), np.uint16)))
-    arn.add_rmsnorm_fwd(x, x.clone(), x.clone(), x.clone(), w)
+    h = 1024
+    x, r, w = synth.workload(5, 4, h)
+    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    out, res = poisoned_like(xd), poisoned_like(xd)
+    L = arn.lib()
     torch.cuda.synchronize()
-    assert (from_dev(canary) == 0x7FC1).all()
+    for path in (arn.PATH_AUTO, arn.PATH_WAVE_ROW, arn.PATH_WG_ROW, arn.PATH_LDS_TWO_PASS,
+                 arn.PATH_GENERAL, arn.PATH_PACKED):
+        cfg = arn.LaunchCfg(path, 0, 0, 0)
+        assert L.add_rmsnorm_fwd_cfg(out.data_ptr(), res.data_ptr(), xd.data_ptr(),
+                                     rd.data_ptr(), wd.data_ptr(), 0, h, 1e-6,
+                                     ctypes.byref(cfg), None) == arn.OK
+    assert L.add_rmsnorm_fwd(out.data_ptr(), res.data_ptr(), xd.data_ptr(), rd.data_ptr(),
+                             wd.data_ptr(), 0, h, 1e-6, None) == arn.OK
+    assert L.rmsnorm_fwd(out.data_ptr(), xd.data_ptr(), wd.data_ptr(), 0, h, 1e-6,
+                         None) == arn.OK
+    torch.cuda.synchronize()
+    assert (from_dev(out) == POISON).all()
+    assert (from_dev(res) == POISON).all()
+    # the same buffers are then written by a call with rows (the check can fail)
+    arn.add_rmsnorm_fwd(out, res, xd, rd, wd, 1e-6)
+    torch.cuda.synchronize()
+    assert not (from_dev(out) == POISON).any()
 
 
 def test_side_stream_and_leading_dims():
