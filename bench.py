@@ -18,7 +18,7 @@ oracle timed on the host as a baseline.
 
   python bench.py [--steps K] [--warmup W] [--workload 4096x8192]
                   [--op bf16|quant|quant_fp8|plain|plain_quant|plain_quant_fp8|general|log1p]
-                  [--no-cpu-baseline] [--calibrate-copy]
+                  [--no-cpu-baseline] [--calibrate-copy] [--ceilings] [--size-sweep]
 """
 from __future__ import annotations
 
@@ -91,6 +91,12 @@ def parse_args(argv=None):
                    help="time budget of the CPU oracle baseline")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain device copy of known size (counter calibration)")
+    p.add_argument("--graph", action="store_true",
+                   help="launch the timed steps as one HIP graph (replayed once) instead of "
+                        "one call each from Python")
+    p.add_argument("--size-sweep", action="store_true",
+                   help="time the fused call and same-bytes streams at 1024..8192 rows of the "
+                        "workload's hidden and fit steady rate and fixed cost per launch")
     p.add_argument("--ceilings", action="store_true",
                    help="measure the device's read-only, write-only and 50/50 copy streaming "
                         "rates at the workload's bytes, beside the fused kernel")
@@ -553,6 +559,86 @@ def ceilings(args, torch, arn, synth):
     return 0
 
 
+def size_sweep(args, torch, arn):
+    """The fused call and same-bytes streams at several row counts, hidden
+    fixed: per-launch time against bytes moved.  A least-squares line
+    t = fixed + bytes / rate gives each one's steady streaming rate (the
+    slope) and its fixed cost per launch (start-up and drain, the intercept).
+    Rows 1024 .. 8192 of the workload's hidden; inputs N(0,1) (weight
+    1 + 0.1 N(0,1)) drawn on the device from a seeded generator, the same
+    distributions as the benchmark; buffer sets rotated past the last-level
+    cache; each case timed in 3 interleaved rounds, the median kept."""
+    hidden = int(args.workload.split("x")[1])
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    rows_list = (1024, 2048, 4096, 8192)
+    kinds = ("add_rmsnorm_fwd", "copy_2in_2out", "read_only", "write_only")
+    # The fused call at the launch its default takes for 4096 rows at this
+    # hidden, at every size (smaller calls would otherwise take another).
+    if hidden <= 2048:
+        pinned = dict(path=arn.PATH_WAVE_ROW, block_threads=256)
+    elif hidden <= 8192:
+        pinned = dict(path=arn.PATH_WG_ROW, block_threads=512)
+    else:
+        pinned = dict(path=arn.PATH_LDS_TWO_PASS, block_threads=1024)
+    w = (1.0 + 0.1 * torch.randn(hidden, generator=gen, device=dev)).to(torch.bfloat16)
+    w = w.view(torch.int16)
+    cases = {}
+    for n in rows_list:
+        count = n * hidden
+        sets = max(1, -(-CACHE_DEFEAT_BYTES // (8 * count)))
+        bufs = []
+        for _ in range(sets):
+            xd = torch.randn(n, hidden, generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+            rd = torch.randn(n, hidden, generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+            bufs.append((torch.empty_like(xd), torch.empty_like(xd), xd, rd))
+        big = [torch.empty(4 * count, dtype=torch.int16, device=dev) for _ in range(sets)]
+        sink = torch.empty_like(big[0])
+
+        def fused(i, bufs=bufs, sets=sets):
+            o, ro, xd, rd = bufs[i % sets]
+            arn.add_rmsnorm_fwd_cfg(o, ro, xd, rd, w, 1e-6, **pinned)
+
+        def copy(i, bufs=bufs, sets=sets):
+            o, ro, xd, rd = bufs[i % sets]
+            arn.add_rmsnorm_test_copy2(ro, o, xd, rd)
+
+        def read(i, big=big, sets=sets, sink=sink):
+            arn.add_rmsnorm_test_stream(sink, big[i % sets], 0)
+
+        def write(i, big=big, sets=sets):
+            b = big[i % sets]
+            arn.add_rmsnorm_test_stream(b, b, 1)
+
+        cases[n] = (8 * count, dict(zip(kinds, (fused, copy, read, write))), bufs, big, sink)
+    times = {(n, k): [] for n in rows_list for k in kinds}
+    steps = min(args.steps, 400)
+    for _ in range(3):
+        for n in rows_list:
+            for k in kinds:
+                ms, _ = time_steps(torch, cases[n][1][k], steps, 10, stream)
+                times[(n, k)].append(ms * 1e3)
+    out = {"workload": "rows 1024..8192 x hidden %d" % hidden, "steps_per_case": steps,
+           "fused_launch": {k: v for k, v in pinned.items()}, "us_per_launch": {}, "fit": {}}
+    for k in kinds:
+        xs, ys = [], []
+        for n in rows_list:
+            t = sorted(times[(n, k)])[1]
+            out["us_per_launch"].setdefault(k, {})[str(n)] = round(t, 3)
+            xs.append(cases[n][0])
+            ys.append(t)
+        mx, my = sum(xs) / len(xs), sum(ys) / len(ys)
+        slope = sum((a - mx) * (b - my) for a, b in zip(xs, ys)) / sum((a - mx) ** 2 for a in xs)
+        fixed = my - slope * mx
+        rate = 1e-3 / slope  # bytes per us -> GB/s
+        out["fit"][k] = {"steady_GBps": round(rate, 1), "steady_frac_of_peak": round(rate / PEAK_HBM_GBPS, 4),
+                         "fixed_us_per_launch": round(fixed, 3)}
+    print(json.dumps(out))
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -579,6 +665,8 @@ def main(argv=None):
         return 0
     if args.ceilings:
         return ceilings(args, torch, arn, synth)
+    if args.size_sweep:
+        return size_sweep(args, torch, arn)
     if args.op == "log1p":
         return bench_log1p(args, torch, arn, hip_build, synth)
     if args.op == "qk":
@@ -640,14 +728,44 @@ def main(argv=None):
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    graph = None
+    if args.graph:
+        # All timed steps captured in one HIP graph and replayed once: the
+        # same launches back to back with no host work between them, so a
+        # profiler's cost per launch leaves no idle gaps between kernels.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
+    if graph is not None:
+        # the replayed results must be those of an eager call on the same set
+        last = (args.steps - 1) % sets
+        replayed = [t.clone() for t in bufs[last][:2]] + ([t.clone() for t in qbufs[last]]
+                                                         if qbufs else [])
+        step(last)
+        torch.cuda.synchronize()
+        eager = list(bufs[last][:2]) + (list(qbufs[last]) if qbufs else [])
+        for k in range(len(eager)):
+            if args.op in QUANT_OPS and k == 0:
+                continue  # the bf16 out buffer is unused by the quantised ops
+            if args.op in PLAIN_OPS and k == 1:
+                continue  # no residual_out in plain RMSNorm
+            if not torch.equal(replayed[k], eager[k]):
+                raise RuntimeError("graph replay differs from an eager call")
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     nbytes = algorithmic_bytes(n_rows, hidden, args.op)
@@ -704,6 +822,7 @@ def main(argv=None):
                                "x,residual~N(0,1), weight~1+0.1N(0,1)"
                                % (ENTRY[args.op], n_rows, hidden),
                    "n_rows": n_rows, "hidden": hidden, "kernel": path,
+                   "launch": "one HIP graph of all steps" if args.graph else "one call per step",
                    "buffer_sets": sets, "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                    "wall_s_timed_region": round(wall_s, 4)},
         "roofline": roofline,
