@@ -547,15 +547,36 @@ def ceilings(args, torch, arn, synth):
         o, ro, xd, rd = bufs[i % sets]
         arn.add_rmsnorm_fwd(o, ro, xd, rd, wd, 1e-6)
 
-    res = {"read_only": rate(read), "write_only": rate(write), "copy_2in_2out": rate(copy),
-           "add_rmsnorm_fwd": rate(fused)}
+    def copy_rows(burst):
+        def f(i):
+            o, ro, xd, rd = bufs[i % sets]
+            arn.add_rmsnorm_test_copy_rows(ro, o, xd, rd, burst)
+        return f
+
+    def torch_copy(i):
+        o, ro, xd, rd = bufs[i % sets]
+        ro.copy_(xd)
+        o.copy_(rd)
+
+    res = {"read_only": rate(read), "write_only": rate(write), "copy_2in_2out": rate(copy)}
+    if hidden % 8 == 0 and hidden <= 16384:
+        for burst in (1, 2, 4):
+            res["copy_rows_burst%d" % burst] = rate(copy_rows(burst))
+    res["torch_device_copy"] = rate(torch_copy)
+    res["add_rmsnorm_fwd"] = rate(fused)
+    copies = {k: v for k, v in res.items() if k.startswith("copy") or k == "torch_device_copy"}
+    best_copy = max(copies, key=copies.get)
     print(json.dumps({"ceilings_GBps": res, "peak_GBps": PEAK_HBM_GBPS,
                       "frac_of_peak": {k: round(v / PEAK_HBM_GBPS, 4) for k, v in res.items()},
+                      "best_copy": best_copy,
+                      "fused_frac_of_best_copy": round(res["add_rmsnorm_fwd"] / copies[best_copy], 4),
                       "workload": args.workload, "bytes_per_step": moved, "buffer_sets": sets,
-                      "what": "8 * rows * hidden bytes per step, one launch each: read-only and "
-                              "write-only stream one buffer of four tensors' size, the copy reads "
-                              "two tensors and writes two, the fused call reads x and residual "
-                              "and writes out and residual_out"}))
+                      "what": "8 * rows * hidden bytes per step: read-only and write-only stream "
+                              "one buffer of four tensors' size; the copies read two tensors and "
+                              "write two: copy_2in_2out grid-stride, copy_rows_burstR one "
+                              "workgroup per R rows with all R rows loaded before any store, "
+                              "torch_device_copy two device-to-device tensor copies; the fused "
+                              "call reads x and residual and writes out and residual_out"}))
     return 0
 
 

@@ -16,7 +16,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libaddrmsnorm.so")
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 MAX_HIDDEN = 32768
 
 OK = 0
@@ -67,7 +67,7 @@ EXPORTS = ("add_rmsnorm_fwd", "add_rmsnorm_fwd_cfg", "add_rmsnorm_fwd_strided",
            "rmsnorm_quant_fp8_fwd_strided", "qk_rmsnorm_fwd", "qk_rmsnorm_fwd_cfg",
            "log1p_f32", "log1p_f32_cfg",
            "add_rmsnorm_test_cvt_range", "add_rmsnorm_test_cvt_e4m3_range",
-           "add_rmsnorm_test_copy2",
+           "add_rmsnorm_test_copy2", "add_rmsnorm_test_copy_rows",
            "add_rmsnorm_test_stream", "add_rmsnorm_strerror", "add_rmsnorm_last_hip_error",
            "add_rmsnorm_abi_version", "add_rmsnorm_build_info")
 
@@ -140,6 +140,8 @@ def lib() -> ctypes.CDLL:
     L.add_rmsnorm_test_cvt_range.argtypes = [vp, ctypes.c_uint32, i64, vp]
     L.add_rmsnorm_test_copy2.restype = i32
     L.add_rmsnorm_test_copy2.argtypes = [vp, vp, vp, vp, i64, vp]
+    L.add_rmsnorm_test_copy_rows.restype = i32
+    L.add_rmsnorm_test_copy_rows.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
     L.add_rmsnorm_test_stream.restype = i32
     L.add_rmsnorm_test_stream.argtypes = [vp, vp, i64, i32, vp]
     L.add_rmsnorm_strerror.restype = ctypes.c_char_p
@@ -704,6 +706,26 @@ def add_rmsnorm_test_copy2(dst0, dst1, src0, src1, stream=None) -> None:
     h = _stream_handle(dev, stream)
     _check(_on_device(dev, lambda: L.add_rmsnorm_test_copy2(
         dst0.data_ptr(), dst1.data_ptr(), src0.data_ptr(), src1.data_ptr(), n, h)))
+
+
+def add_rmsnorm_test_copy_rows(dst0, dst1, src0, src1, rows_per_burst: int = 1,
+                               stream=None) -> None:
+    """dst0 <- src0, dst1 <- src1 with the register kernel's row structure,
+    rows_per_burst rows loaded per workgroup before any store (a reference
+    rate).  Contiguous 16-bit GPU tensors of one shape [..., hidden]."""
+    ts = (dst0, dst1, src0, src1)
+    for t in ts:
+        if not t.is_cuda or t.element_size() != 2 or not t.is_contiguous() or \
+                t.shape != src0.shape or t.dim() < 1:
+            raise ValueError("copy_rows takes four contiguous 16-bit GPU tensors of one shape")
+    hidden = src0.shape[-1]
+    n_rows = src0.numel() // hidden if hidden else 0
+    dev = src0.get_device()
+    L = lib()
+    h = _stream_handle(dev, stream)
+    _check(_on_device(dev, lambda: L.add_rmsnorm_test_copy_rows(
+        dst0.data_ptr(), dst1.data_ptr(), src0.data_ptr(), src1.data_ptr(), n_rows, hidden,
+        rows_per_burst, h)))
 
 
 def add_rmsnorm_test_stream(dst, src, mode: int, stream=None) -> None:

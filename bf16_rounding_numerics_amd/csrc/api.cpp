@@ -667,6 +667,28 @@ int add_rmsnorm_test_copy2(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
   return ADD_RMSNORM_OK;
 }
 
+int add_rmsnorm_test_copy_rows(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
+                               const uint16_t* src1, int64_t n_rows, int64_t hidden,
+                               int rows_per_burst, struct ihipStream_t* stream) {
+  if (n_rows < 0 || hidden <= 0 || !(rows_per_burst == 1 || rows_per_burst == 2 ||
+                                     rows_per_burst == 4))
+    return ADD_RMSNORM_EINVAL;
+  if (hidden % 8 != 0) return ADD_RMSNORM_EALIGN;
+  if (hidden > 16384 || n_rows > ((int64_t)1 << 30)) return ADD_RMSNORM_ERANGE;
+  if (n_rows == 0) return ADD_RMSNORM_OK;
+  if (!dst0 || !dst1 || !src0 || !src1) return ADD_RMSNORM_EINVAL;
+  if (!aligned16(dst0) || !aligned16(dst1) || !aligned16(src0) || !aligned16(src1))
+    return ADD_RMSNORM_EALIGN;
+  const uint64_t n = (uint64_t)n_rows * (uint64_t)hidden * 2;
+  if (overlap(dst0, n, dst1, n) || overlap(dst0, n, src0, n) || overlap(dst0, n, src1, n) ||
+      overlap(dst1, n, src0, n) || overlap(dst1, n, src1, n))
+    return ADD_RMSNORM_EALIAS;
+  hipError_t e = addrms::launch_copy_rows(dst0, dst1, src0, src1, n_rows, (int)hidden,
+                                          rows_per_burst, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_failure(e);
+  return ADD_RMSNORM_OK;
+}
+
 int add_rmsnorm_test_stream(uint16_t* dst, const uint16_t* src, int64_t count, int mode,
                             struct ihipStream_t* stream) {
   if (count < 0 || (mode != 0 && mode != 1)) return ADD_RMSNORM_EINVAL;

@@ -1186,6 +1186,42 @@ __global__ __launch_bounds__(256) void k_copy2(u32x4* d0, u32x4* d1, const u32x4
   }
 }
 
+// The same copy with the fused kernels' row structure, and reads grouped:
+// each workgroup of 512 threads takes R consecutive rows of hidden = 8 * segs
+// elements (thread t holds segments t + 512 j, J of them), issues every load
+// of its R rows, then every store.  With R = 1 it moves data exactly as one
+// fused call's register kernel does; R = 2, 4 put longer same-direction
+// bursts on each compute unit.  One workgroup per R rows.
+template <int R, int J>
+__global__ __launch_bounds__(512) void k_copy_rows(u32x4* d0, u32x4* d1, const u32x4* s0,
+                                                 const u32x4* s1, int64_t n_rows, int segs) {
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  u32x4 a[R][J], b[R][J];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const bool v = r0 + k < n_rows;
+    const __amdgpu_buffer_rsrc_t ra = row_rsrc(s0, r0 + k, segs, segs, v);
+    const __amdgpu_buffer_rsrc_t rb = row_rsrc(s1, r0 + k, segs, segs, v);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      a[k][j] = load_seg(ra, t + 512 * j);
+      b[k][j] = load_seg(rb, t + 512 * j);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const bool v = r0 + k < n_rows;
+    const __amdgpu_buffer_rsrc_t wa = row_rsrc(d0, r0 + k, segs, segs, v);
+    const __amdgpu_buffer_rsrc_t wb = row_rsrc(d1, r0 + k, segs, segs, v);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      store_seg(wa, t + 512 * j, a[k][j]);
+      store_seg(wb, t + 512 * j, b[k][j]);
+    }
+  }
+}
+
 // One-directional streams with the same access pattern: read-only (the
 // loaded words are folded together and written out only if they match a
 // pattern no test data holds, so the loads stay live and almost nothing is
@@ -1731,6 +1767,38 @@ hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const ui
                      reinterpret_cast<u32x4*>(d1), reinterpret_cast<const u32x4*>(s0),
                      reinterpret_cast<const u32x4*>(s1), segs);
   return hipGetLastError();
+}
+
+template <int R>
+hipError_t go_copy_rows(u32x4* d0, u32x4* d1, const u32x4* s0, const u32x4* s1, int64_t n_rows,
+                        int segs, hipStream_t s) {
+  const int64_t g = (n_rows + R - 1) / R;
+  const unsigned grid = (unsigned)(g < ((int64_t)1 << 30) ? g : ((int64_t)1 << 30));
+  const int j = (segs + 511) / 512;
+  if (g > ((int64_t)1 << 30)) return hipErrorInvalidValue;
+  switch (j) {
+    case 1: hipLaunchKernelGGL((k_copy_rows<R, 1>), dim3(grid), dim3(512), 0, s, d0, d1, s0, s1, n_rows, segs); break;
+    case 2: hipLaunchKernelGGL((k_copy_rows<R, 2>), dim3(grid), dim3(512), 0, s, d0, d1, s0, s1, n_rows, segs); break;
+    case 3:
+    case 4: hipLaunchKernelGGL((k_copy_rows<R, 4>), dim3(grid), dim3(512), 0, s, d0, d1, s0, s1, n_rows, segs); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,
+                            int64_t n_rows, int hidden, int rows_per_burst, hipStream_t s) {
+  u32x4* a = reinterpret_cast<u32x4*>(d0);
+  u32x4* b = reinterpret_cast<u32x4*>(d1);
+  const u32x4* c = reinterpret_cast<const u32x4*>(s0);
+  const u32x4* d = reinterpret_cast<const u32x4*>(s1);
+  const int segs = hidden / 8;
+  switch (rows_per_burst) {
+    case 1: return go_copy_rows<1>(a, b, c, d, n_rows, segs, s);
+    case 2: return go_copy_rows<2>(a, b, c, d, n_rows, segs, s);
+    case 4: return go_copy_rows<4>(a, b, c, d, n_rows, segs, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_cvt_e4m3_range(uint8_t* out, uint32_t start, int64_t count, hipStream_t s) {

@@ -111,6 +111,13 @@ hipError_t launch_stream(uint16_t* dst, const uint16_t* src, int64_t count, int 
 hipError_t launch_copy2(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,
                         int64_t count, hipStream_t stream);
 
+// Reference copy with row structure: d0 <- s0 and d1 <- s1, n_rows rows of
+// hidden elements (hidden a multiple of 8, at most 16384), one workgroup of
+// 512 threads per rows_per_burst (1, 2 or 4) rows, all loads of its rows
+// issued before any store.
+hipError_t launch_copy_rows(uint16_t* d0, uint16_t* d1, const uint16_t* s0, const uint16_t* s1,
+                            int64_t n_rows, int hidden, int rows_per_burst, hipStream_t stream);
+
 // Test hook: the store epilogue applied to consecutive fp32 bit patterns.
 hipError_t launch_cvt_range(uint16_t* out, uint32_t start, int64_t count, hipStream_t stream);
 

@@ -54,7 +54,7 @@ struct ihipStream_t;
  * local to that prototype). */
 struct add_rmsnorm_launch_cfg;
 
-#define ADD_RMSNORM_ABI_VERSION 9
+#define ADD_RMSNORM_ABI_VERSION 10
 
 /* Largest supported hidden size. */
 #define ADD_RMSNORM_MAX_HIDDEN 32768
@@ -404,6 +404,21 @@ int add_rmsnorm_test_cvt_e4m3_range(uint8_t* out, uint32_t start, int64_t count,
  */
 int add_rmsnorm_test_copy2(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
                            const uint16_t* src1, int64_t count, struct ihipStream_t* stream);
+
+/*
+ * Measurement hook: the copy of add_rmsnorm_test_copy2 with the fused
+ * kernels' row structure: dst0 <- src0 and dst1 <- src1, n_rows contiguous
+ * rows of hidden 16-bit elements each.  One workgroup of 512 threads takes
+ * rows_per_burst (1, 2 or 4) consecutive rows and issues every load of them
+ * before any store, so each compute unit's traffic comes in same-direction
+ * bursts (with 1, exactly the register kernel's access pattern).  hidden a
+ * multiple of 8 (ADD_RMSNORM_EALIGN) and at most 16384, n_rows at most 2^30
+ * (ADD_RMSNORM_ERANGE); device pointers, 16-byte aligned; no buffer may
+ * overlap another (ADD_RMSNORM_EALIAS).  Enqueued on stream.
+ */
+int add_rmsnorm_test_copy_rows(uint16_t* dst0, uint16_t* dst1, const uint16_t* src0,
+                               const uint16_t* src1, int64_t n_rows, int64_t hidden,
+                               int rows_per_burst, struct ihipStream_t* stream);
 
 /*
  * Measurement hook: one-directional streams with the same access pattern as

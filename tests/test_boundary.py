@@ -346,6 +346,24 @@ def test_copy2_errors():
 
 
 @fake_addresses
+def test_copy_rows_errors():
+    L = arn.lib()
+    c = L.add_rmsnorm_test_copy_rows
+    args = (A, A + MB, A + 2 * MB, A + 3 * MB)
+    assert c(*args, -1, 1024, 1, None) == arn.EINVAL        # negative rows
+    assert c(*args, 4, 0, 1, None) == arn.EINVAL            # hidden <= 0
+    assert c(*args, 4, 1024, 3, None) == arn.EINVAL         # rows per burst 1, 2 or 4
+    assert c(*args, 4, 1020, 1, None) == arn.EALIGN         # hidden % 8 != 0
+    assert c(*args, 4, 16392, 1, None) == arn.ERANGE        # hidden above 16384
+    assert c(*args, (1 << 30) + 1, 8, 1, None) == arn.ERANGE
+    assert c(A + 2, A + MB, A + 2 * MB, A + 3 * MB, 4, 1024, 1, None) == arn.EALIGN
+    assert c(0, A + MB, A + 2 * MB, A + 3 * MB, 4, 1024, 1, None) == arn.EINVAL
+    assert c(A, A + 4096, A + 2 * MB, A + 3 * MB, 4, 1024, 1, None) == arn.EALIAS
+    assert c(A, A + MB, A + 2 * MB, A + 16, 4, 1024, 2, None) == arn.EALIAS
+    assert c(0, 0, 0, 0, 0, 1024, 4, None) == arn.OK        # no rows: nothing checked further
+
+
+@fake_addresses
 def test_stream_hook_errors():
     L = arn.lib()
     assert L.add_rmsnorm_test_stream(A, A + MB, -8, 0, None) == arn.EINVAL

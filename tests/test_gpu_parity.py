@@ -212,6 +212,23 @@ def test_copy_reference_copies_bit_exactly():
     assert np.array_equal(from_dev(d0), x) and np.array_equal(from_dev(d1), r)
 
 
+@pytest.mark.parametrize("burst", [1, 2, 4])
+@pytest.mark.parametrize("n,h", [(333, 1024), (37, 12288), (5, 16384), (1, 8)])
+def test_row_copy_reference_copies_bit_exactly(burst, n, h):
+    """The row-structured measurement copy moves every byte of every row,
+    for row counts that leave a partial burst and hidden that leaves a
+    partial set of 512-thread segments."""
+    import torch
+
+    announce("copy_rows reference %dx%d burst %d" % (n, h, burst))
+    x, r, _ = synth.workload(92, n, h)
+    xd, rd = to_dev(x), to_dev(r)
+    d0, d1 = poisoned_like(xd), poisoned_like(xd)
+    arn.add_rmsnorm_test_copy_rows(d0, d1, xd, rd, burst)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(d0), x) and np.array_equal(from_dev(d1), r)
+
+
 def test_stream_hooks():
     """The read-only and write-only measurement streams: writing fills every
     element with bf16 1.0; reading leaves the sink untouched (its fold of
