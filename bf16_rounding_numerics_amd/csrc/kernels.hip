@@ -821,13 +821,13 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
   __syncthreads();
   uint16_t* sl = reinterpret_cast<uint16_t*>(slot[wave]);
 
-  int parity = 0;
-  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x, parity ^= 1) {
+  // Each workgroup walks rows blockIdx.x, + gridDim.x, ...; the next row's
+  // loads are issued before the current row's barrier and out stores
+  // (measured on MI355X at 4096 x 8191: see the comment on the launch).
+  uint16_t xv[J][8], rv[J][8];
+  auto load_row = [&](int64_t row) {
     const uint16_t* xr = p.x + row * p.x_stride;
     const uint16_t* rr = R ? p.residual + row * p.r_stride : nullptr;
-    uint16_t* ror = R ? p.residual_out + row * p.ro_stride : nullptr;
-    uint16_t* orow = p.out + row * p.out_stride;
-    uint16_t xv[J][8], rv[J][8];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
 #pragma unroll
@@ -837,6 +837,12 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
         if constexpr (R) rv[j][k] = e < H ? rr[e] : (uint16_t)0;
       }
     }
+  };
+  if ((int64_t)blockIdx.x < p.n_rows) load_row(blockIdx.x);
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x, parity ^= 1) {
+    uint16_t* ror = R ? p.residual_out + row * p.ro_stride : nullptr;
+    uint16_t* orow = p.out + row * p.out_stride;
     float acc[J][8];
     float bs[J];
 #pragma unroll
@@ -866,6 +872,7 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
       }
       wave_fence();
     }
+    if (row + gridDim.x < p.n_rows) load_row(row + gridDim.x);
 #pragma unroll
     for (int j = 0; j < J; ++j) bs[j] = wave_block_sum(bs[j]);
     if (lane == 0) {
