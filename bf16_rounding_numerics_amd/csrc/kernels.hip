@@ -805,6 +805,26 @@ __global__ __launch_bounds__(B) void k_general(GenParams p) {
 // LDS once per workgroup, in segment order, zero padded.
 DEV void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
+// Stores a wavefront's block of 512 elements (first element b0 of the row)
+// from its regrouping slot, one 16-bit element per lane and instruction,
+// consecutive lanes at consecutive elements.  The slot is read whole before
+// any store, so the eight LDS reads overlap (a read guarded by its store's
+// own mask would wait for each in turn); only a block that ends past the
+// row's end masks its stores.
+DEV void store_block(uint16_t* dst, int b0, int h, const uint16_t* sl, int lane) {
+  uint16_t v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = sl[64 * k + lane];
+  if (b0 + 512 <= h) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[b0 + 64 * k + lane] = v[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (b0 + 64 * k + lane < h) dst[b0 + 64 * k + lane] = v[k];
+  }
+}
+
 template <int B, int J, bool R>
 __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
   constexpr int W = B / 64;
@@ -864,11 +884,7 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
         wave_fence();
         slot[wave][lane] = pack8_rne(acc[j]);
         wave_fence();
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int e = 512 * (wave + W * j) + 64 * k + lane;
-          if (e < H) ror[e] = sl[64 * k + lane];
-        }
+        store_block(ror, 512 * (wave + W * j), H, sl, lane);
       }
       wave_fence();
     }
@@ -887,11 +903,7 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
       const u32x4 wq = wseg[64 * (wave + W * j) + lane];
       slot[wave][lane] = normalise8(acc[j], rinv, wq);
       wave_fence();
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = 512 * (wave + W * j) + 64 * k + lane;
-        if (e < H) orow[e] = sl[64 * k + lane];
-      }
+      store_block(orow, 512 * (wave + W * j), H, sl, lane);
       wave_fence();
     }
   }
@@ -952,11 +964,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_general_wave(GenParams p) {
         wave_fence();
         slot[wave][lane] = pack8_rne(acc[j]);
         wave_fence();
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int e = 512 * j + 64 * k + lane;
-          if (e < H) ror[e] = sl[64 * k + lane];
-        }
+        store_block(ror, 512 * j, H, sl, lane);
       }
       wave_fence();
     }
@@ -968,11 +976,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_general_wave(GenParams p) {
     for (int j = 0; j < J; ++j) {
       slot[wave][lane] = normalise8(acc[j], rinv, wseg[64 * j + lane]);
       wave_fence();
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = 512 * j + 64 * k + lane;
-        if (e < H) orow[e] = sl[64 * k + lane];
-      }
+      store_block(orow, 512 * j, H, sl, lane);
       wave_fence();
     }
   }
