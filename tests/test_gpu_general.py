@@ -51,7 +51,8 @@ def gpu_plain(x, w, eps=1e-6, path=0, block=0, grid=0):
     return from_dev(out)
 
 
-HIDDEN = [1, 3, 7, 9, 15, 100, 1001, 2049, 4095, 4097, 8191, 12289, 16385, 24577, 32767]
+HIDDEN = [1, 3, 7, 9, 15, 100, 513, 575, 577, 1001, 1601, 2049, 4095, 4097, 8191, 12289, 16385,
+          24577, 32767]
 
 
 @pytest.mark.parametrize("h", HIDDEN)
