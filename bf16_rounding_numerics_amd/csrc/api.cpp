@@ -94,6 +94,12 @@ int small_call_threads(int64_t n_rows, int64_t segs) {
 constexpr int64_t kVariantWaveRowMaxHidden = 1024;
 constexpr int64_t kVariantWgRowMaxHidden = 16384;
 constexpr int kVariantWgRowSmallThreads = 128;
+// Plain quantised out: two segments per thread (rather than four) up to this
+// many elements per call, for hidden up to 8192.
+constexpr int64_t kPlainQuantTwoSegMaxElems = (int64_t)1 << 25;
+// Plain bf16 small calls: hidden 4096-8192 and at most 2^23 elements per call.
+constexpr int64_t kPlainSmallMinHidden = 4096;
+constexpr int64_t kPlainSmallMaxElems = (int64_t)1 << 23;
 
 // The device's LDS limit per workgroup, asked of the runtime once per device
 // (a device attribute never changes; the query costs host time per call).
@@ -253,15 +259,31 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
       hidden <= (a.qout ? kPackAutoMaxHiddenQuant : kPackAutoMaxHidden) &&
       a.n_rows < addrms::kPackMaxRows)
     path = ADD_RMSNORM_PATH_PACKED;
+  // Plain bf16 small calls take one workgroup per row (see below).
+  bool plain_small = false;
   if (path == ADD_RMSNORM_PATH_AUTO && variant) {
     if (hidden <= kVariantWaveRowMaxHidden) {
       path = ADD_RMSNORM_PATH_WAVE_ROW;
     } else if (hidden <= kVariantWgRowMaxHidden) {
       path = ADD_RMSNORM_PATH_WG_ROW;
       if (block == 0 && a.qout != nullptr && a.residual == nullptr) {
-        // plain int8: four segments per thread measured best (5-10%)
+        // Plain quantised out: two segments per thread up to hidden 8192 and
+        // 2^25 elements, four beyond (measured on MI355X against four
+        // everywhere: 1-13% faster in that range, even at its edge, 3% slower
+        // at 16384 x 4096 and 35-40% at hidden 16384).
+        const int per = hidden <= kWgRowMaxHidden && a.n_rows * hidden <= kPlainQuantTwoSegMaxElems
+                            ? 2 : 4;
         block = 64;
-        while (block < 512 && block * 4 * 8 < hidden) block *= 2;
+        while (block < 1024 && block * per * 8 < hidden) block *= 2;
+      } else if (block == 0 && a.qout == nullptr && a.residual == nullptr &&
+                 hidden >= kPlainSmallMinHidden && hidden <= kWgRowMaxHidden &&
+                 a.n_rows * hidden <= kPlainSmallMaxElems) {
+        // Plain bf16 small calls: the fused op's small-call workgroup, one
+        // workgroup per row (measured on MI355X against the resident grid of
+        // 512 threads: 1-14% faster from 512 x 4096 to 1024 x 8192; 9-13%
+        // slower at 3072 x 8192 and 4096 x 4096, beyond the range).
+        block = small_call_threads(a.n_rows, hidden / 8);
+        plain_small = true;
       } else if (block == 0 && hidden <= kWaveRowMaxHidden) {
         block = kVariantWgRowSmallThreads;
       }
@@ -301,7 +323,8 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
   // weight once, which for these rows is as many bytes as x itself (measured
   // 7-16% faster on MI355X; the fused kernels gain nothing from it).
   int64_t grid = c.grid_blocks;
-  if (grid == 0 && a.residual == nullptr && path != ADD_RMSNORM_PATH_GENERAL) grid = -1;
+  if (grid == 0 && a.residual == nullptr && path != ADD_RMSNORM_PATH_GENERAL && !plain_small)
+    grid = -1;
   if (path == ADD_RMSNORM_PATH_GENERAL) {
     // Rows up to 1024 take one wavefront each, four rows per workgroup.
     // Longer rows take one workgroup each, by default with one segment per

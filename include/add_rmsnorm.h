@@ -139,9 +139,11 @@ int add_rmsnorm_fwd_strided(uint16_t* out, int64_t out_stride, uint16_t* residua
  *                  runs block_threads / 64 rows per workgroup, the packed
  *                  path block_threads / 64 wavefronts of several rows each).
  *   grid_blocks    0: the library's choice: one workgroup per row (per row
- *                  group on the wave path) for the fused fast kernels, as
- *                  many as fit on the device for plain RMSNorm, the packed
- *                  path and the general kernels; > 0: exactly that many
+ *                  group on the wave path) for the fused fast kernels and for
+ *                  small plain bf16 calls (hidden 4096-8192, at most 2^23
+ *                  elements), as many as fit on the device for other plain
+ *                  RMSNorm calls, the packed path and the general kernels;
+ *                  > 0: exactly that many
  *                  workgroups, each looping over rows (a persistent grid);
  *                  -1: as many as fit on the device at once.
  *   flags          0, or on ADD_RMSNORM_PATH_PACKED the row groups each
