@@ -122,6 +122,29 @@ def pin_zero_rows(orc):
         assert np.array_equal(out[0], expect)
 
 
+def pin_zero_row_eps_zero(orc):
+    """eps = 0 and a zero row: the mean of squares is 0, rinv = 1/sqrt(0) = +Inf
+    and every (acc * rinv) * w is 0 * Inf, a NaN (IEEE, as in the page's fp32
+    reference); residual_out is the zero itself.  A nonzero row beside it is
+    unaffected: rows are independent."""
+    rng = np.random.default_rng(15)
+    h = 192
+    w = random_bf16_weights(rng, h)
+    x = np.zeros((2, h), dtype=np.uint16)
+    r = np.zeros((2, h), dtype=np.uint16)
+    x[1, 7] = 0x3F80  # 1.0 at k = 7: out_7 = sqrt(h) w_7 / 1, the rest +-0
+    out, ro = orc.add_rmsnorm(x, r, w, 0.0)
+    assert is_nan16(out[0]).all()
+    assert (ro[0] == 0).all()
+    assert not is_nan16(out[1]).any()
+    wf = bits16_to_f32(w).astype(np.float64)
+    y7 = np.sqrt(float(h)) * wf[7]
+    got7 = float(bits16_to_f32(out[1:2, 7:8])[0, 0])
+    assert abs(got7 - y7) <= abs(y7) * 2.0 ** -8  # within one bf16 rounding
+    others = np.delete(out[1], 7)
+    assert ((others & 0x7FFF) == 0).all()
+
+
 def pin_power_of_two_scaling(orc):
     """eps = 0: scaling x and residual by 2^k leaves out unchanged, bit for bit,
     and scales residual_out exactly (correct rounding commutes with it)."""
@@ -374,5 +397,5 @@ def pin_page_chain_experiment(orc):
 
 
 FAST_PINS = [pin_constant_rows, pin_eps_inside_sqrt_after_mean, pin_one_hot_rows,
-             pin_zero_rows, pin_power_of_two_scaling, pin_exact_rationals_small_rows,
-             pin_special_values]
+             pin_zero_rows, pin_zero_row_eps_zero, pin_power_of_two_scaling,
+             pin_exact_rationals_small_rows, pin_special_values]

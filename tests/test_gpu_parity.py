@@ -110,6 +110,20 @@ def test_special_values(h):
     assert is_nan16(out[1]).all() and is_nan16(exp_out[1]).all()
 
 
+@pytest.mark.parametrize("h", [256, 1024, 4096, 8192, 16384])
+def test_zero_row_with_eps_zero_is_nan(h):
+    """eps = 0: a zero row's out is NaN throughout on both sides (0 * Inf), its
+    residual_out zero; the other rows are untouched by it."""
+    announce("zero row, eps 0, hidden %d" % h)
+    x, r, w = synth.workload(41, 6, h)
+    x[2] = 0
+    r[2] = 0
+    out, res = gpu_fwd(x, r, w, 0.0)
+    check_parity(x, r, w, 0.0, out, res, label="zero row eps 0 h=%d" % h)
+    assert is_nan16(out[2]).all() and (res[2] == 0).all()
+    assert not is_nan16(np.delete(out, 2, axis=0)).any()
+
+
 @pytest.mark.parametrize("k", [-40, -9, 5, 30])
 def test_power_of_two_scaling_bitwise(k):
     """With eps = 0, scaling x and residual by 2^k must leave out unchanged
