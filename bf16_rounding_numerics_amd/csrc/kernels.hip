@@ -805,11 +805,24 @@ __global__ __launch_bounds__(B) void k_general(GenParams p) {
 // with the same block sums and tree.  Loads and stores are 16-bit and
 // coalesced: wavefront w reads the 512 elements of its segment block
 // w + W j one element per lane (eight loads), then regroups them into one
-// segment per lane through its own 1 KiB of LDS, and sends residual_out and
-// out back out the same way.  A wavefront's LDS accesses execute in order,
-// so the regrouping needs no workgroup barrier; a wavefront-scope fence keeps
+// segment per lane through its own LDS slot, and sends residual_out and out
+// back out the same way.  A wavefront's LDS accesses execute in order, so
+// the regrouping needs no workgroup barrier; a wavefront-scope fence keeps
 // the compiler from moving them across one another.  The weight is staged in
 // LDS once per workgroup, in segment order, zero padded.
+//
+// Every row access goes through a buffer resource over the row, so the
+// hardware range check, not a branch, handles the row's end.  With no
+// branch around them the compiler counts how many accesses follow each
+// prefetched load and waits for that load alone; with a branch per access
+// it waited for every earlier access, the previous row's out stores
+// included (measured on MI355X: 54.1 -> 52.3 us at 4096 x 8191, 58.1 -> 56.1
+// us at 2048 x 16383, 67.1 -> 60.8 us at 4096 x 9001).
+//
+// A (line-aligned): each 16-bit access covers one whole 128-byte line
+// instead of straddling two lines of a misaligned row, nine accesses per
+// block instead of eight.  F: every block holds row elements; otherwise
+// blocks past the row's end are skipped.
 DEV void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
 // Stores a wavefront's block of 512 elements (first element b0 of the row)
@@ -832,12 +845,29 @@ DEV void store_block(uint16_t* dst, int b0, int h, const uint16_t* sl, int lane)
   }
 }
 
-template <int B, int J, bool R>
+// A row's element offset within its 128-byte L2 line (0..63).
+DEV int line_offset(const uint16_t* row) {
+  return (int)((reinterpret_cast<uintptr_t>(row) >> 1) & 63);
+}
+
+// Buffer resource over one row of hidden h, starting o elements before the
+// row (at its line in the line-aligned form below): the hardware range check
+// drops stores and zeroes loads past the row's end, so no access needs a
+// branch.  The last word selects 32-bit raw data (gfx9 layout).
+DEV __amdgpu_buffer_rsrc_t gen_row_rsrc(const uint16_t* row, int o, int h) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row - o), 0, 2 * (o + h),
+                                           0x00020000);
+}
+
+template <int B, int J, bool R, bool A, bool F>
 __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
   constexpr int W = B / 64;
   constexpr int NB = W * J;
+  constexpr int NW = A ? 9 : 8;     // 16-bit accesses per lane and block
+  constexpr int PAD = A ? 64 : 0;   // slot elements on either side of the block
+  constexpr int OOB = 1 << 30;      // a byte offset past every row resource
   __shared__ float blk[2][NB];  // alternates by row so one barrier per row suffices
-  __shared__ u32x4 slot[W][64];
+  __shared__ u32x4 slot[W][(512 + 2 * PAD) / 8];
   extern __shared__ u32x4 wseg[];  // B * J segments of weight
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -846,53 +876,104 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
   uint16_t* wl = reinterpret_cast<uint16_t*>(wseg);
   for (int i = t; i < 8 * B * J; i += B) wl[i] = i < H ? p.weight[i] : (uint16_t)0;
   __syncthreads();
-  uint16_t* sl = reinterpret_cast<uint16_t*>(slot[wave]);
+  uint16_t* sl = reinterpret_cast<uint16_t*>(slot[wave]) + PAD;  // sl[i]: element i of the block
+  u32x4* sq = slot[wave] + PAD / 8;                              // sq[l]: segment l of the block
 
+  // Access k of lane l in block b touches element 512 b + 64 k + l - o of
+  // the row (o = 0 unless line-aligned), at byte 2 (512 b + 64 k + l) of the
+  // row's resource; the first and last access drop the lanes outside the block.
+  auto voff = [&](int o, int b, int k) {
+    const int off = 2 * (512 * b + 64 * k + lane);
+    if constexpr (A) {
+      if (k == 0) return lane < o ? OOB : off;
+      if (k == NW - 1) return lane < o ? off : OOB;
+    }
+    return off;
+  };
+  uint16_t xv[J][NW], rv[J][NW];
+  auto load_block = [&](__amdgpu_buffer_rsrc_t rs, int o, int b, uint16_t (&v)[NW]) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff(o, b, k), 0, 0);
+  };
+  // Element i of the block to sl[i]; lanes outside the block write the padding.
+  auto to_slot = [&](const uint16_t (&v)[NW], int o) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) sl[64 * k + lane - o] = v[k];
+  };
+  // The block back out from the slot, all slot reads before any store.
+  auto store_block_rs = [&](__amdgpu_buffer_rsrc_t rs, int o, int b) {
+    uint16_t v[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) v[k] = sl[64 * k + lane - o];
+    if (F || 512 * b < H) {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) __builtin_amdgcn_raw_buffer_store_b16(v[k], rs, voff(o, b, k), 0, 0);
+    }
+  };
+  // F: every block holds row elements, and no access has a branch.
+  // Otherwise a block past the row's end is skipped whole, x and residual
+  // under one branch (a branch per access would leave the waits for the
+  // prefetched loads uncounted).  With J > 1 a skipped block's registers are
+  // not zeroed, its processing is skipped instead (with a zero fill the
+  // compiler packed the values in pairs, waiting for each load).
+  auto load_row = [&](int64_t row) {
+    const uint16_t* xr = p.x + row * p.x_stride;
+    const int ox = A ? line_offset(xr) : 0;
+    const auto xs = gen_row_rsrc(xr, ox, H);
+    const uint16_t* rr = R ? p.residual + row * p.r_stride : nullptr;
+    const int orr = A && R ? line_offset(rr) : 0;
+    const auto rs = gen_row_rsrc(R ? rr : xr, orr, R ? H : 0);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (F || 512 * (wave + W * j) < H) {
+        load_block(xs, ox, wave + W * j, xv[j]);
+        if constexpr (R) load_block(rs, orr, wave + W * j, rv[j]);
+      } else if constexpr (J == 1) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) xv[j][k] = rv[j][k] = 0;
+      }
+    }
+  };
   // Each workgroup walks rows blockIdx.x, + gridDim.x, ...; the next row's
   // loads are issued before the current row's barrier and out stores
   // (measured on MI355X: 56.3 -> 54.8 us at 4096 x 8191, 64.3 -> 59.2 us at
   // 2048 x 16383).
-  uint16_t xv[J][8], rv[J][8];
-  auto load_row = [&](int64_t row) {
-    const uint16_t* xr = p.x + row * p.x_stride;
-    const uint16_t* rr = R ? p.residual + row * p.r_stride : nullptr;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = 512 * (wave + W * j) + 64 * k + lane;
-        xv[j][k] = e < H ? xr[e] : (uint16_t)0;
-        if constexpr (R) rv[j][k] = e < H ? rr[e] : (uint16_t)0;
-      }
-    }
-  };
   if ((int64_t)blockIdx.x < p.n_rows) load_row(blockIdx.x);
   int parity = 0;
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x, parity ^= 1) {
-    uint16_t* ror = R ? p.residual_out + row * p.ro_stride : nullptr;
+    const int ox = A ? line_offset(p.x + row * p.x_stride) : 0;
+    const int orr = A && R ? line_offset(p.residual + row * p.r_stride) : 0;
     uint16_t* orow = p.out + row * p.out_stride;
+    const int oo = A ? line_offset(orow) : 0;
     float acc[J][8];
     float bs[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
+      if (!F && J > 1 && 512 * (wave + W * j) >= H) {
+        // An empty block: its sum is +0 and nothing of it is stored.
+        bs[j] = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sl[64 * k + lane] = xv[j][k];
+        for (int k = 0; k < 8; ++k) acc[j][k] = 0.0f;
+        continue;
+      }
+      to_slot(xv[j], ox);
       wave_fence();
-      const u32x4 xq = slot[wave][lane];
+      const u32x4 xq = sq[lane];
       u32x4 rq = {0, 0, 0, 0};
       if constexpr (R) {
         wave_fence();
-#pragma unroll
-        for (int k = 0; k < 8; ++k) sl[64 * k + lane] = rv[j][k];
+        to_slot(rv[j], orr);
         wave_fence();
-        rq = slot[wave][lane];
+        rq = sq[lane];
       }
       bs[j] = add_segment<R>(xq, rq, acc[j]);
       if constexpr (R) {
+        uint16_t* ror = p.residual_out + row * p.ro_stride;
+        const int oro = A ? line_offset(ror) : 0;
         wave_fence();
-        slot[wave][lane] = pack8_rne(acc[j]);
+        sq[lane] = pack8_rne(acc[j]);
         wave_fence();
-        store_block(ror, 512 * (wave + W * j), H, sl, lane);
+        store_block_rs(gen_row_rsrc(ror, oro, H), oro, wave + W * j);
       }
       wave_fence();
     }
@@ -906,12 +987,13 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
     __syncthreads();
     const float sumsq = pairwise_tree_lds<NB>(blk[parity]);
     const float rinv = 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
+    const auto os = gen_row_rsrc(orow, oo, H);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const u32x4 wq = wseg[64 * (wave + W * j) + lane];
-      slot[wave][lane] = normalise8(acc[j], rinv, wq);
+      sq[lane] = normalise8(acc[j], rinv, wq);
       wave_fence();
-      store_block(orow, 512 * (wave + W * j), H, sl, lane);
+      store_block_rs(os, oo, wave + W * j);
       wave_fence();
     }
   }
@@ -921,7 +1003,11 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
 // WAVES rows per workgroup, each wavefront one row, its J segment blocks
 // regrouped through its own LDS slot as in k_general_reg; the J block sums
 // finish the tree in registers, so no barrier is needed after the weight is
-// staged.
+// staged.  (Buffer-resource accesses with a next-row prefetch, as in
+// k_general_reg, were slower here wherever the last block is short, since
+// every access of it is issued: 26.8 -> 32.0 us at 65536 x 127, 32.3 -> 37.8
+// us at 32768 x 513, against 30.4 -> 29.7 us at 16384 x 1001, measured on
+// MI355X.)
 template <int WAVES, int J, bool R>
 __global__ __launch_bounds__(WAVES * 64) void k_general_wave(GenParams p) {
   __shared__ u32x4 slot[WAVES][64];
@@ -1469,28 +1555,40 @@ hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t 
   return hipGetLastError();
 }
 
+template <int B, int J, bool R, bool A, bool F = false>
+hipError_t go_general_reg_k(const GenParams& p, int64_t grid, hipStream_t s) {
+  const size_t lds = (size_t)B * J * 16;
+  auto k = k_general_reg<B, J, R, A, F>;
+  if (grid == -1) grid = resident(k, B, lds);
+  hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
+  return hipGetLastError();
+}
+
+// The line-aligned accesses (one segment per thread, at most 512 threads)
+// take rows whose last block holds more than 128 elements (measured on
+// MI355X: 32.3 -> 30.9 us at 8192 x 2047, 18.1 -> 17.6 us at 2048 x 4095,
+// 57.2 -> 55.7 us at 8192 x 4095, 28.8 -> 28.3 us at 8192 x 1791; with fewer
+// elements they were slower: 27.2 -> 27.4 us at 8192 x 1663, 34.1 -> 35.9 us
+// at 16384 x 1025).
+bool general_lines(int hidden) { return hidden % 512 == 0 || hidden % 512 > 128; }
+
 template <bool R, int B>
 hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s) {
-  const size_t lds = (size_t)B * j * 16;
+  // Every one of the j * B / 64 blocks of 512 elements holds row elements:
+  // the kernel without branches on the row's end.
+  const bool full = 512 * (j * B / 64 - 1) < p.hidden;
   switch (j) {
-    case 1: {
-      auto k = k_general_reg<B, 1, R>;
-      if (grid == -1) grid = resident(k, B, lds);
-      hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
-      return hipGetLastError();
-    }
-    case 2: {
-      auto k = k_general_reg<B, 2, R>;
-      if (grid == -1) grid = resident(k, B, lds);
-      hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
-      return hipGetLastError();
-    }
+    case 1:
+      if constexpr (B <= 512)
+        if (general_lines(p.hidden)) return go_general_reg_k<B, 1, R, true>(p, grid, s);
+      return go_general_reg_k<B, 1, R, false>(p, grid, s);
+    case 2:
+      if (full) return go_general_reg_k<B, 2, R, false, true>(p, grid, s);
+      return go_general_reg_k<B, 2, R, false>(p, grid, s);
     case 4:
       if constexpr (B * 4 <= 2048) {
-        auto k = k_general_reg<B, 4, R>;
-        if (grid == -1) grid = resident(k, B, lds);
-        hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
-        return hipGetLastError();
+        if (full) return go_general_reg_k<B, 4, R, false, true>(p, grid, s);
+        return go_general_reg_k<B, 4, R, false>(p, grid, s);
       }
       break;
   }
