@@ -100,6 +100,34 @@ def test_general_path_gives_the_fast_kernels_bits(h):
             assert np.array_equal(from_dev(o), ref_plain), (b, grid)
 
 
+@pytest.mark.parametrize("h", [1100, 1601, 1663, 2600, 4095, 6143, 9001, 12289])
+def test_general_blocks_and_grids_agree_on_odd_rows(h):
+    """Every workgroup size and grid of the general path gives the fp32
+    model's bits on rows that start anywhere in a 128-byte line: one to four
+    segments per thread, blocks past the row's end (1100 at 64 threads,
+    2600 at 128, 9001 and 12289 at 1024), rows that fill every block, and
+    the line-aligned accesses (last block above 128 elements) beside the
+    row-relative ones (1100, 1663)."""
+    import torch
+
+    n = 19
+    x, r, w = synth.workload(5450 + h, n, h)
+    announce("general blocks x grids, hidden %d" % h)
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
+    m_plain, _ = fp32_model.add_rmsnorm(x, None, w, 1e-6)
+    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    for b in BLOCKS:
+        for grid in (0, 7, -1):
+            out, res = gpu_fwd(x, r, w, 1e-6, path=arn.PATH_GENERAL, block=b, grid=grid,
+                               xd=xd, rd=rd, wd=wd)
+            assert same16(out, m_out) and same16(res, m_res), (b, grid)
+            o = poisoned_like(xd)
+            arn.rmsnorm_fwd_cfg(o, xd, wd, 1e-6, path=arn.PATH_GENERAL, block_threads=b,
+                                grid_blocks=grid)
+            torch.cuda.synchronize()
+            assert same16(from_dev(o), m_plain), (b, grid)
+
+
 def test_unaligned_pointers_take_the_general_kernel():
     import torch
 
