@@ -999,6 +999,113 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
   }
 }
 
+// Long rows (above 16384 elements) of any alignment, 1024 threads per row:
+// k_general's element-wise staging and arithmetic, thread t handling the G
+// elements t + 1024 u of the row (u < G) in two halves of G / 2.  Every access
+// goes through a buffer resource over its row (past the row: loads read +0,
+// stores are dropped), so none sits under a branch.  The first half of the
+// next row is loaded as soon as the current row's sums are staged in LDS,
+// ahead of its reduction and out stores; its second half is loaded when the
+// row starts, while the first half is added and staged.  Thread t stages and
+// later reads back only its own elements, and the block sums are rewritten
+// only after the next row's first barrier, so two barriers per row suffice.
+// (Measured on MI355X against k_general at 1024 threads: 168.2 -> 72.8 us at
+// 1024 x 32767, 257.1 -> 102.6 us at 2048 x 24001, 248.0 -> 142.2 us at
+// 4096 x 16385, bit-identical.  The weight staged in LDS beside the sums
+// instead of read for each row was no faster: 102.6 -> 108.8 us at
+// 2048 x 24001.)
+template <int NB, int G, bool R>
+__global__ __launch_bounds__(1024) void k_general_long(GenParams p) {
+  constexpr int B = 1024, W = B / 64, G2 = G / 2;
+  __shared__ float blk[NB];
+  extern __shared__ float4 stage4[];  // acc of element j at stage[j], padded to 8 * C
+  float* stage = reinterpret_cast<float*>(stage4);
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int H = p.hidden;
+  const int C = (H + 7) / 8;
+  const int chunks = (C + B - 1) / B;
+  // Element t + B u of a row: byte 2 t of the row's resource, plus 2 B u as
+  // the (uniform) scalar offset, so no address register per element.
+  const int vo = 2 * t;
+  const auto ws = gen_row_rsrc(p.weight, 0, H);
+  // Loads of half h (elements u = G2 h .. G2 h + G2 - 1) of a row.
+  auto load_half = [&](int64_t row, int h, uint16_t (&xv)[G2], uint16_t (&rv)[G2]) {
+    const auto xs = gen_row_rsrc(p.x + row * p.x_stride, 0, H);
+#pragma unroll
+    for (int u = 0; u < G2; ++u)
+      xv[u] = __builtin_amdgcn_raw_buffer_load_b16(xs, vo, 2 * B * (G2 * h + u), 0);
+    if constexpr (R) {
+      const auto rs = gen_row_rsrc(p.residual + row * p.r_stride, 0, H);
+#pragma unroll
+      for (int u = 0; u < G2; ++u)
+        rv[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, 2 * B * (G2 * h + u), 0);
+    }
+  };
+  // acc by element (+0 past the row, as the loads there read +0) staged in
+  // LDS, and residual_out stored the same way.
+  auto stage_half = [&](int64_t row, int h, const uint16_t (&xv)[G2], const uint16_t (&rv)[G2]) {
+    const auto ros = R ? gen_row_rsrc(p.residual_out + row * p.ro_stride, 0, H)
+                       : gen_row_rsrc(p.out, 0, 0);
+#pragma unroll
+    for (int u = 0; u < G2; ++u) {
+      const int j = t + B * (G2 * h + u);
+      float a = __builtin_bit_cast(float, (uint32_t)xv[u] << 16);
+      if constexpr (R) {
+        a = a + __builtin_bit_cast(float, (uint32_t)rv[u] << 16);
+        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a), ros, vo, 2 * B * (G2 * h + u), 0);
+      }
+      if (j < 8 * C) stage[j] = a;
+    }
+  };
+  uint16_t xa[G2], ra[G2], xb[G2], rb[G2];
+  if ((int64_t)blockIdx.x < p.n_rows) load_half(blockIdx.x, 0, xa, ra);
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
+    load_half(row, 1, xb, rb);
+    stage_half(row, 0, xa, ra);
+    stage_half(row, 1, xb, rb);
+    if (row + gridDim.x < p.n_rows) load_half(row + gridDim.x, 0, xa, ra);
+    for (int i = chunks * W + t; i < NB; i += B) blk[i] = 0.0f;
+    __syncthreads();
+    // the segments' sums, thread t holding segments t + B c as everywhere
+    for (int c = 0; c < chunks; ++c) {
+      const int s = c * B + t;
+      float acc[8];
+      if (s < C) {
+        const float4 l = stage4[2 * s];
+        const float4 h = stage4[2 * s + 1];
+        acc[0] = l.x; acc[1] = l.y; acc[2] = l.z; acc[3] = l.w;
+        acc[4] = h.x; acc[5] = h.y; acc[6] = h.z; acc[7] = h.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+      }
+      const float bs = wave_block_sum(seg_sumsq(acc));
+      if (lane == 0) blk[c * W + wave] = bs;
+    }
+    __syncthreads();
+    const float sumsq = pairwise_tree_lds<NB>(blk);
+    const float rinv = 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
+    const auto os = gen_row_rsrc(p.out + row * p.out_stride, 0, H);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint16_t wv[G2];
+#pragma unroll
+      for (int u = 0; u < G2; ++u)
+        wv[u] = __builtin_amdgcn_raw_buffer_load_b16(ws, vo, 2 * B * (G2 * h + u), 0);
+#pragma unroll
+      for (int u = 0; u < G2; ++u) {
+        const int j = t + B * (G2 * h + u);
+        const float a = j < 8 * C ? stage[j] : 0.0f;
+        const float w = __builtin_bit_cast(float, (uint32_t)wv[u] << 16);
+        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1((a * rinv) * w), os, vo,
+                                              2 * B * (G2 * h + u), 0);
+      }
+    }
+  }
+}
+
 // Wavefront-per-row general kernel for short rows (at most 64 J segments):
 // WAVES rows per workgroup, each wavefront one row, its J segment blocks
 // regrouped through its own LDS slot as in k_general_reg; the J block sums
@@ -1540,9 +1647,29 @@ hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, h
 
 // ---------------------------------------------------------------- internal API
 
+template <int NB, int G, bool R>
+hipError_t go_general_long(const GenParams& p, size_t lds, int64_t grid, hipStream_t s) {
+  auto k = k_general_long<NB, G, R>;
+  if (grid == -1) grid = resident(k, 1024, lds);
+  hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(1024), lds, s, p);
+  return hipGetLastError();
+}
+
 template <bool R, int B>
 hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t s) {
   const size_t lds = (size_t)((hidden + 7) / 8) * 32;
+  // Rows above 16384 at 1024 threads: the long-row kernel, with the fewest
+  // elements per thread (of 18, 20, 24, 28, 32) that cover the row.
+  if constexpr (B == 1024) {
+    if (hidden > 16384 && hidden <= 32768) {
+      const int g = (hidden + 1023) / 1024;
+      if (g <= 18) return go_general_long<64, 18, R>(p, lds, grid, s);
+      if (g <= 20) return go_general_long<64, 20, R>(p, lds, grid, s);
+      if (g <= 24) return go_general_long<64, 24, R>(p, lds, grid, s);
+      if (g <= 28) return go_general_long<64, 28, R>(p, lds, grid, s);
+      return go_general_long<64, 32, R>(p, lds, grid, s);
+    }
+  }
   if (two_pass_nb(hidden) == 32) {
     auto k = k_general<B, 32, R>;
     if (grid == -1) grid = resident(k, B, lds);

@@ -100,14 +100,15 @@ def test_general_path_gives_the_fast_kernels_bits(h):
             assert np.array_equal(from_dev(o), ref_plain), (b, grid)
 
 
-@pytest.mark.parametrize("h", [1100, 1601, 1663, 2600, 4095, 6143, 9001, 12289])
+@pytest.mark.parametrize("h", [1100, 1601, 1663, 2600, 4095, 6143, 9001, 12289, 17000, 28001])
 def test_general_blocks_and_grids_agree_on_odd_rows(h):
     """Every workgroup size and grid of the general path gives the fp32
     model's bits on rows that start anywhere in a 128-byte line: one to four
     segments per thread, blocks past the row's end (1100 at 64 threads,
-    2600 at 128, 9001 and 12289 at 1024), rows that fill every block, and
-    the line-aligned accesses (last block above 128 elements) beside the
-    row-relative ones (1100, 1663)."""
+    2600 at 128, 9001 and 12289 at 1024), rows that fill every block, the
+    line-aligned accesses (last block above 128 elements) beside the
+    row-relative ones (1100, 1663), and rows above 16384 (the long-row
+    kernel at 1024 threads, the LDS kernel below)."""
     import torch
 
     n = 19
