@@ -1698,13 +1698,16 @@ hipError_t go_general_reg_k(const GenParams& p, int64_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The line-aligned accesses (one segment per thread) take rows whose last
-// block holds more than 128 elements (measured on MI355X: 32.3 -> 30.9 us at
-// 8192 x 2047, 18.1 -> 17.6 us at 2048 x 4095, 57.2 -> 55.7 us at
-// 8192 x 4095, 28.8 -> 28.3 us at 8192 x 1791, 81.6 -> 80.6 us at
-// 8192 x 6143; with fewer elements they were slower: 27.2 -> 27.4 us at
-// 8192 x 1663, 34.1 -> 35.9 us at 16384 x 1025; with two segments per
-// thread, 56.6 -> 57.2 us at 2048 x 16383).
+// The line-aligned accesses take rows whose last block holds more than 128
+// elements, with one segment per thread, or with two when every block holds
+// row elements.  Measured on MI355X before the line-aligned form's accesses
+// became nontemporal: 32.3 -> 30.9 us at 8192 x 2047, 18.1 -> 17.6 us at
+// 2048 x 4095, 57.2 -> 55.7 us at 8192 x 4095, 28.8 -> 28.3 us at
+// 8192 x 1791, 81.6 -> 80.6 us at 8192 x 6143; with fewer elements they
+// were slower: 27.2 -> 27.4 us at 8192 x 1663, 34.1 -> 35.9 us at
+// 16384 x 1025.  With two segments per thread and nontemporal accesses:
+// 56.3 -> 52.0 us at 2048 x 16383; with blocks past the row's end, slower
+// (61.0 -> 66.1 us at 4096 x 9001, 80.5 -> 81.7 us at 4096 x 12287).
 bool general_lines(int hidden) { return hidden % 512 == 0 || hidden % 512 > 128; }
 
 template <bool R, int B>
@@ -1717,6 +1720,7 @@ hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s
       if (general_lines(p.hidden)) return go_general_reg_k<B, 1, R, true>(p, grid, s);
       return go_general_reg_k<B, 1, R, false>(p, grid, s);
     case 2:
+      if (full && general_lines(p.hidden)) return go_general_reg_k<B, 2, R, true, true>(p, grid, s);
       if (full) return go_general_reg_k<B, 2, R, false, true>(p, grid, s);
       return go_general_reg_k<B, 2, R, false>(p, grid, s);
     case 4:
