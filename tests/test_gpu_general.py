@@ -154,6 +154,46 @@ def test_unaligned_pointers_take_the_general_kernel():
     assert from_dev(ob)[0] == POISON and (from_dev(ob)[1 + n * h:] == POISON).all()
 
 
+@pytest.mark.parametrize("h", [1100, 4095, 8191, 9001, 16383])
+def test_tensors_at_different_line_offsets(h):
+    """x, residual, out and residual_out each start at a different element
+    offset (0, 1, 3 and 63 elements past a 256-byte boundary), so every row
+    of each tensor sits at its own place in its 128-byte lines: the
+    line-aligned accesses (4095, 8191, 16383) and the row-relative ones
+    (1100, 9001) give the contiguous bits and write nothing outside."""
+    import torch
+
+    n = 23
+    x, r, w = synth.workload(5600 + h, n, h)
+    announce("general: tensors at different line offsets, hidden %d" % h)
+    ref_out, ref_res = gpu_fwd(x, r, w, 1e-6)
+
+    def placed(a, off, fill=None):
+        buf = torch.full((a.size + 128,), np.int16(np.uint16(POISON).view(np.int16)),
+                         dtype=torch.int16, device="cuda:0")
+        view = buf[off:off + a.size]
+        if fill is not None:
+            view.copy_(to_dev(fill.reshape(-1)))
+        return buf, view.view(a.shape)
+
+    _, xd = placed(x, 0, x)
+    _, rd = placed(r, 1, r)
+    ob, out = placed(x, 3)
+    rb, res = placed(x, 63)
+    arn.add_rmsnorm_fwd(out, res, xd, rd, to_dev(w), 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), ref_out) and np.array_equal(from_dev(res), ref_res)
+    for buf, off in ((ob, 3), (rb, 63)):
+        b = from_dev(buf)
+        assert (b[:off] == POISON).all() and (b[off + n * h:] == POISON).all()
+    pb, po = placed(x, 7)
+    arn.rmsnorm_fwd(po, rd, to_dev(w), 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(po), gpu_plain(r, w))
+    b = from_dev(pb)
+    assert (b[:7] == POISON).all() and (b[7 + n * h:] == POISON).all()
+
+
 def _matrix(rows, cols, fill=POISON):
     import torch
 
