@@ -414,7 +414,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_wave_row(Params p) {
 // it.  Measured on MI355X with one small workgroup per row (x and residual
 // together at most 64 MiB): 4-14% faster than holding it, as the row's
 // stores then follow its loads later (2048 x 4096: 12.0 against 13.1 us).
-template <int B, int J, int Q, bool R, bool L>
+template <int B, int J, int Q, bool R, bool L, bool FB = false>
 __global__ __launch_bounds__(B) void k_wg_row(Params p) {
   static_assert(!L || Q == 0, "the late weight read is built for bf16 out only");
   constexpr int W = B / 64;
@@ -441,21 +441,28 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
     }
   }
 
-  // Plain quantised rows are read and written through per-row buffer
-  // resources, as in k_wave_row: segments past the row read as zero and their
-  // stores are dropped, so nothing branches on the row's end (measured 1-4%
-  // faster there).  The other variants use bounds-checked pointer accesses
-  // (measured 2% faster for plain bf16, the same for the fused forms).
-  constexpr bool BUF = Q != 0 && !R;
+  // Plain quantised rows, and fused bf16 rows whose segments fill every
+  // thread's J slots (FB), are read and written through per-row buffer
+  // resources, as in k_wave_row: segments past the row read as zero and
+  // their stores are dropped, so nothing branches on the row's end.
+  // Measured on MI355X: 1-4% faster for plain quantised rows; for FB rows
+  // the same at 4096 x 8192, 23.46 -> 22.68 us at 4096 x 4096, 12.06 ->
+  // 11.94 us at 2048 x 4096, 7.17 -> 7.01 us at 1024 x 4096; for every fused
+  // bf16 row, 5% slower at 4096 x 2560, where 37% of the slots lie past the
+  // row (hence FB).  The
+  // other forms use bounds-checked pointer accesses (measured 2% faster for
+  // plain bf16).
+  constexpr bool BUF = (Q != 0 && !R) || FB;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x, parity ^= 1) {
     u32x4 xq[J], rq[J];
     if constexpr (BUF) {
       const __amdgpu_buffer_rsrc_t rx = row_rsrc(p.x, row, p.x_stride, C, true);
+      const __amdgpu_buffer_rsrc_t rr = row_rsrc(p.residual, row, p.r_stride, C, R);
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         xq[j] = load_seg(rx, t + B * j);
-        rq[j] = u32x4{0, 0, 0, 0};
+        rq[j] = R ? load_seg(rr, t + B * j) : u32x4{0, 0, 0, 0};
       }
     } else {
       const u32x4* xr = p.x + row * p.x_stride;
@@ -478,7 +485,10 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
     for (int j = 0; j < J; ++j) {
       const int s = t + B * j;
       bs[j] = add_segment<R>(xq[j], rq[j], acc[j]);
-      if (R && s < C) store_stream(p.residual_out + row * p.ro_stride + s, pack8_rne(acc[j]));
+      if constexpr (R && BUF)
+        store_seg(row_rsrc(p.residual_out, row, p.ro_stride, C, true), s, pack8_rne(acc[j]));
+      else if (R && s < C)
+        store_stream(p.residual_out + row * p.ro_stride + s, pack8_rne(acc[j]));
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) bs[j] = wave_block_sum(bs[j]);
@@ -489,7 +499,14 @@ __global__ __launch_bounds__(B) void k_wg_row(Params p) {
     if constexpr (L) __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     const float rinv = row_rinv(pairwise_tree_lds<NB>(blk[parity]), p);
-    if constexpr (!Q) {
+    if constexpr (!Q && BUF) {
+      const __amdgpu_buffer_rsrc_t ro = row_rsrc(p.out, row, p.out_stride, C, true);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int s = t + B * j;
+        store_seg(ro, s, normalise8(acc[j], rinv, L ? p.weight[s < C ? s : 0] : wq[L ? 0 : j]));
+      }
+    } else if constexpr (!Q) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int s = t + B * j;
@@ -1614,18 +1631,18 @@ hipError_t go_wave(const Params& p, int j, int64_t grid, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int Q, bool R, int B, bool L>
+template <int Q, bool R, int B, bool L, bool FB = false>
 hipError_t go_wg(const Params& p, int j, int64_t grid, hipStream_t s) {
   switch (j) {
-    case 1: return launch(k_wg_row<B, 1, Q, R, L>, B, 0, grid, p.n_rows, p, s);
-    case 2: return launch(k_wg_row<B, 2, Q, R, L>, B, 0, grid, p.n_rows, p, s);
+    case 1: return launch(k_wg_row<B, 1, Q, R, L, FB>, B, 0, grid, p.n_rows, p, s);
+    case 2: return launch(k_wg_row<B, 2, Q, R, L, FB>, B, 0, grid, p.n_rows, p, s);
     case 4:
       if constexpr (B * 4 <= 2048)
-        return launch(k_wg_row<B, 4, Q, R, L>, B, 0, grid, p.n_rows, p, s);
+        return launch(k_wg_row<B, 4, Q, R, L, FB>, B, 0, grid, p.n_rows, p, s);
       break;
     case 8:
       if constexpr (B * 8 <= 2048)
-        return launch(k_wg_row<B, 8, Q, R, L>, B, 0, grid, p.n_rows, p, s);
+        return launch(k_wg_row<B, 8, Q, R, L, FB>, B, 0, grid, p.n_rows, p, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -1633,6 +1650,13 @@ hipError_t go_wg(const Params& p, int j, int64_t grid, hipStream_t s) {
 
 template <int Q, bool R, int B>
 hipError_t go_wg_late(const Params& p, int j, int64_t grid, bool late, hipStream_t s) {
+  if constexpr (Q == 0 && R) {
+    // Fused bf16 rows whose segments fill every thread's slots.
+    if (p.segs == B * j) {
+      if (late) return go_wg<Q, R, B, true, true>(p, j, grid, s);
+      return go_wg<Q, R, B, false, true>(p, j, grid, s);
+    }
+  }
   if constexpr (Q == 0) {
     if (late) return go_wg<Q, R, B, true>(p, j, grid, s);
   } else {
