@@ -1068,14 +1068,23 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
 // ahead of its reduction and out stores; its second half is loaded when the
 // row starts, while the first half is added and staged.  Thread t stages and
 // later reads back only its own elements, and the block sums are rewritten
-// only after the next row's first barrier, so two barriers per row suffice.
+// only after the next row's first barrier, so two barriers per row suffice
+// (three in the line-aligned form below).
 // (Measured on MI355X against k_general at 1024 threads: 168.2 -> 72.8 us at
 // 1024 x 32767, 257.1 -> 102.6 us at 2048 x 24001, 248.0 -> 142.2 us at
 // 4096 x 16385, bit-identical.  The weight staged in LDS beside the sums
 // instead of read for each row was no faster: 102.6 -> 108.8 us at
-// 2048 x 24001.)
-template <int NB, int G, bool R>
+// 2048 x 24001.)  A: when all tensors' rows sit at the same offset o in their
+// 128-byte lines (checked on the host), thread t's element u is t + 1024 u - o
+// and every access covers one whole line, nontemporal; this needs G elements
+// per thread to cover o + the padded row, so rows above 32704 elements keep
+// the row-relative form (measured, with its third barrier: 102.8 -> 84.4 us
+// at 2048 x 24001, 142.2 -> 124.6 us at 4096 x 16385, 121.1 -> 98.8 us at
+// 2048 x 28001).
+template <int NB, int G, bool R, bool A>
 __global__ __launch_bounds__(1024) void k_general_long(GenParams p) {
+  constexpr int CP = A ? 2 : 0;  // nontemporal in the line-aligned form
+  constexpr int OOB = 1 << 30;
   constexpr int B = 1024, W = B / 64, G2 = G / 2;
   __shared__ float blk[NB];
   extern __shared__ float4 stage4[];  // acc of element j at stage[j], padded to 8 * C
@@ -1089,34 +1098,41 @@ __global__ __launch_bounds__(1024) void k_general_long(GenParams p) {
   // Element t + B u of a row: byte 2 t of the row's resource, plus 2 B u as
   // the (uniform) scalar offset, so no address register per element.
   const int vo = 2 * t;
-  const auto ws = gen_row_rsrc(p.weight, 0, H);
+  // A: every tensor's row starts o elements into its 128-byte line (checked
+  // on the host); thread t's element u is t + B u - o, so each access covers
+  // one whole line, and lanes with t + B u < o (before the row) are dropped.
+  auto line_o = [&](int64_t row) { return A ? line_offset(p.x + row * p.x_stride) : 0; };
+  auto vo0 = [&](int o) { return t < o ? OOB : vo; };  // the first access's offset
   // Loads of half h (elements u = G2 h .. G2 h + G2 - 1) of a row.
   auto load_half = [&](int64_t row, int h, uint16_t (&xv)[G2], uint16_t (&rv)[G2]) {
-    const auto xs = gen_row_rsrc(p.x + row * p.x_stride, 0, H);
+    const int o = line_o(row);
+    const auto xs = gen_row_rsrc(p.x + row * p.x_stride, o, H);
 #pragma unroll
     for (int u = 0; u < G2; ++u)
-      xv[u] = __builtin_amdgcn_raw_buffer_load_b16(xs, vo, 2 * B * (G2 * h + u), 0);
+      xv[u] = __builtin_amdgcn_raw_buffer_load_b16(xs, G2 * h + u == 0 ? vo0(o) : vo, 2 * B * (G2 * h + u), CP);
     if constexpr (R) {
-      const auto rs = gen_row_rsrc(p.residual + row * p.r_stride, 0, H);
+      const auto rs = gen_row_rsrc(p.residual + row * p.r_stride, o, H);
 #pragma unroll
       for (int u = 0; u < G2; ++u)
-        rv[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, 2 * B * (G2 * h + u), 0);
+        rv[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, G2 * h + u == 0 ? vo0(o) : vo, 2 * B * (G2 * h + u), CP);
     }
   };
   // acc by element (+0 past the row, as the loads there read +0) staged in
   // LDS, and residual_out stored the same way.
   auto stage_half = [&](int64_t row, int h, const uint16_t (&xv)[G2], const uint16_t (&rv)[G2]) {
-    const auto ros = R ? gen_row_rsrc(p.residual_out + row * p.ro_stride, 0, H)
+    const int o = line_o(row);
+    const auto ros = R ? gen_row_rsrc(p.residual_out + row * p.ro_stride, o, H)
                        : gen_row_rsrc(p.out, 0, 0);
 #pragma unroll
     for (int u = 0; u < G2; ++u) {
-      const int j = t + B * (G2 * h + u);
+      const int j = t + B * (G2 * h + u) - o;
       float a = __builtin_bit_cast(float, (uint32_t)xv[u] << 16);
       if constexpr (R) {
         a = a + __builtin_bit_cast(float, (uint32_t)rv[u] << 16);
-        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a), ros, vo, 2 * B * (G2 * h + u), 0);
+        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a), ros, G2 * h + u == 0 ? vo0(o) : vo,
+                                              2 * B * (G2 * h + u), CP);
       }
-      if (j < 8 * C) stage[j] = a;
+      if (j >= 0 && j < 8 * C) stage[j] = a;
     }
   };
   uint16_t xa[G2], ra[G2], xb[G2], rb[G2];
@@ -1147,22 +1163,28 @@ __global__ __launch_bounds__(1024) void k_general_long(GenParams p) {
     __syncthreads();
     const float sumsq = pairwise_tree_lds<NB>(blk);
     const float rinv = 1.0f / __builtin_sqrtf(sumsq / p.hidden_f + p.eps);
-    const auto os = gen_row_rsrc(p.out + row * p.out_stride, 0, H);
+    const int o = line_o(row);
+    const auto os = gen_row_rsrc(p.out + row * p.out_stride, o, H);
+    const auto ws = gen_row_rsrc(p.weight, o, H);  // the weight in the row's element order
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint16_t wv[G2];
 #pragma unroll
       for (int u = 0; u < G2; ++u)
-        wv[u] = __builtin_amdgcn_raw_buffer_load_b16(ws, vo, 2 * B * (G2 * h + u), 0);
+        wv[u] = __builtin_amdgcn_raw_buffer_load_b16(ws, G2 * h + u == 0 ? vo0(o) : vo, 2 * B * (G2 * h + u), 0);
 #pragma unroll
       for (int u = 0; u < G2; ++u) {
-        const int j = t + B * (G2 * h + u);
-        const float a = j < 8 * C ? stage[j] : 0.0f;
+        const int j = t + B * (G2 * h + u) - o;
+        const float a = j >= 0 && j < 8 * C ? stage[j] : 0.0f;
         const float w = __builtin_bit_cast(float, (uint32_t)wv[u] << 16);
-        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1((a * rinv) * w), os, vo,
-                                              2 * B * (G2 * h + u), 0);
+        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1((a * rinv) * w), os, G2 * h + u == 0 ? vo0(o) : vo,
+                                              2 * B * (G2 * h + u), CP);
       }
     }
+    // In the line-aligned form a thread's elements move with the row's line
+    // offset, so the next row's sums may land in slots other threads are
+    // still reading.
+    if constexpr (A) __syncthreads();
   }
 }
 
@@ -1714,9 +1736,9 @@ hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, h
 
 // ---------------------------------------------------------------- internal API
 
-template <int NB, int G, bool R>
+template <int NB, int G, bool R, bool A = false>
 hipError_t go_general_long(const GenParams& p, size_t lds, int64_t grid, hipStream_t s) {
-  auto k = k_general_long<NB, G, R>;
+  auto k = k_general_long<NB, G, R, A>;
   if (grid == -1) grid = resident(k, 1024, lds);
   hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(1024), lds, s, p);
   return hipGetLastError();
@@ -1726,8 +1748,25 @@ template <bool R, int B>
 hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t s) {
   const size_t lds = (size_t)((hidden + 7) / 8) * 32;
   // Rows above 16384 at 1024 threads: the long-row kernel, with the fewest
-  // elements per thread (of 18, 20, 24, 28, 32) that cover the row.
+  // elements per thread (of 18, 20, 24, 28, 32) that cover the row, in the
+  // line-aligned form when every tensor's rows share their line offset.
   if constexpr (B == 1024) {
+    auto off = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) >> 1) & 63; };
+    const bool same = off(p.x) == off(p.out) && p.x_stride % 64 == p.out_stride % 64 &&
+                      (!R || (off(p.x) == off(p.residual) && off(p.x) == off(p.residual_out) &&
+                              p.x_stride % 64 == p.r_stride % 64 &&
+                              p.x_stride % 64 == p.ro_stride % 64));
+    // Thread t's elements t + 1024 u - o (o <= 63) must cover the row padded
+    // to whole segments.
+    const int padded = (hidden + 7) / 8 * 8;
+    if (same && hidden > 16384 && padded + 63 <= 32768) {
+      const int g = (padded + 63 + 1023) / 1024;
+      if (g <= 18) return go_general_long<64, 18, R, true>(p, lds, grid, s);
+      if (g <= 20) return go_general_long<64, 20, R, true>(p, lds, grid, s);
+      if (g <= 24) return go_general_long<64, 24, R, true>(p, lds, grid, s);
+      if (g <= 28) return go_general_long<64, 28, R, true>(p, lds, grid, s);
+      return go_general_long<64, 32, R, true>(p, lds, grid, s);
+    }
     if (hidden > 16384 && hidden <= 32768) {
       const int g = (hidden + 1023) / 1024;
       if (g <= 18) return go_general_long<64, 18, R>(p, lds, grid, s);

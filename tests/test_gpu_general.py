@@ -129,10 +129,11 @@ def test_general_blocks_and_grids_agree_on_odd_rows(h):
             assert same16(from_dev(o), m_plain), (b, grid)
 
 
-def test_unaligned_pointers_take_the_general_kernel():
+@pytest.mark.parametrize("h", [4096, 24000])
+def test_unaligned_pointers_take_the_general_kernel(h):
     import torch
 
-    n, h = 24, 4096
+    n = 24
     x, r, w = synth.workload(5500, n, h)
     announce("general: pointers offset by one element")
     ref_out, ref_res = gpu_fwd(x, r, w, 1e-6)
@@ -154,7 +155,7 @@ def test_unaligned_pointers_take_the_general_kernel():
     assert from_dev(ob)[0] == POISON and (from_dev(ob)[1 + n * h:] == POISON).all()
 
 
-@pytest.mark.parametrize("h", [1100, 4095, 8191, 9001, 16383])
+@pytest.mark.parametrize("h", [1100, 4095, 8191, 9001, 16383, 20000])
 def test_tensors_at_different_line_offsets(h):
     """x, residual, out and residual_out each start at a different element
     offset (0, 1, 3 and 63 elements past a 256-byte boundary), so every row
