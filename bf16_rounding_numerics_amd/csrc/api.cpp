@@ -330,7 +330,7 @@ int dispatch(const addrms::FwdArgs& a, const add_rmsnorm_launch_cfg& c,
     // Longer rows take one workgroup each, by default with one segment per
     // thread (the fewest registers, so the most rows in flight): the smallest
     // workgroup that covers the row, 64 to 1024 threads; two segments per
-    // thread at 1024 threads up to 16384, and the LDS kernel above.
+    // thread at 1024 threads up to 16384, and the long-row kernel above.
     int b = c.block_threads;
     if (b == 0 && hidden <= 1024) {
       b = 256;

@@ -1085,7 +1085,9 @@ template <int NB, int G, bool R, bool A>
 __global__ __launch_bounds__(1024) void k_general_long(GenParams p) {
   constexpr int CP = A ? 2 : 0;  // nontemporal in the line-aligned form
   constexpr int OOB = 1 << 30;
-  constexpr int B = 1024, W = B / 64, G2 = G / 2;
+  constexpr int B = 1024, W = B / 64;
+  constexpr int G0 = (G + 1) / 2;  // accesses of the first half; G - G0 in the second
+  auto in_half = [](int h, int u) { return u < (h ? G - G0 : G0); };
   __shared__ float blk[NB];
   extern __shared__ float4 stage4[];  // acc of element j at stage[j], padded to 8 * C
   float* stage = reinterpret_cast<float*>(stage4);
@@ -1096,46 +1098,59 @@ __global__ __launch_bounds__(1024) void k_general_long(GenParams p) {
   const int C = (H + 7) / 8;
   const int chunks = (C + B - 1) / B;
   // Element t + B u of a row: byte 2 t of the row's resource, plus 2 B u as
-  // the (uniform) scalar offset, so no address register per element.
+  // the (uniform) scalar offset, so no address register per element.  An
+  // access wholly past the row (2 B u at or beyond the resource's size) takes
+  // the size itself as its scalar offset: then it is out of range whether the
+  // hardware adds the scalar offset to the checked offset or subtracts it
+  // from the size, and no subtraction can wrap.  Only the last four accesses
+  // can lie wholly past the row (G - 4 <= ceil(hidden / B), checked at
+  // launch); the others keep constant offsets (clamping all of them cost
+  // 1-2% on MI355X).
   const int vo = 2 * t;
+  auto so = [&](int o, int u) { return u < G - 4 ? 2 * B * u : min(2 * B * u, 2 * (o + H)); };
   // A: every tensor's row starts o elements into its 128-byte line (checked
   // on the host); thread t's element u is t + B u - o, so each access covers
   // one whole line, and lanes with t + B u < o (before the row) are dropped.
   auto line_o = [&](int64_t row) { return A ? line_offset(p.x + row * p.x_stride) : 0; };
   auto vo0 = [&](int o) { return t < o ? OOB : vo; };  // the first access's offset
-  // Loads of half h (elements u = G2 h .. G2 h + G2 - 1) of a row.
-  auto load_half = [&](int64_t row, int h, uint16_t (&xv)[G2], uint16_t (&rv)[G2]) {
+  // Loads of half h (elements u = G0 h .. G0 h + G0 - 1, below G) of a row.
+  auto load_half = [&](int64_t row, int h, uint16_t (&xv)[G0], uint16_t (&rv)[G0]) {
     const int o = line_o(row);
     const auto xs = gen_row_rsrc(p.x + row * p.x_stride, o, H);
 #pragma unroll
-    for (int u = 0; u < G2; ++u)
-      xv[u] = __builtin_amdgcn_raw_buffer_load_b16(xs, G2 * h + u == 0 ? vo0(o) : vo, 2 * B * (G2 * h + u), CP);
+    for (int u = 0; u < G0; ++u)
+      if (in_half(h, u))
+        xv[u] = __builtin_amdgcn_raw_buffer_load_b16(xs, G0 * h + u == 0 ? vo0(o) : vo,
+                                                     so(o, G0 * h + u), CP);
     if constexpr (R) {
       const auto rs = gen_row_rsrc(p.residual + row * p.r_stride, o, H);
 #pragma unroll
-      for (int u = 0; u < G2; ++u)
-        rv[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, G2 * h + u == 0 ? vo0(o) : vo, 2 * B * (G2 * h + u), CP);
+      for (int u = 0; u < G0; ++u)
+        if (in_half(h, u))
+          rv[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, G0 * h + u == 0 ? vo0(o) : vo,
+                                                       so(o, G0 * h + u), CP);
     }
   };
   // acc by element (+0 past the row, as the loads there read +0) staged in
   // LDS, and residual_out stored the same way.
-  auto stage_half = [&](int64_t row, int h, const uint16_t (&xv)[G2], const uint16_t (&rv)[G2]) {
+  auto stage_half = [&](int64_t row, int h, const uint16_t (&xv)[G0], const uint16_t (&rv)[G0]) {
     const int o = line_o(row);
     const auto ros = R ? gen_row_rsrc(p.residual_out + row * p.ro_stride, o, H)
                        : gen_row_rsrc(p.out, 0, 0);
 #pragma unroll
-    for (int u = 0; u < G2; ++u) {
-      const int j = t + B * (G2 * h + u) - o;
+    for (int u = 0; u < G0; ++u) {
+      if (!in_half(h, u)) continue;
+      const int j = t + B * (G0 * h + u) - o;
       float a = __builtin_bit_cast(float, (uint32_t)xv[u] << 16);
       if constexpr (R) {
         a = a + __builtin_bit_cast(float, (uint32_t)rv[u] << 16);
-        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a), ros, G2 * h + u == 0 ? vo0(o) : vo,
-                                              2 * B * (G2 * h + u), CP);
+        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a), ros, G0 * h + u == 0 ? vo0(o) : vo,
+                                              so(o, G0 * h + u), CP);
       }
       if (j >= 0 && j < 8 * C) stage[j] = a;
     }
   };
-  uint16_t xa[G2], ra[G2], xb[G2], rb[G2];
+  uint16_t xa[G0], ra[G0], xb[G0], rb[G0];
   if ((int64_t)blockIdx.x < p.n_rows) load_half(blockIdx.x, 0, xa, ra);
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
     load_half(row, 1, xb, rb);
@@ -1168,17 +1183,20 @@ __global__ __launch_bounds__(1024) void k_general_long(GenParams p) {
     const auto ws = gen_row_rsrc(p.weight, o, H);  // the weight in the row's element order
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint16_t wv[G2];
+      uint16_t wv[G0];
 #pragma unroll
-      for (int u = 0; u < G2; ++u)
-        wv[u] = __builtin_amdgcn_raw_buffer_load_b16(ws, G2 * h + u == 0 ? vo0(o) : vo, 2 * B * (G2 * h + u), 0);
+      for (int u = 0; u < G0; ++u)
+        if (in_half(h, u))
+          wv[u] = __builtin_amdgcn_raw_buffer_load_b16(ws, G0 * h + u == 0 ? vo0(o) : vo,
+                                                       so(o, G0 * h + u), 0);
 #pragma unroll
-      for (int u = 0; u < G2; ++u) {
-        const int j = t + B * (G2 * h + u) - o;
+      for (int u = 0; u < G0; ++u) {
+        if (!in_half(h, u)) continue;
+        const int j = t + B * (G0 * h + u) - o;
         const float a = j >= 0 && j < 8 * C ? stage[j] : 0.0f;
         const float w = __builtin_bit_cast(float, (uint32_t)wv[u] << 16);
-        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1((a * rinv) * w), os, G2 * h + u == 0 ? vo0(o) : vo,
-                                              2 * B * (G2 * h + u), CP);
+        __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1((a * rinv) * w), os, G0 * h + u == 0 ? vo0(o) : vo,
+                                              so(o, G0 * h + u), CP);
       }
     }
     // In the line-aligned form a thread's elements move with the row's line
@@ -1738,6 +1756,8 @@ hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, h
 
 template <int NB, int G, bool R, bool A = false>
 hipError_t go_general_long(const GenParams& p, size_t lds, int64_t grid, hipStream_t s) {
+  // the kernel clamps the scalar offsets of its last four accesses only
+  if (G - 4 > (p.hidden + 1023) / 1024) return hipErrorInvalidValue;
   auto k = k_general_long<NB, G, R, A>;
   if (grid == -1) grid = resident(k, 1024, lds);
   hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(1024), lds, s, p);
@@ -1748,8 +1768,9 @@ template <bool R, int B>
 hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t s) {
   const size_t lds = (size_t)((hidden + 7) / 8) * 32;
   // Rows above 16384 at 1024 threads: the long-row kernel, with the fewest
-  // elements per thread (of 18, 20, 24, 28, 32) that cover the row, in the
-  // line-aligned form when every tensor's rows share their line offset.
+  // elements per thread (of 18, 20, 24, 28, 32, and 33 for the line-aligned
+  // form's extra line) that cover the row, in the line-aligned form when
+  // every tensor's rows share their line offset.
   if constexpr (B == 1024) {
     auto off = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) >> 1) & 63; };
     const bool same = off(p.x) == off(p.out) && p.x_stride % 64 == p.out_stride % 64 &&
@@ -1759,13 +1780,14 @@ hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t 
     // Thread t's elements t + 1024 u - o (o <= 63) must cover the row padded
     // to whole segments.
     const int padded = (hidden + 7) / 8 * 8;
-    if (same && hidden > 16384 && padded + 63 <= 32768) {
+    if (same && hidden > 16384) {
       const int g = (padded + 63 + 1023) / 1024;
       if (g <= 18) return go_general_long<64, 18, R, true>(p, lds, grid, s);
       if (g <= 20) return go_general_long<64, 20, R, true>(p, lds, grid, s);
       if (g <= 24) return go_general_long<64, 24, R, true>(p, lds, grid, s);
       if (g <= 28) return go_general_long<64, 28, R, true>(p, lds, grid, s);
-      return go_general_long<64, 32, R, true>(p, lds, grid, s);
+      if (g <= 32) return go_general_long<64, 32, R, true>(p, lds, grid, s);
+      return go_general_long<64, 33, R, true>(p, lds, grid, s);
     }
     if (hidden > 16384 && hidden <= 32768) {
       const int g = (hidden + 1023) / 1024;

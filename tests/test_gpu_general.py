@@ -195,6 +195,52 @@ def test_tensors_at_different_line_offsets(h):
     assert (b[:7] == POISON).all() and (b[7 + n * h:] == POISON).all()
 
 
+@pytest.mark.parametrize("h", [16385, 17000, 24001, 32705, 32767, 32768])
+def test_long_rows_sharing_a_line_offset_write_only_their_rows(h):
+    """Rows above 16384 whose four tensors all start 5 elements past a
+    256-byte boundary take the line-aligned long-row kernel (18 to 34
+    elements per thread).  At 16385 and 17000 each thread's last access lies
+    wholly past every row; from 32705 up the rows need the 34-element form.
+    The fused op and plain RMSNorm give the fp32 model's bits at every grid
+    tried and write nothing before or after the tensors, including the 4 KiB
+    that the accesses past the last row would reach."""
+    import torch
+
+    n, off, tail = 7, 5, 4096
+    x, r, w = synth.workload(5700 + h, n, h)
+    announce("general: long rows sharing a line offset, hidden %d" % h)
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
+    m_plain, _ = fp32_model.add_rmsnorm(x, None, w, 1e-6)
+    wd = to_dev(w)
+
+    def placed(fill=None):
+        buf = torch.full((off + n * h + tail,), np.int16(np.uint16(POISON).view(np.int16)),
+                         dtype=torch.int16, device="cuda:0")
+        view = buf[off:off + n * h]
+        if fill is not None:
+            view.copy_(to_dev(fill.reshape(-1)))
+        return buf, view.view(n, h)
+
+    def untouched(buf):
+        b = from_dev(buf)
+        return (b[:off] == POISON).all() and (b[off + n * h:] == POISON).all()
+
+    _, xd = placed(x)
+    _, rd = placed(r)
+    for grid in (0, 3, n):
+        ob, out = placed()
+        rb, res = placed()
+        arn.add_rmsnorm_fwd_cfg(out, res, xd, rd, wd, 1e-6, path=arn.PATH_GENERAL,
+                                grid_blocks=grid)
+        torch.cuda.synchronize()
+        assert same16(from_dev(out), m_out) and same16(from_dev(res), m_res), grid
+        assert untouched(ob) and untouched(rb), grid
+        pb, po = placed()
+        arn.rmsnorm_fwd_cfg(po, xd, wd, 1e-6, path=arn.PATH_GENERAL, grid_blocks=grid)
+        torch.cuda.synchronize()
+        assert same16(from_dev(po), m_plain) and untouched(pb), grid
+
+
 def _matrix(rows, cols, fill=POISON):
     import torch
 
