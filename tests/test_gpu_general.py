@@ -241,6 +241,58 @@ def test_long_rows_sharing_a_line_offset_write_only_their_rows(h):
         assert same16(from_dev(po), m_plain) and untouched(pb), grid
 
 
+IN_PLACE_MODES = ["out=x,residual_out=residual", "out=x", "residual_out=residual",
+                  "out=residual,residual_out=x"]
+
+
+@pytest.mark.parametrize("mode", IN_PLACE_MODES)
+@pytest.mark.parametrize("h", [1001, 1663, 4095, 9001, 16383, 17000, 32767])
+def test_general_kernels_in_place(h, mode):
+    """An output that is an input's own buffer, on each general kernel: one
+    wavefront per row (1001), the register kernel row-relative (1663) and
+    line-aligned (4095, 9001, 16383), the long-row kernel line-aligned
+    (17000, 32767).  Every element's inputs are read before its outputs are
+    written, so the results are the fp32 model's bits, as out of place."""
+    import torch
+
+    n = 13
+    x, r, w = synth.workload(5800 + h, n, h)
+    announce("general in place: hidden %d, %s" % (h, mode))
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
+    xd, rd, wd = to_dev(x), to_dev(r), to_dev(w)
+    out = {"out=x,residual_out=residual": xd, "out=x": xd, "residual_out=residual": None,
+           "out=residual,residual_out=x": rd}[mode]
+    res = {"out=x,residual_out=residual": rd, "out=x": None, "residual_out=residual": rd,
+           "out=residual,residual_out=x": xd}[mode]
+    out = poisoned_like(xd) if out is None else out
+    res = poisoned_like(xd) if res is None else res
+    arn.add_rmsnorm_fwd(out, res, xd, rd, wd, 1e-6)
+    torch.cuda.synchronize()
+    assert same16(from_dev(out), m_out) and same16(from_dev(res), m_res)
+
+
+@pytest.mark.parametrize("h", [4095, 9001, 20000])
+def test_general_in_place_tensors_at_different_offsets(h):
+    """out = x and residual_out = residual with x one element past a 256-byte
+    boundary and residual on it, so the two streams sit at different places
+    in their lines: the register kernel's line-aligned form with a line
+    offset per tensor (4095, 9001) and the long-row kernel's row-relative
+    form (20000), in place."""
+    import torch
+
+    n = 9
+    x, r, w = synth.workload(5900 + h, n, h)
+    announce("general in place, tensors at different offsets: hidden %d" % h)
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
+    buf = torch.empty(n * h + 128, dtype=torch.int16, device="cuda:0")
+    xv = buf[1:1 + n * h].view(n, h)
+    xv.copy_(to_dev(x))
+    rd = to_dev(r)
+    arn.add_rmsnorm_fwd(xv, rd, xv, rd, to_dev(w), 1e-6)
+    torch.cuda.synchronize()
+    assert same16(from_dev(xv), m_out) and same16(from_dev(rd), m_res)
+
+
 def _matrix(rows, cols, fill=POISON):
     import torch
 
