@@ -839,7 +839,11 @@ __global__ __launch_bounds__(B) void k_general(GenParams p) {
 // A (line-aligned): each 16-bit access covers one whole 128-byte line
 // instead of straddling two lines of a misaligned row, nine accesses per
 // block instead of eight.  F: every block holds row elements; otherwise
-// blocks past the row's end are skipped.
+// blocks past the row's end are skipped.  S (with A): all four tensors sit
+// at one offset in their lines (checked on the host), so the sums and
+// residual_out are formed where loaded, and each line that two blocks share
+// is written whole, by the wavefront of the first block, after the row's
+// barrier (so every wavefront has read the row, in place too).
 DEV void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
 // Stores a wavefront's block of 512 elements (first element b0 of the row)
@@ -876,8 +880,9 @@ DEV __amdgpu_buffer_rsrc_t gen_row_rsrc(const uint16_t* row, int o, int h) {
                                            0x00020000);
 }
 
-template <int B, int J, bool R, bool A, bool F>
+template <int B, int J, bool R, bool A, bool F, bool S = false>
 __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
+  static_assert(!S || A, "shared line offsets are a case of the line-aligned form");
   constexpr int W = B / 64;
   constexpr int NB = W * J;
   constexpr int NW = A ? 9 : 8;     // 16-bit accesses per lane and block
@@ -899,8 +904,8 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
   // sit at different offsets in their lines, was slower with it: 49.7 ->
   // 51.0 us at 4096 x 8191).  The 16-bit slot (out, and x and residual in
   // the other form) is the first half of the fp32 one.
-  constexpr bool EW = !A;
-  __shared__ float4 slotf4[W][EW ? 128 : (512 + 2 * PAD) / 8];
+  constexpr bool EW = !A || S;
+  __shared__ float4 slotf4[W][S ? (512 + 2 * PAD) / 4 : EW ? 128 : (512 + 2 * PAD) / 8];
   extern __shared__ u32x4 wseg[];  // B * J segments of weight
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -911,7 +916,7 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
   __syncthreads();
   uint16_t* sl = reinterpret_cast<uint16_t*>(slotf4[wave]) + PAD;  // sl[i]: element i of the block
   u32x4* sq = reinterpret_cast<u32x4*>(slotf4[wave]) + PAD / 8;    // sq[l]: segment l of the block
-  float* slf = reinterpret_cast<float*>(slotf4[wave]);             // slf[i]: element i, fp32 (EW)
+  float* slf = reinterpret_cast<float*>(slotf4[wave]) + (S ? PAD : 0);  // slf[i]: element i, fp32 (EW)
 
   // Access k of lane l in block b touches element 512 b + 64 k + l - o of
   // the row (o = 0 unless line-aligned), at byte 2 (512 b + 64 k + l) of the
@@ -924,24 +929,42 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
     }
     return off;
   };
+  // S: the last access of a block reads its whole line (the next block's
+  // first elements too), and a block after the first stores nothing of its
+  // first line, which the block before it writes whole.
+  auto voff_load = [&](int o, int b, int k) {
+    if constexpr (S) {
+      if (k == NW - 1) return 2 * (512 * b + 64 * k + lane);
+    }
+    return voff(o, b, k);
+  };
+  auto voff_store = [&](int o, int b, int k) {
+    if constexpr (S) {
+      if (k == 0 && b > 0) return OOB;
+    }
+    return voff(o, b, k);
+  };
   uint16_t xv[J][NW], rv[J][NW];
   auto load_block = [&](__amdgpu_buffer_rsrc_t rs, int o, int b, uint16_t (&v)[NW]) {
 #pragma unroll
-    for (int k = 0; k < NW; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff(o, b, k), 0, CP);
+    for (int k = 0; k < NW; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff_load(o, b, k), 0, CP);
   };
   // Element i of the block to sl[i]; lanes outside the block write the padding.
   auto to_slot = [&](const uint16_t (&v)[NW], int o) {
 #pragma unroll
     for (int k = 0; k < NW; ++k) sl[64 * k + lane - o] = v[k];
   };
-  // The block back out from the slot, all slot reads before any store.
+  // The block back out from the slot, all slot reads before any store (S:
+  // all but its last line, which is written apart).
   auto store_block_rs = [&](__amdgpu_buffer_rsrc_t rs, int o, int b) {
-    uint16_t v[NW];
+    constexpr int NS = S ? NW - 1 : NW;
+    uint16_t v[NS];
 #pragma unroll
-    for (int k = 0; k < NW; ++k) v[k] = sl[64 * k + lane - o];
+    for (int k = 0; k < NS; ++k) v[k] = sl[64 * k + lane - o];
     if (F || 512 * b < H) {
 #pragma unroll
-      for (int k = 0; k < NW; ++k) __builtin_amdgcn_raw_buffer_store_b16(v[k], rs, voff(o, b, k), 0, CP);
+      for (int k = 0; k < NS; ++k)
+        __builtin_amdgcn_raw_buffer_store_b16(v[k], rs, voff_store(o, b, k), 0, CP);
     }
   };
   // F: every block holds row elements, and no access has a branch.
@@ -981,6 +1004,7 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
     const int oo = A ? line_offset(orow) : 0;
     float acc[J][8];
     float bs[J];
+    float a8[S ? J : 1];  // S: the fp32 sums of each block's last line, as loaded
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (!F && J > 1 && 512 * (wave + W * j) >= H) {
@@ -999,17 +1023,19 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
         }
         if constexpr (R) {
           if (F || 512 * (wave + W * j) < H) {
-            const auto ros = gen_row_rsrc(p.residual_out + row * p.ro_stride, 0, H);
+            const auto ros = gen_row_rsrc(p.residual_out + row * p.ro_stride, ox, H);
 #pragma unroll
-            for (int k = 0; k < NW; ++k)
-              __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a[k]), ros, voff(0, wave + W * j, k), 0,
-                                                    CP);
+            for (int k = 0; k < (S ? NW - 1 : NW); ++k)
+              __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a[k]), ros, voff_store(ox, wave + W * j, k),
+                                                    0, CP);
           }
         }
+        if constexpr (S) a8[j] = a[NW - 1];
 #pragma unroll
-        for (int k = 0; k < NW; ++k) slf[64 * k + lane] = a[k];
+        for (int k = 0; k < NW; ++k) slf[64 * k + lane - ox] = a[k];
         wave_fence();
-        const float4 l4 = slotf4[wave][2 * lane], h4 = slotf4[wave][2 * lane + 1];
+        constexpr int SP = S ? PAD / 4 : 0;  // the slot's padding, in float4
+        const float4 l4 = slotf4[wave][SP + 2 * lane], h4 = slotf4[wave][SP + 2 * lane + 1];
         acc[j][0] = l4.x; acc[j][1] = l4.y; acc[j][2] = l4.z; acc[j][3] = l4.w;
         acc[j][4] = h4.x; acc[j][5] = h4.y; acc[j][6] = h4.z; acc[j][7] = h4.w;
         bs[j] = seg_sumsq(acc[j]);
@@ -1055,6 +1081,21 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
       wave_fence();
       store_block_rs(os, oo, wave + W * j);
       wave_fence();
+      if constexpr (S) {
+        // The block's last line, whole: its own last elements and the next
+        // block's first ones (past the row's end the stores are dropped).
+        const int b = wave + W * j;
+        if (F || 512 * b < H) {
+          const int e = min(512 * (b + 1) + lane - oo, 8 * B * J - 1);  // row element, in wl
+          const float w = __builtin_bit_cast(float, (uint32_t)wl[e] << 16);
+          const int off = 2 * (512 * b + 64 * (NW - 1) + lane);
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1((a8[j] * rinv) * w), os, off, 0, CP);
+          if constexpr (R) {
+            const auto ros = gen_row_rsrc(p.residual_out + row * p.ro_stride, oo, H);
+            __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a8[j]), ros, off, 0, CP);
+          }
+        }
+      }
     }
   }
 }
@@ -1754,6 +1795,16 @@ hipError_t two_pass_by_block(const Params& p, int b, int hidden, int64_t grid, h
 
 // ---------------------------------------------------------------- internal API
 
+// Every tensor's rows start at one offset in their 128-byte lines: the same
+// offset at the first row, and row strides equal modulo a line.
+template <bool R>
+bool shared_line_offsets(const GenParams& p) {
+  auto off = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) >> 1) & 63; };
+  return off(p.x) == off(p.out) && p.x_stride % 64 == p.out_stride % 64 &&
+         (!R || (off(p.x) == off(p.residual) && off(p.x) == off(p.residual_out) &&
+                 p.x_stride % 64 == p.r_stride % 64 && p.x_stride % 64 == p.ro_stride % 64));
+}
+
 template <int NB, int G, bool R, bool A = false>
 hipError_t go_general_long(const GenParams& p, size_t lds, int64_t grid, hipStream_t s) {
   // the kernel clamps the scalar offsets of its last four accesses only
@@ -1772,11 +1823,7 @@ hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t 
   // form's extra line) that cover the row, in the line-aligned form when
   // every tensor's rows share their line offset.
   if constexpr (B == 1024) {
-    auto off = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) >> 1) & 63; };
-    const bool same = off(p.x) == off(p.out) && p.x_stride % 64 == p.out_stride % 64 &&
-                      (!R || (off(p.x) == off(p.residual) && off(p.x) == off(p.residual_out) &&
-                              p.x_stride % 64 == p.r_stride % 64 &&
-                              p.x_stride % 64 == p.ro_stride % 64));
+    const bool same = shared_line_offsets<R>(p);
     // Thread t's elements t + 1024 u - o (o <= 63) must cover the row padded
     // to whole segments.
     const int padded = (hidden + 7) / 8 * 8;
@@ -1810,10 +1857,10 @@ hipError_t go_general(const GenParams& p, int hidden, int64_t grid, hipStream_t 
   return hipGetLastError();
 }
 
-template <int B, int J, bool R, bool A, bool F = false>
+template <int B, int J, bool R, bool A, bool F = false, bool S = false>
 hipError_t go_general_reg_k(const GenParams& p, int64_t grid, hipStream_t s) {
   const size_t lds = (size_t)B * J * 16;
-  auto k = k_general_reg<B, J, R, A, F>;
+  auto k = k_general_reg<B, J, R, A, F, S>;
   if (grid == -1) grid = resident(k, B, lds);
   hipLaunchKernelGGL(k, dim3(grid_for(grid, p.n_rows)), dim3(B), lds, s, p);
   return hipGetLastError();
@@ -1838,6 +1885,19 @@ hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s
   const bool full = 512 * (j * B / 64 - 1) < p.hidden;
   switch (j) {
     case 1:
+      if (general_lines(p.hidden) && shared_line_offsets<R>(p)) {
+        // Lines shared by two blocks written whole pays once each workgroup
+        // slot takes three or more rows.  Measured on MI355X (one segment
+        // per thread, default launch): 49.9 -> 48.6 us at 4096 x 8191, 39.3
+        // -> 38.2 at 4096 x 6143, 28.2 -> 27.6 at 8192 x 2047, 27.3 -> 26.9
+        // at 4096 x 4095, within 1% at three rounds; with two rounds slower:
+        // 15.1 -> 15.5 us at 1024 x 8191, 15.3 -> 15.5 at 2048 x 4095.
+        auto ks = k_general_reg<B, 1, R, true, false, true>;
+        const int64_t res = resident(ks, B, (size_t)B * 16);
+        const int64_t slots = grid > 0 && grid < res ? grid : res;
+        if (slots > 0 && p.n_rows >= 3 * slots)
+          return go_general_reg_k<B, 1, R, true, false, true>(p, grid, s);
+      }
       if (general_lines(p.hidden)) return go_general_reg_k<B, 1, R, true>(p, grid, s);
       return go_general_reg_k<B, 1, R, false>(p, grid, s);
     case 2:

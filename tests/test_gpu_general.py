@@ -108,10 +108,13 @@ def test_general_blocks_and_grids_agree_on_odd_rows(h):
     2600 at 128, 9001 and 12289 at 1024), rows that fill every block, the
     line-aligned accesses (last block above 128 elements) beside the
     row-relative ones (1100, 1663), and rows above 16384 (the long-row
-    kernel at 1024 threads, the LDS kernel below)."""
+    kernel at 1024 threads, the LDS kernel below).  With 22 rows, the grid
+    of 7 gives each workgroup three or more rows, so the line-aligned rows
+    with one segment per thread take the form that writes shared lines
+    whole there."""
     import torch
 
-    n = 19
+    n = 22
     x, r, w = synth.workload(5450 + h, n, h)
     announce("general blocks x grids, hidden %d" % h)
     m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
@@ -245,14 +248,17 @@ IN_PLACE_MODES = ["out=x,residual_out=residual", "out=x", "residual_out=residual
                   "out=residual,residual_out=x"]
 
 
+@pytest.mark.parametrize("grid", [0, 2])
 @pytest.mark.parametrize("mode", IN_PLACE_MODES)
 @pytest.mark.parametrize("h", [1001, 1663, 4095, 9001, 16383, 17000, 32767])
-def test_general_kernels_in_place(h, mode):
+def test_general_kernels_in_place(h, mode, grid):
     """An output that is an input's own buffer, on each general kernel: one
     wavefront per row (1001), the register kernel row-relative (1663) and
-    line-aligned (4095, 9001, 16383), the long-row kernel line-aligned
-    (17000, 32767).  Every element's inputs are read before its outputs are
-    written, so the results are the fp32 model's bits, as out of place."""
+    line-aligned (4095, 9001, 16383; with two workgroups, 4095 takes the
+    form that writes each line two blocks share whole, after the row's
+    barrier), the long-row kernel line-aligned (17000, 32767).  Every
+    element's inputs are read before its outputs are written, so the results
+    are the fp32 model's bits, as out of place."""
     import torch
 
     n = 13
@@ -266,9 +272,59 @@ def test_general_kernels_in_place(h, mode):
            "out=residual,residual_out=x": xd}[mode]
     out = poisoned_like(xd) if out is None else out
     res = poisoned_like(xd) if res is None else res
-    arn.add_rmsnorm_fwd(out, res, xd, rd, wd, 1e-6)
+    arn.add_rmsnorm_fwd_cfg(out, res, xd, rd, wd, 1e-6, path=arn.PATH_GENERAL, grid_blocks=grid)
     torch.cuda.synchronize()
     assert same16(from_dev(out), m_out) and same16(from_dev(res), m_res)
+
+
+@pytest.mark.parametrize("h", [2047, 4095, 6143, 8191, 8192])
+def test_whole_line_form_writes_only_its_rows(h):
+    """All four tensors 5 elements past a 256-byte boundary, and few enough
+    workgroups that each takes three or more rows: the register kernel
+    writes every line two blocks share whole, from the first block's
+    wavefront.  The fp32 model's bits, fused and plain, at every workgroup
+    size with one segment per thread, and nothing written before or after
+    the tensors (the last block's whole-line stores past the row's end are
+    dropped)."""
+    import torch
+
+    n, off, tail = 12, 5, 1024
+    x, r, w = synth.workload(6000 + h, n, h)
+    announce("general whole-line form: hidden %d" % h)
+    m_out, m_res = fp32_model.add_rmsnorm(x, r, w, 1e-6)
+    m_plain, _ = fp32_model.add_rmsnorm(x, None, w, 1e-6)
+    wd = to_dev(w)
+
+    def placed(fill=None):
+        buf = torch.full((off + n * h + tail,), np.int16(np.uint16(POISON).view(np.int16)),
+                         dtype=torch.int16, device="cuda:0")
+        view = buf[off:off + n * h]
+        if fill is not None:
+            view.copy_(to_dev(fill.reshape(-1)))
+        return buf, view.view(n, h)
+
+    def untouched(buf):
+        b = from_dev(buf)
+        return (b[:off] == POISON).all() and (b[off + n * h:] == POISON).all()
+
+    _, xd = placed(x)
+    _, rd = placed(r)
+    for b in BLOCKS:
+        if b * 8 < h:
+            continue  # one segment per thread only
+        for grid in (1, 2, 4):
+            ob, out = placed()
+            rb, res = placed()
+            arn.add_rmsnorm_fwd_cfg(out, res, xd, rd, wd, 1e-6, path=arn.PATH_GENERAL,
+                                    block_threads=b, grid_blocks=grid)
+            torch.cuda.synchronize()
+            assert same16(from_dev(out), m_out) and same16(from_dev(res), m_res), (b, grid)
+            assert untouched(ob) and untouched(rb), (b, grid)
+            pb, po = placed()
+            arn.rmsnorm_fwd_cfg(po, xd, wd, 1e-6, path=arn.PATH_GENERAL, block_threads=b,
+                                grid_blocks=grid)
+            torch.cuda.synchronize()
+            assert same16(from_dev(po), m_plain) and untouched(pb), (b, grid)
 
 
 @pytest.mark.parametrize("h", [4095, 9001, 20000])
