@@ -1897,7 +1897,7 @@ hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s
   switch (j) {
     case 1:
       if (general_lines(p.hidden) && shared_line_offsets<R>(p)) {
-        // Lines shared by two blocks written whole pays once each workgroup
+        // Writing the lines two blocks share whole pays once each workgroup
         // slot takes three or more rows.  Measured on MI355X (one segment
         // per thread, default launch): 49.9 -> 48.6 us at 4096 x 8191, 39.3
         // -> 38.2 at 4096 x 6143, 28.2 -> 27.6 at 8192 x 2047, 27.3 -> 26.9
