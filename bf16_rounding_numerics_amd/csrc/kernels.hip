@@ -843,7 +843,9 @@ __global__ __launch_bounds__(B) void k_general(GenParams p) {
 // at one offset in their lines (checked on the host), so the sums and
 // residual_out are formed where loaded, and each line that two blocks share
 // is written whole, by the wavefront of the first block, after the row's
-// barrier (so every wavefront has read the row, in place too).
+// barrier (so every wavefront has read the row, in place too; no wavefront
+// writes that line before, so with two segments per thread its x and
+// residual are read again there).
 DEV void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
 
 // Stores a wavefront's block of 512 elements (first element b0 of the row)
@@ -1015,7 +1017,7 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
     const int oo = A ? line_offset(orow) : 0;
     float acc[J][8];
     float bs[J];
-    float a8[S ? J : 1];  // S: the fp32 sums of each block's last line, as loaded
+    float a8[S && J == 1 ? J : 1];  // S: the fp32 sums of each block's last line, as loaded
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (!F && J > 1 && 512 * (wave + W * j) >= H) {
@@ -1041,7 +1043,7 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
                                                     0, CP);
           }
         }
-        if constexpr (S) a8[j] = a[NW - 1];
+        if constexpr (S && J == 1) a8[j] = a[NW - 1];
 #pragma unroll
         for (int k = 0; k < NW; ++k) slf[64 * k + lane - ox] = a[k];
         wave_fence();
@@ -1100,10 +1102,25 @@ __global__ __launch_bounds__(B) void k_general_reg(GenParams p) {
           const int e = min(512 * (b + 1) + lane - oo, 8 * B * J - 1);  // row element, in wl
           const float w = __builtin_bit_cast(float, (uint32_t)wl[e] << 16);
           const int off = 2 * (512 * b + 64 * (NW - 1) + lane);
-          __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1((a8[j] * rinv) * w), os, off, 0, CP);
+          float s8;
+          if constexpr (J == 1) {
+            s8 = a8[j];
+          } else {
+            // read again (from L2): two segments per thread leave no
+            // registers to keep the sums across the barrier
+            const auto xs8 = gen_row_rsrc(p.x + row * p.x_stride, oo, H);
+            const uint16_t x8 = __builtin_amdgcn_raw_buffer_load_b16(xs8, off, 0, 0);
+            s8 = __builtin_bit_cast(float, (uint32_t)x8 << 16);
+            if constexpr (R) {
+              const auto rs8 = gen_row_rsrc(p.residual + row * p.r_stride, oo, H);
+              const uint16_t r8 = __builtin_amdgcn_raw_buffer_load_b16(rs8, off, 0, 0);
+              s8 = s8 + __builtin_bit_cast(float, (uint32_t)r8 << 16);
+            }
+          }
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1((s8 * rinv) * w), os, off, 0, CP);
           if constexpr (R) {
             const auto ros = gen_row_rsrc(p.residual_out + row * p.ro_stride, oo, H);
-            __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(a8[j]), ros, off, 0, CP);
+            __builtin_amdgcn_raw_buffer_store_b16(bf16_rne1(s8), ros, off, 0, CP);
           }
         }
       }
@@ -1912,6 +1929,15 @@ hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s
       if (general_lines(p.hidden)) return go_general_reg_k<B, 1, R, true>(p, grid, s);
       return go_general_reg_k<B, 1, R, false>(p, grid, s);
     case 2:
+      if (full && general_lines(p.hidden) && shared_line_offsets<R>(p)) {
+        // As above (measured on MI355X: 52.2 -> 51.0 us at 2048 x 16383,
+        // 98.3 -> 94.7 us at 4096 x 16383, 53.2 -> 51.4 us at 2048 x 16001).
+        auto ks = k_general_reg<B, 2, R, true, true, true>;
+        const int64_t res = resident(ks, B, (size_t)B * 32);
+        const int64_t slots = grid > 0 && grid < res ? grid : res;
+        if (slots > 0 && p.n_rows >= 3 * slots)
+          return go_general_reg_k<B, 2, R, true, true, true>(p, grid, s);
+      }
       if (full && general_lines(p.hidden)) return go_general_reg_k<B, 2, R, true, true>(p, grid, s);
       if (full) return go_general_reg_k<B, 2, R, false, true>(p, grid, s);
       return go_general_reg_k<B, 2, R, false>(p, grid, s);
