@@ -1939,6 +1939,18 @@ hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s
           return go_general_reg_k<B, 2, R, true, true, true>(p, grid, s);
       }
       if (full && general_lines(p.hidden)) return go_general_reg_k<B, 2, R, true, true>(p, grid, s);
+      // Rows with blocks past their end keep the row-relative form, but with
+      // every tensor at one line offset the whole-line form beats it
+      // (measured on MI355X: 58.1 -> 56.1 us at 4096 x 9001, 80.0 -> 74.7 us
+      // at 4096 x 12287, 36.0 -> 33.3 us at 2048 x 10001, 90.8 -> 83.8 us at
+      // 4096 x 14001).
+      if (general_lines(p.hidden) && shared_line_offsets<R>(p)) {
+        auto ks = k_general_reg<B, 2, R, true, false, true>;
+        const int64_t res = resident(ks, B, (size_t)B * 32);
+        const int64_t slots = grid > 0 && grid < res ? grid : res;
+        if (slots > 0 && p.n_rows >= 3 * slots)
+          return go_general_reg_k<B, 2, R, true, false, true>(p, grid, s);
+      }
       if (full) return go_general_reg_k<B, 2, R, false, true>(p, grid, s);
       return go_general_reg_k<B, 2, R, false>(p, grid, s);
     case 4:
