@@ -1913,7 +1913,13 @@ hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s
   const bool full = 512 * (j * B / 64 - 1) < p.hidden;
   switch (j) {
     case 1:
-      if (general_lines(p.hidden) && shared_line_offsets<R>(p)) {
+      // Rows whose last block is short (row-relative form otherwise) take it
+      // too when more than half of the blocks hold row elements, as with the
+      // default workgroup (measured on MI355X: 27.1 -> 24.0 us at 8192 x
+      // 1663, 34.0 -> 32.5 us at 16384 x 1025, 21.4 -> 18.8 us at 4096 x
+      // 2600, 45.1 -> 40.1 us at 8192 x 3100; with most blocks empty, slower:
+      // 37.5 -> 42.6 us at 16384 x 1025 with 512 threads).
+      if ((general_lines(p.hidden) || 512 * (B / 128) < p.hidden) && shared_line_offsets<R>(p)) {
         // Writing the lines two blocks share whole pays once each workgroup
         // slot takes three or more rows.  Measured on MI355X (one segment
         // per thread, default launch): 49.9 -> 48.6 us at 4096 x 8191, 39.3
