@@ -1949,8 +1949,10 @@ hipError_t go_general_reg(const GenParams& p, int j, int64_t grid, hipStream_t s
       // every tensor at one line offset the whole-line form beats it
       // (measured on MI355X: 58.1 -> 56.1 us at 4096 x 9001, 80.0 -> 74.7 us
       // at 4096 x 12287, 36.0 -> 33.3 us at 2048 x 10001, 90.8 -> 83.8 us at
-      // 4096 x 14001).
-      if (general_lines(p.hidden) && shared_line_offsets<R>(p)) {
+      // 4096 x 14001), also with a short last block when more than half of
+      // the blocks hold row elements (43.7 -> 40.3 us at 2048 x 12289, 66.6
+      // -> 63.6 us at 4096 x 10300, 49.6 -> 46.9 us at 2048 x 14400).
+      if ((general_lines(p.hidden) || 512 * (B / 64) < p.hidden) && shared_line_offsets<R>(p)) {
         auto ks = k_general_reg<B, 2, R, true, false, true>;
         const int64_t res = resident(ks, B, (size_t)B * 32);
         const int64_t slots = grid > 0 && grid < res ? grid : res;
