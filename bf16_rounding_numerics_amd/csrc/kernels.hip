@@ -2100,9 +2100,16 @@ hipError_t launch_general(const FwdArgs& a, int block_threads, int64_t grid_bloc
   p.eps = a.eps;
   // Rows of at most 128 segments take one wavefront each; other rows that fit
   // in registers (at most 4 segments per thread and 2048 per workgroup) the
-  // register-resident kernel, the rest the LDS one.
+  // register-resident kernel, the rest the LDS one.  Rows of 65-128 segments
+  // whose tensors all share a line offset, with a last block of more than
+  // 128 elements, take the register kernel too, for its whole-line form
+  // (measured on MI355X: 30.1 -> 27.7 us at 16384 x 1001, 56.4 -> 52.2 us at
+  // 32768 x 1000, 111.0 -> 103.1 us at 65536 x 1000; with a short last block
+  // slower: 36.3 -> 41.1 us at 32768 x 600).
   const int segs = (a.hidden + 7) / 8;
-  if (segs <= 128) {
+  const bool whole_lines = segs > 64 && general_lines(a.hidden) &&
+                           (a.residual ? shared_line_offsets<true>(p) : shared_line_offsets<false>(p));
+  if (segs <= 128 && !whole_lines) {
     const int jw = segs <= 64 ? 1 : 2;
     return a.residual ? general_wave_by_block<true>(p, block_threads, jw, grid_blocks, s)
                       : general_wave_by_block<false>(p, block_threads, jw, grid_blocks, s);

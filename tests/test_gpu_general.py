@@ -277,8 +277,8 @@ def test_general_kernels_in_place(h, mode, grid):
     assert same16(from_dev(out), m_out) and same16(from_dev(res), m_res)
 
 
-@pytest.mark.parametrize("h", [1025, 1663, 2047, 2600, 4095, 6143, 8191, 8192, 9001, 10300,
-                               12287, 12289, 16001, 16383])
+@pytest.mark.parametrize("h", [767, 1001, 1025, 1663, 2047, 2600, 4095, 6143, 8191, 8192, 9001,
+                               10300, 12287, 12289, 16001, 16383])
 def test_whole_line_form_writes_only_its_rows(h):
     """All four tensors 5 elements past a 256-byte boundary, and few enough
     workgroups that each takes three or more rows: the register kernel
@@ -286,7 +286,8 @@ def test_whole_line_form_writes_only_its_rows(h):
     wavefront (with two segments per thread, 9001 to 16383 at 1024 threads,
     reading that line's x and residual again after the barrier; 9001 and
     12287 with blocks past the row's end; 1025, 1663, 2600, 10300 and 12289
-    with a short last block).
+    with a short last block; 767 and 1001, rows one wavefront would take
+    otherwise).
     The fp32 model's bits, fused and plain, at every workgroup size with one
     or two segments per thread, and nothing written before or after the
     tensors (the last block's whole-line stores past the row's end are
